@@ -1,0 +1,175 @@
+"""CPU oracle for the Q8_0 decode matvec -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``libq8dec``) never
+does, and the two share no code.  The arithmetic lives in ``q8_oracle.c``
+(plain C11, binary64, no fast-math); this module only marshals numpy arrays.
+
+Parity bar (the acceptance rule these helpers implement):
+  * every output:  |y_gpu - y_ref| <= 1e-4 * sum|scale*q*x| + 1e-6;
+  * argmax: the GPU index g is accepted when it equals the oracle's index i*,
+    or when y_ref[i*] - y_ref[g] <= tol[i*] + tol[g] (the two logits lie
+    within the bound, so either index is a correct answer).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8_oracle.c")
+_LIB = os.path.join(_HERE, "libq8oracle.so")
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+          "-shared", "-Wall"]
+
+REL_TOL = 1e-4
+ABS_TOL = 1e-6
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle (optionally another source, for mutation tests)."""
+    subprocess.run(["gcc", *CFLAGS, src, "-o", out, "-lm", "-lpthread"],
+                   check=True)
+    return out
+
+
+def _bind(lib):
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.q8o_half_to_double.restype = ctypes.c_double
+    lib.q8o_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.q8o_matvec.restype = None
+    lib.q8o_matvec.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.q8o_matvec_batched.restype = None
+    lib.q8o_matvec_batched.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    lib.q8o_matvec_mt.restype = ctypes.c_int
+    lib.q8o_matvec_mt.argtypes = [vp, vp, i64, i64, vp, vp, ctypes.c_int]
+    lib.q8o_argmax_f64.restype = i64
+    lib.q8o_argmax_f64.argtypes = [vp, i64]
+    lib.q8o_argmax_f32.restype = i64
+    lib.q8o_argmax_f32.argtypes = [vp, i64]
+    return lib
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        self.lib = _bind(ctypes.CDLL(path))
+
+    def half_to_double(self, bits) -> np.ndarray:
+        bits = np.asarray(bits, dtype=np.uint16).ravel()
+        f = self.lib.q8o_half_to_double
+        return np.array([f(int(b)) for b in bits], dtype=np.float64)
+
+    @staticmethod
+    def _check_w(w: np.ndarray, n: int, p: int | None) -> tuple[np.ndarray, int]:
+        """Weights as uint8 [p, n/32*34]; p from the first axis if not given."""
+        if n % 32:
+            raise ValueError("n must be a multiple of 32")
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        if p is None:
+            p = w.shape[0]
+        if w.size != p * (n // 32) * 34:
+            raise ValueError("weight bytes do not match (p, n)")
+        return w, p
+
+    def matvec(self, w: np.ndarray, x: np.ndarray, p: int | None = None):
+        """y, tol (float64 [p]) for w = p rows of Q8_0 blocks and x[n]."""
+        x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+        n = x.size
+        w, p = self._check_w(w, n, p)
+        y = np.empty(p, dtype=np.float64)
+        tol = np.empty(p, dtype=np.float64)
+        self.lib.q8o_matvec(w.ctypes.data, x.ctypes.data, n, p, y.ctypes.data,
+                            tol.ctypes.data)
+        return y, tol
+
+    def matvec_batched(self, w: np.ndarray, x: np.ndarray, p: int | None = None):
+        """y, tol (float64 [m, p]) for x [m, n]."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        m, n = x.shape
+        w, p = self._check_w(w, n, p)
+        y = np.empty((m, p), dtype=np.float64)
+        tol = np.empty((m, p), dtype=np.float64)
+        self.lib.q8o_matvec_batched(w.ctypes.data, x.ctypes.data, m, n, p,
+                                    y.ctypes.data, tol.ctypes.data)
+        return y, tol
+
+    def matvec_mt(self, w: np.ndarray, x: np.ndarray, threads: int):
+        """Row-parallel matvec; returns y, tol and the thread count used."""
+        x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+        n = x.size
+        w, p = self._check_w(w, n, None)
+        y = np.empty(p, dtype=np.float64)
+        tol = np.empty(p, dtype=np.float64)
+        used = self.lib.q8o_matvec_mt(w.ctypes.data, x.ctypes.data, n, p,
+                                      y.ctypes.data, tol.ctypes.data, threads)
+        return y, tol, used
+
+    def argmax_f64(self, v) -> int:
+        v = np.ascontiguousarray(v, dtype=np.float64).ravel()
+        return int(self.lib.q8o_argmax_f64(v.ctypes.data, v.size))
+
+    def argmax_f32(self, v) -> int:
+        v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+        return int(self.lib.q8o_argmax_f32(v.ctypes.data, v.size))
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``q8_oracle.c`` (compiled on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def matvec(w, x, p=None):
+    return get().matvec(w, x, p)
+
+
+def matvec_batched(w, x, p=None):
+    return get().matvec_batched(w, x, p)
+
+
+def argmax_f64(v) -> int:
+    return get().argmax_f64(v)
+
+
+def argmax_f32(v) -> int:
+    return get().argmax_f32(v)
+
+
+# ---- the parity bar --------------------------------------------------------
+
+def matvec_errors(y_gpu, y_ref, tol) -> np.ndarray:
+    """|y_gpu - y_ref| / tol per output (<= 1 passes).
+
+    Equal values (infinities included) and NaN against NaN count as zero
+    error; any other NaN fails."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref) / np.asarray(tol, dtype=np.float64)
+    same = (np.isnan(y_gpu) & np.isnan(y_ref)) | (y_gpu == y_ref)
+    err[same] = 0.0
+    err[np.isnan(err)] = np.inf
+    return err
+
+
+def argmax_accepted(g: int, y_ref, tol) -> bool:
+    """True when index g is a correct argmax of the exact logits y_ref."""
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    tol = np.asarray(tol, dtype=np.float64)
+    best = argmax_f64(y_ref)
+    if g == best:
+        return True
+    if best < 0 or g < 0 or g >= y_ref.size or np.isnan(y_ref[g]):
+        return False
+    return bool(y_ref[best] - y_ref[g] <= tol[best] + tol[g])

@@ -1,0 +1,307 @@
+"""Pins that tie the oracle to facts outside itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with something the pages or the mathematics fix:
+  * printed values (golden fixtures with citations),
+  * the IEEE-754 binary16 format as decoded by numpy (an independent routine),
+  * brute force: a dense binary64 dequantised matrix built with numpy and
+    multiplied with numpy, on tiny inputs,
+  * closed forms: all-ones x, one-hot x, a single nonzero quant,
+    power-of-two scales with small-integer x (exact dyadic sums),
+  * invariants: exact homogeneity in powers of two, odd symmetry, row
+    permutation, batched == per-row, threaded == single-threaded,
+  * the argmax rule: lowest index on ties, NaN skipped, -0 == +0.
+The mutation tests compile deliberately broken copies of the oracle and
+require every one of them to fail at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import gen
+from tests import pagegen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---- independent helpers (numpy, not the oracle) ---------------------------
+
+def dense_dequant(w: np.ndarray, n: int) -> np.ndarray:
+    """W as a dense float64 [p, n] matrix, decoded by numpy's float16."""
+    p = w.shape[0]
+    bpr = n // 32
+    blk = np.ascontiguousarray(w).reshape(p, bpr, 34)
+    scale = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2")[..., 0]
+    q = np.ascontiguousarray(blk[:, :, 2:]).view(np.int8)
+    return (scale.astype(np.float64)[:, :, None] * q.astype(np.float64)).reshape(p, n)
+
+
+def make_blocks(scale_bits: np.ndarray, quants: np.ndarray) -> np.ndarray:
+    """Assemble uint8 [p, bpr*34] from scale bits [p, bpr] and int8 [p, bpr, 32]."""
+    p, bpr = scale_bits.shape
+    out = np.empty((p, bpr, 34), dtype=np.uint8)
+    sb = scale_bits.astype(np.uint16)
+    out[:, :, 0] = (sb & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (sb >> 8).astype(np.uint8)
+    out[:, :, 2:] = quants.astype(np.int8).view(np.uint8)
+    return out.reshape(p, bpr * 34)
+
+
+def rich_case(p: int, n: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Generator weights with planted extremes: -128 quants, subnormal, zero,
+    negative and large scales."""
+    w = gen.weights(p, n, seed=seed, index=seed)
+    x = gen.activations(1, n, seed=seed, index=seed)[0]
+    bpr = n // 32
+    blk = w.reshape(p, bpr, 34)
+    rng = np.random.default_rng(seed)
+    specials = [0x0001, 0x03FF, 0x0000, 0x8000, 0xAC00, 0x7BFF, 0x0400, 0x8001]
+    for i, bits in enumerate(specials):
+        r, b = i % p, (i * 7) % bpr
+        blk[r, b, 0] = bits & 0xFF
+        blk[r, b, 1] = bits >> 8
+    flat = blk[:, :, 2:].reshape(-1)
+    idx = rng.choice(flat.size, size=max(1, flat.size // 50), replace=False)
+    flat[idx] = 0x80  # int8 -128
+    blk[:, :, 2:] = flat.reshape(p, bpr, 32)
+    return blk.reshape(p, bpr * 34), x
+
+
+def sum_bound(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """n * 2^-52 * sum|scale*q*x| per row: a rounding bound for any order."""
+    d = np.abs(dense_dequant(w, x.size))
+    return x.size * 2.0 ** -52 * (d @ np.abs(x.astype(np.float64))) + 1e-300
+
+
+# ---- pins -------------------------------------------------------------------
+
+def pin_f16_golden(orc):
+    """Printed and format-defined binary16 values."""
+    kv = pagegen.read_kv(os.path.join(GOLDEN, "f16_values.txt"))
+    assert kv, "empty fixture"
+    for key, vals in kv.items():
+        bits = int(key, 16)
+        want = float(vals[0][0])
+        got = float(orc.half_to_double([bits])[0])
+        if math.isnan(want):
+            assert math.isnan(got), f"{key}: {got} != nan"
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), \
+                f"{key}: {got!r} != {want!r}"
+
+
+def pin_f16_exhaustive(orc):
+    """All 65,536 binary16 patterns against numpy's own float16 decoder."""
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.half_to_double(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "NaN patterns differ"
+    assert np.array_equal(got[~nan], want[~nan]), "values differ"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), "signs differ"
+
+
+def pin_bruteforce_dense(orc):
+    """Tiny shapes vs a dense numpy float64 dequantised matmul."""
+    for p, n, seed in [(1, 32, 1), (3, 96, 2), (50, 96, 3), (7, 128, 4),
+                       (5, 1024, 5), (9, 64, 6)]:
+        w, x = rich_case(p, n, seed)
+        y, tol = orc.matvec(w, x)
+        d = dense_dequant(w, n)
+        ref = d @ x.astype(np.float64)
+        bound = sum_bound(w, x)
+        assert np.all(np.abs(y - ref) <= bound), f"p={p} n={n}: y differs"
+        mag = np.abs(d) @ np.abs(x.astype(np.float64))
+        want_tol = 1e-4 * mag + 1e-6
+        assert np.allclose(tol, want_tol, rtol=1e-12, atol=0), f"p={p} n={n}: tol"
+
+
+def pin_page_matvec_case(orc):
+    """The page's matvec test inputs (p=50, n=96, seeds 7/42) vs brute force
+    and the page's own 5e-4 absolute bound against a float32 sequential sum."""
+    kv = pagegen.read_kv(os.path.join(GOLDEN, "page_matvec_case.txt"))
+    p, n = int(kv["p"][0][0]), int(kv["n"][0][0])
+    w = pagegen.fabricated_q8(p, n, int(kv["weight_seed"][0][0]),
+                              int(kv["scale_bits"][0][0], 16))
+    x = pagegen.lcg_f32(int(kv["x_seed"][0][0]), n)
+    y, _ = orc.matvec(w, x)
+    ref = dense_dequant(w, n) @ x.astype(np.float64)
+    assert np.all(np.abs(y - ref) <= sum_bound(w, x))
+    # the page's expected value: a sequential f32 sum with the scale inside
+    blk = w.reshape(p, n // 32, 34)
+    q = np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).reshape(p, n)
+    scale = np.float32(1.0 / 16.0)
+    seq = np.zeros(p, dtype=np.float32)
+    for c in range(n):
+        seq = seq + scale * q[:, c].astype(np.float32) * x[c]
+    assert np.max(np.abs(y - seq.astype(np.float64))) < float(kv["abs_tol"][0][0])
+
+
+def pin_closed_form_ones(orc):
+    """x = 1: y[r] = sum_b scale_b * sum_j q_bj, computed with exact rationals."""
+    p, n = 6, 256
+    w, _ = rich_case(p, n, 11)
+    blk = w.reshape(p, n // 32, 34)
+    scale = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2")[..., 0]
+    qsum = np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).astype(np.int64).sum(axis=2)
+    y, _ = orc.matvec(w, np.ones(n, dtype=np.float32))
+    for r in range(p):
+        exact = sum((Fraction(float(scale[r, b])) * int(qsum[r, b])
+                     for b in range(n // 32)), Fraction(0))
+        mag = sum((abs(Fraction(float(scale[r, b]))) * int(abs(qsum[r, b]))
+                   for b in range(n // 32)), Fraction(0))
+        assert abs(Fraction(float(y[r])) - exact) <= mag * Fraction(n, 2 ** 52), r
+
+
+def pin_closed_form_one_hot(orc):
+    """x = e_k: y[r] = scale[r, k/32] * q[r, k/32, k%32] exactly."""
+    p, n = 5, 128
+    w, _ = rich_case(p, n, 12)
+    d = dense_dequant(w, n)
+    for k in [0, 1, 31, 32, 33, 77, 127]:
+        x = np.zeros(n, dtype=np.float32)
+        x[k] = 1.0
+        y, _ = orc.matvec(w, x)
+        assert np.array_equal(y, d[:, k]), f"k={k}"
+
+
+def pin_single_nonzero_quant(orc):
+    """One nonzero weight isolates one term: y = scale*q*x[c] at its row only."""
+    p, n = 4, 96
+    x = gen.activations(1, n, seed=13, index=13)[0]
+    for (r, c, qv, sbits) in [(0, 0, 5, 0x3C00), (3, 95, -128, 0x2C00),
+                              (2, 40, 127, 0x0003), (1, 63, -1, 0xC200)]:
+        quants = np.zeros((p, n // 32, 32), dtype=np.int8)
+        quants[r, c // 32, c % 32] = qv
+        sb = np.full((p, n // 32), sbits, dtype=np.uint16)
+        w = make_blocks(sb, quants)
+        y, _ = orc.matvec(w, x)
+        s = float(np.array([sbits], dtype=np.uint16).view(np.float16)[0])
+        want = np.zeros(p)
+        want[r] = s * qv * float(x[c])
+        assert np.array_equal(y, want), (r, c)
+
+
+def pin_pow2_integer_exact(orc):
+    """Power-of-two scales and small-integer x: every partial sum is an exact
+    dyadic, so y equals the integer arithmetic exactly."""
+    p, n = 8, 512
+    rng = np.random.default_rng(14)
+    quants = rng.integers(-128, 128, size=(p, n // 32, 32), dtype=np.int64)
+    expo = rng.integers(-6, 3, size=(p, n // 32))
+    sb = (15 + expo).astype(np.uint16) << 10  # 2^expo
+    w = make_blocks(sb, quants)
+    xi = rng.integers(-8, 9, size=n)
+    y, _ = orc.matvec(w, xi.astype(np.float32))
+    for r in range(p):
+        exact = Fraction(0)
+        for b in range(n // 32):
+            dot = int(np.dot(quants[r, b], xi[32 * b:32 * b + 32]))
+            exact += Fraction(2) ** int(expo[r, b]) * dot
+        assert Fraction(float(y[r])) == exact, r
+
+
+def pin_homogeneity_and_sign(orc):
+    """y(2^k x) == 2^k y(x) and y(-x) == -y(x), bit for bit."""
+    w, x = rich_case(7, 160, 15)
+    y, _ = orc.matvec(w, x)
+    for k in (-3, 1, 5):
+        yk, _ = orc.matvec(w, (x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(yk, y * 2.0 ** k), k
+    yn, _ = orc.matvec(w, -x)
+    assert np.array_equal(yn, -y)
+
+
+def pin_row_permutation(orc):
+    """Permuting weight rows permutes y (rows are independent)."""
+    w, x = rich_case(9, 96, 16)
+    y, _ = orc.matvec(w, x)
+    perm = np.random.default_rng(16).permutation(9)
+    yp, _ = orc.matvec(w[perm], x)
+    assert np.array_equal(yp, y[perm])
+
+
+def pin_batched_and_threads(orc):
+    """Batched row i == single matvec on row i; threaded == single, bitwise."""
+    p, n, m = 33, 256, 5
+    w = gen.weights(p, n, seed=17, index=17)
+    xs = gen.activations(m, n, seed=17, index=17)
+    yb, tb = orc.matvec_batched(w, xs)
+    for i in range(m):
+        y, t = orc.matvec(w, xs[i])
+        assert np.array_equal(yb[i], y) and np.array_equal(tb[i], t), i
+    y, t = orc.matvec(w, xs[0])
+    for threads in (1, 3, 8):
+        ym, tm, used = orc.matvec_mt(w, xs[0], threads)
+        assert used == threads
+        assert np.array_equal(ym, y) and np.array_equal(tm, t), threads
+
+
+def pin_tolerance_hand_case(orc):
+    """tol = 1e-4 * sum|scale*q*x| + 1e-6 on a hand-worked block: scale 1,
+    q = (1, -2, 0, ...), x = (3, 5, 7, ...) gives y = -7 and sum|t| = 13."""
+    quants = np.zeros((1, 1, 32), dtype=np.int8)
+    quants[0, 0, 0], quants[0, 0, 1] = 1, -2
+    w = make_blocks(np.array([[0x3C00]], dtype=np.uint16), quants)
+    x = np.arange(3, 3 + 2 * 32, 2).astype(np.float32)
+    y, tol = orc.matvec(w, x)
+    assert y[0] == -7.0
+    assert abs(tol[0] - (1e-4 * 13 + 1e-6)) < 1e-18
+
+
+def pin_argmax_page_tie(orc):
+    """The page's argmax example: ties at 140011/140012 go to 140011."""
+    kv = pagegen.read_kv(os.path.join(GOLDEN, "argmax_tie.txt"))
+    n, seed = int(kv["n"][0][0]), int(kv["seed"][0][0])
+    v = pagegen.lcg_f32(seed, n)
+    for idx, val in kv["plant"]:
+        v[int(idx)] = np.float32(float(val))
+    want = int(kv["expect"][0][0])
+    assert orc.argmax_f32(v) == want
+    assert orc.argmax_f64(v.astype(np.float64)) == want
+
+
+def pin_argmax_rules(orc):
+    """Lowest index on ties; NaN never wins (even at index 0); -0 == +0."""
+    nan, inf = float("nan"), float("inf")
+    cases = [
+        ([1.0, 3.0, 3.0, 2.0], 1),
+        ([5.0, 1.0, 5.0], 0),
+        ([1.0, 2.0, 9.0], 2),
+        ([2.0, 2.0, 2.0, 2.0], 0),
+        ([nan, 1.0, 0.5], 1),
+        ([0.5, nan, 7.0, nan], 2),
+        ([nan, nan], -1),
+        ([], -1),
+        ([-0.0, 0.0], 0),
+        ([0.0, -0.0], 0),
+        ([-1.0, -0.0, 0.0, -2.0], 1),
+        ([-inf, -inf], 0),
+        ([1.0, inf, inf], 1),
+        ([nan, -inf], 1),
+    ]
+    for vals, want in cases:
+        assert orc.argmax_f64(np.array(vals, dtype=np.float64)) == want, vals
+        assert orc.argmax_f32(np.array(vals, dtype=np.float32)) == want, vals
+
+
+ALL_PINS = [
+    pin_f16_golden,
+    pin_f16_exhaustive,
+    pin_bruteforce_dense,
+    pin_page_matvec_case,
+    pin_closed_form_ones,
+    pin_closed_form_one_hot,
+    pin_single_nonzero_quant,
+    pin_pow2_integer_exact,
+    pin_homogeneity_and_sign,
+    pin_row_permutation,
+    pin_batched_and_threads,
+    pin_tolerance_hand_case,
+    pin_argmax_page_tie,
+    pin_argmax_rules,
+]

@@ -1,0 +1,70 @@
+"""Mutation tests: a plausible mistake planted in a copy of the oracle (on the
+CPU, never on the GPU path) must make at least one pin fail.  This is what
+shows the pins are strong enough to trust the oracle."""
+import os
+
+import pytest
+
+import oracle
+from tests.oracle_pins import ALL_PINS
+
+MUTANTS = [
+    ("scale dropped",
+     "double t = scale * q * (double)x[32 * b + j];",
+     "double t = q * (double)x[32 * b + j];"),
+    ("quant read unsigned",
+     "(double)(int8_t)blk[2 + j]", "(double)blk[2 + j]"),
+    ("quant offset off by one",
+     "(int8_t)blk[2 + j]", "(int8_t)blk[1 + j]"),
+    ("x index rotated",
+     "x[32 * b + j]", "x[32 * b + (j + 1) % 32]"),
+    ("block stride 32 bytes",
+     "row + (size_t)b * 34u", "row + (size_t)b * 32u"),
+    ("row stride 32 bytes per block",
+     "(size_t)r * (size_t)blocks * 34u", "(size_t)r * (size_t)blocks * 32u"),
+    ("scale bytes big-endian",
+     "(blk[0] | (blk[1] << 8))", "(blk[1] | (blk[0] << 8))"),
+    ("exponent bias off by one",
+     "expo - 25", "expo - 24"),
+    ("subnormal decoded as normal",
+     "v = ldexp((double)frac, -24);", "v = ldexp((double)(1024 + frac), -25);"),
+    ("hidden bit dropped",
+     "ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(frac), expo - 25)"),
+    ("sign bit ignored",
+     "return sign ? -v : v;", "return v;"),
+    ("product rounded to f32",
+     "double t = scale * q * (double)x[32 * b + j];",
+     "double t = (float)(scale * q) * x[32 * b + j];"),
+    ("row sum in f32",
+     "double sum = 0.0, mag = 0.0;", "float sum = 0.0f; double mag = 0.0;"),
+    ("last block skipped",
+     "for (int64_t b = 0; b < blocks; b++)", "for (int64_t b = 0; b + 1 < blocks; b++)"),
+    ("tolerance uses signed terms",
+     "mag += fabs(t);", "mag += t;"),
+    ("tolerance constant",
+     "1e-4 * mag + 1e-6", "1e-3 * mag + 1e-6"),
+    ("argmax ties to the higher index",
+     "v[i] > bv", "v[i] >= bv"),
+    ("argmax keeps NaN",
+     "if (isnan(v[i])) continue;", ""),
+    ("argmax never updates the best value",
+     "bv = v[i];", ""),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_fails_a_pin(tmp_path, name, old, new):
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert old in src, f"mutation site for '{name}' no longer in the oracle"
+    src_path = tmp_path / "mutant.c"
+    src_path.write_text(src.replace(old, new))
+    lib = oracle.build(str(src_path), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:  # a wrong value, or a NaN where none belongs
+            failed.append(pin.__name__)
+    assert failed, f"mutant '{name}' passed every pin"
