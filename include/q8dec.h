@@ -1,0 +1,168 @@
+/*
+ * q8dec.h - C ABI of libq8dec, the Q8_0 single-token decode matvec for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (inferno.rs "IV.4: One command buffer per token", section
+ * "Eight kernels", the q8_matvec listing and the prose after it):
+ *   W has p rows and n columns, stored row-major as Q8_0 blocks.  A block is
+ *   34 bytes: a little-endian IEEE binary16 scale, then 32 signed 8-bit
+ *   quants; block b of a row covers x[32b .. 32b+31].  Row r of W is the
+ *   n/32 blocks at byte offset r * (n/32) * 34.  The weights are the raw
+ *   block bytes, never repacked ("The decoder: kernels and helpers", q8_bytes).
+ *     y[r] = sum_b scale(r,b) * sum_j q(r,b,j) * x[32b + j]
+ *   computed in binary32 from exact binary32 products of each quant with x;
+ *   the scale is applied once per block (the dequantise-in-the-dot shape the
+ *   same section describes).
+ * The argmax ("Eight kernels", argmax_row and the prose after it): the index
+ *   of the largest logit, ties to the lowest index, so only four bytes per
+ *   row leave the device.  NaN logits never win; -0 and +0 are equal; a row
+ *   whose logits are all NaN yields -1.
+ * The step (sections "One command buffer" and "The seam"): the 197 matvecs
+ *   of one decode step (7 projections x 28 layers, then the lm_head and its
+ *   argmax) are recorded once and submitted once, and one int32 comes back.
+ *
+ * Conventions for every entry point
+ *   - Pointers named w, x, y, logits, idx are DEVICE pointers owned by the
+ *     caller; the library never allocates, frees or retains them.  host_idx
+ *     is caller-owned PINNED host memory (hipHostMalloc).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are stream-ordered and asynchronous: results are valid once the
+ *     caller has synchronised the stream.  Outputs are bit-identical from run
+ *     to run for the same inputs.
+ *   - Layouts: w is p rows x (n/32) blocks x 34 bytes, contiguous; x is
+ *     [m][n] float32 row-major; y is [m][p] float32 row-major; idx is int32[m].
+ *   - Alignment: w and x 16 bytes; y, logits and idx 4 bytes.  A pointer may
+ *     be NULL only when its buffer holds zero bytes.
+ *   - Every argument is validated before any HIP call; a refused call does
+ *     no GPU work and returns a nonzero Q8_ERR_* status.  Q8_OK is 0.
+ *   - The argmax entry points keep a small per-device workspace inside the
+ *     library (allocated by q8_init or on first use, outside any stream
+ *     capture).  Two argmax calls that run at the same time on one device
+ *     share it and race; issue them in one stream order.
+ */
+#ifndef Q8DEC_H
+#define Q8DEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define Q8_OK 0
+#define Q8_ERR_NULL 1        /* a required pointer is NULL                  */
+#define Q8_ERR_SHAPE 2       /* bad m, n or p (see limits)                  */
+#define Q8_ERR_ALIGN 3       /* a pointer breaks the alignment rule         */
+#define Q8_ERR_NO_DEVICE 4   /* no HIP device is visible                    */
+#define Q8_ERR_ARCH 5        /* the current device is not gfx950            */
+#define Q8_ERR_CODE_OBJECT 6 /* kernels not loadable on this device; sticky */
+#define Q8_ERR_HIP 7         /* a HIP call failed: see q8_last_hip_error()  */
+#define Q8_ERR_GRAPH 8       /* step-graph capture or instantiation failed  */
+#define Q8_ERR_BAD_HANDLE 9  /* NULL, unknown or destroyed graph handle     */
+#define Q8_ERR_COUNT 10      /* descriptor count or argmax count out of range */
+#define Q8_ERR_MODE 11       /* unknown step-graph mode                     */
+
+/* ---- limits --------------------------------------------------------- */
+#define Q8_BLOCK 32                 /* quants per block                       */
+#define Q8_BLOCK_BYTES 34           /* bytes per block                        */
+#define Q8_MAX_M 8                  /* activation rows per batched call       */
+#define Q8_MAX_N 65536              /* 0 <= n <= Q8_MAX_N, n % 32 == 0        */
+#define Q8_MAX_P 0x7FFFFFFF         /* 0 <= p; p >= 1 where an argmax is taken */
+#define Q8_MAX_DESCS 4096           /* descriptors per step graph             */
+#define Q8_MAX_ARGMAX_DESCS 64      /* argmax descriptors per step graph      */
+
+/* ---- status and device ---------------------------------------------- */
+
+/* Name of a status code ("q8_ok", "q8_err_shape", ...); any other value
+ * gives "q8_code_out_of_range".  Never touches the GPU. */
+const char *q8_status_name(int status);
+
+/* The hipError_t of the most recent HIP failure seen by this thread
+ * (0 if none). */
+int q8_last_hip_error(void);
+
+/* Number of visible HIP devices (0 when none), without selecting one. */
+int q8_device_count(int32_t *count);
+
+/* Checks the current device (gfx950, kernels loadable) and allocates its
+ * argmax workspace.  Optional: every entry point does it on first use.  A
+ * failure is remembered for that device and returned again (sticky). */
+int q8_init(void);
+
+/* ---- matvec ------------------------------------------------------------ */
+
+/* y[p] = W x for one activation row x[n] (the page's q8_matvec, m = 1).
+ * p == 0 or n == 0 is allowed (n == 0 writes zeros). */
+int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
+              void *stream);
+
+/* Batched decode: y[m][p] = x[m][n] W^T with 1 <= m <= 8; the weight blocks
+ * are streamed once for all m rows. */
+int q8_matvec_batched(const void *w, const float *x, float *y, int32_t m,
+                      int32_t n, int32_t p, void *stream);
+
+/* idx[i] = argmax over logits[i][0..p-1] for i < m; 1 <= m <= 8, p >= 1. */
+int q8_argmax(const float *logits, int32_t m, int32_t p, int32_t *idx,
+              void *stream);
+
+/* Fused lm_head: the matvec of q8_matvec_batched followed by the argmax of
+ * each output row, without a logits round trip.  y_or_null may be NULL (no
+ * logits written) or a [m][p] buffer that also receives the logits. */
+int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
+                     int32_t *idx, int32_t m, int32_t n, int32_t p,
+                     void *stream);
+
+/* ---- decode step graph --------------------------------------------------- */
+
+/* One matvec of a step.  x is [m][n], y is [m][p]; idx != NULL asks for the
+ * fused argmax (then y may be NULL). */
+typedef struct q8_matvec_desc {
+  const void *w;
+  const float *x;
+  float *y;
+  int32_t *idx;
+  int32_t n;
+  int32_t p;
+} q8_matvec_desc;
+
+typedef struct q8_step_graph q8_step_graph;
+
+/* How a step graph is recorded.
+ *  Q8_GRAPH_CHAIN: one kernel node per descriptor, in descriptor order, each
+ *    depending on the previous one (the in-order semantics of one command
+ *    buffer), then the readback copy.
+ *  Q8_GRAPH_PERSISTENT: one kernel node that walks a device-side table of
+ *    all descriptors with no ordering between them (valid when no
+ *    descriptor reads another's output), then the readback copy. */
+#define Q8_GRAPH_CHAIN 0
+#define Q8_GRAPH_PERSISTENT 1
+
+/* Records the descriptors (1 <= count <= Q8_MAX_DESCS, at most
+ * Q8_MAX_ARGMAX_DESCS with idx) for m activation rows into an instantiated
+ * hipGraph.  If host_idx is non-NULL the graph ends with one device-to-host
+ * copy of every argmax result (m int32 per argmax descriptor, in descriptor
+ * order) into host_idx.  The descriptors' pointers are baked in: to change
+ * inputs, write new values into the same x buffers.  `stream` only names the
+ * device context; nothing is enqueued on it.  *out receives a handle owned
+ * by the caller (free with q8_step_graph_destroy). */
+int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
+                        int32_t *host_idx, int32_t mode, void *stream,
+                        q8_step_graph **out);
+
+/* Enqueues the whole step with one hipGraphLaunch on `stream`. */
+int q8_step_graph_launch(q8_step_graph *g, void *stream);
+
+/* Node counts of the instantiated graph (kernel nodes, memcpy nodes): the
+ * per-step dispatch budget. */
+int q8_step_graph_info(const q8_step_graph *g, int32_t *kernel_nodes,
+                       int32_t *memcpy_nodes);
+
+/* Destroys the graph and its workspace; the handle becomes invalid. */
+int q8_step_graph_destroy(q8_step_graph *g);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8DEC_H */

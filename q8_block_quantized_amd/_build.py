@@ -1,0 +1,48 @@
+"""Build step of libq8dec: compiles the HIP sources for gfx950 in-tree.
+
+Usage: ``python -m q8_block_quantized_amd._build``.  The shared library lands
+next to this file as ``libq8dec.so`` and travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "q8dec_api.hip"),
+           os.path.join(CSRC, "q8dec_kernels.hip")]
+LIB = os.path.join(HERE, "libq8dec.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    # no packed FP32 (v_pk_*_f32) anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-rdc", "-Wall",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libq8dec")
+    if verbose:
+        noise = "packed-fp32-ops"
+        for line in (res.stdout + res.stderr).splitlines():
+            if noise not in line:
+                print(line)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,365 @@
+// C ABI of libq8dec (declared in include/q8dec.h): argument validation,
+// per-device set-up, launches and the decode-step graph.
+//
+// Error convention (after the Metal decode pages: the inferno.rs decoder
+// hands back "not handled" instead of failing, and the Algenta "Metal LLM
+// decode" page refuses with named status codes before any GPU work and maps
+// unknown codes to an out-of-range name): every entry point checks all of its
+// arguments first and returns a Q8_ERR_* code without touching the GPU when
+// one is wrong.  A device that fails its set-up stays failed (the inferno.rs
+// decoder slot remembers a failed start and never retries it).
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <set>
+#include <vector>
+
+#include "../../include/q8dec.h"
+#include "q8dec_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return Q8_ERR_HIP;
+}
+
+// ---- per-device state --------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  int status = -1;                  // -1 unchecked, else a Q8 status
+  q8::ArgmaxSlot *slot = nullptr;   // workspace of the standalone argmax calls
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+// Selects nothing: checks the current device and sets it up once.
+int ensure_device(int *dev_out) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return Q8_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return Q8_ERR_NO_DEVICE;
+  if (dev_out) *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState &st = g_dev[dev];
+  if (st.status >= 0) return st.status;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    st.status = Q8_ERR_ARCH;
+    return st.status;
+  }
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, q8::probe_kernel());
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    st.status = Q8_ERR_CODE_OBJECT;
+    return st.status;
+  }
+  void *p = nullptr;
+  e = hipMalloc(&p, sizeof(q8::ArgmaxSlot));
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipMemset(p, 0, sizeof(q8::ArgmaxSlot));
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e);
+  }
+  st.slot = (q8::ArgmaxSlot *)p;
+  st.status = Q8_OK;
+  return Q8_OK;
+}
+
+// ---- argument checks (no HIP calls) -----------------------------------
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shape and pointer rules shared by every matvec entry point.
+int check_matvec(const void *w, const float *x, const float *y,
+                 const int32_t *idx, int32_t m, int32_t n, int32_t p,
+                 bool need_y) {
+  if (m < 1 || m > Q8_MAX_M) return Q8_ERR_SHAPE;
+  if (n < 0 || n > Q8_MAX_N || (n % Q8_BLOCK) != 0) return Q8_ERR_SHAPE;
+  if (p < 0) return Q8_ERR_SHAPE;
+  if (idx && p < 1) return Q8_ERR_SHAPE;
+  const bool wbytes = n > 0 && p > 0;
+  if ((wbytes && !w) || (n > 0 && !x)) return Q8_ERR_NULL;
+  if (need_y && p > 0 && !y) return Q8_ERR_NULL;
+  if ((w && !aligned(w, 16)) || (x && !aligned(x, 16))) return Q8_ERR_ALIGN;
+  if ((y && !aligned(y, 4)) || (idx && !aligned(idx, 4))) return Q8_ERR_ALIGN;
+  return Q8_OK;
+}
+
+// ---- step graph ----------------------------------------------------------
+
+constexpr uint32_t kGraphMagic = 0x51384447u;  // "Q8DG"
+
+}  // namespace
+
+struct q8_step_graph {
+  uint32_t magic;
+  int device;
+  int mode;
+  int32_t kernel_nodes;
+  int32_t memcpy_nodes;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  void *workspace;  // argmax slots (+ descriptor table in persistent mode)
+};
+
+namespace {
+
+std::set<const q8_step_graph *> g_graphs;  // live handles, guarded by g_mu
+
+bool live_graph(const q8_step_graph *g) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return g && g_graphs.count(g) && g->magic == kGraphMagic;
+}
+
+void release_graph(q8_step_graph *g) {
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->workspace) (void)hipFree(g->workspace);
+  g->magic = 0;
+  delete g;
+}
+
+int count_nodes(q8_step_graph *g) {
+  size_t num = 0;
+  hipError_t e = hipGraphGetNodes(g->graph, nullptr, &num);
+  if (e != hipSuccess) return hip_fail(e);
+  std::vector<hipGraphNode_t> nodes(num);
+  if (num) {
+    e = hipGraphGetNodes(g->graph, nodes.data(), &num);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  g->kernel_nodes = 0;
+  g->memcpy_nodes = 0;
+  for (size_t i = 0; i < num; i++) {
+    hipGraphNodeType t;
+    e = hipGraphNodeGetType(nodes[i], &t);
+    if (e != hipSuccess) return hip_fail(e);
+    if (t == hipGraphNodeTypeKernel) g->kernel_nodes++;
+    if (t == hipGraphNodeTypeMemcpy) g->memcpy_nodes++;
+  }
+  return Q8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q8_status_name(int status) {
+  switch (status) {
+    case Q8_OK: return "q8_ok";
+    case Q8_ERR_NULL: return "q8_err_null";
+    case Q8_ERR_SHAPE: return "q8_err_shape";
+    case Q8_ERR_ALIGN: return "q8_err_align";
+    case Q8_ERR_NO_DEVICE: return "q8_err_no_device";
+    case Q8_ERR_ARCH: return "q8_err_arch";
+    case Q8_ERR_CODE_OBJECT: return "q8_err_code_object";
+    case Q8_ERR_HIP: return "q8_err_hip";
+    case Q8_ERR_GRAPH: return "q8_err_graph";
+    case Q8_ERR_BAD_HANDLE: return "q8_err_bad_handle";
+    case Q8_ERR_COUNT: return "q8_err_count";
+    case Q8_ERR_MODE: return "q8_err_mode";
+    default: return "q8_code_out_of_range";
+  }
+}
+
+int q8_last_hip_error(void) { return g_last_hip; }
+
+int q8_device_count(int32_t *count) {
+  if (!count) return Q8_ERR_NULL;
+  int c = 0;
+  if (hipGetDeviceCount(&c) != hipSuccess) {
+    (void)hipGetLastError();
+    c = 0;
+  }
+  *count = c;
+  return Q8_OK;
+}
+
+int q8_init(void) { return ensure_device(nullptr); }
+
+int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
+              void *stream) {
+  int st = check_matvec(w, x, y, nullptr, 1, n, p, true);
+  if (st) return st;
+  if ((st = ensure_device(nullptr))) return st;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, 1, n, p, nullptr,
+                                   nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_matvec_batched(const void *w, const float *x, float *y, int32_t m,
+                      int32_t n, int32_t p, void *stream) {
+  int st = check_matvec(w, x, y, nullptr, m, n, p, true);
+  if (st) return st;
+  if ((st = ensure_device(nullptr))) return st;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, m, n, p, nullptr,
+                                   nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_argmax(const float *logits, int32_t m, int32_t p, int32_t *idx,
+              void *stream) {
+  if (m < 1 || m > Q8_MAX_M || p < 1) return Q8_ERR_SHAPE;
+  if (!logits || !idx) return Q8_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(idx, 4)) return Q8_ERR_ALIGN;
+  int dev = 0;
+  int st = ensure_device(&dev);
+  if (st) return st;
+  hipError_t e = q8::launch_argmax(logits, m, p, g_dev[dev].slot, idx,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
+                     int32_t *idx, int32_t m, int32_t n, int32_t p,
+                     void *stream) {
+  if (!idx) return Q8_ERR_NULL;
+  int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
+  if (st) return st;
+  int dev = 0;
+  if ((st = ensure_device(&dev))) return st;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
+                                   g_dev[dev].slot, idx, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
+                        int32_t *host_idx, int32_t mode, void *stream,
+                        q8_step_graph **out) {
+  (void)stream;
+  if (!out || !descs) return Q8_ERR_NULL;
+  *out = nullptr;
+  if (count < 1 || count > Q8_MAX_DESCS) return Q8_ERR_COUNT;
+  if (mode != Q8_GRAPH_CHAIN && mode != Q8_GRAPH_PERSISTENT) return Q8_ERR_MODE;
+  if (m < 1 || m > Q8_MAX_M) return Q8_ERR_SHAPE;
+  int nargmax = 0;
+  for (int32_t i = 0; i < count; i++) {
+    const q8_matvec_desc &d = descs[i];
+    int st = check_matvec(d.w, d.x, d.y, d.idx, m, d.n, d.p, d.idx == nullptr);
+    if (st) return st;
+    if (d.idx) nargmax++;
+  }
+  if (nargmax > Q8_MAX_ARGMAX_DESCS) return Q8_ERR_COUNT;
+  if (host_idx && !aligned(host_idx, 4)) return Q8_ERR_ALIGN;
+  int dev = 0;
+  int st = ensure_device(&dev);
+  if (st) return st;
+  if (mode == Q8_GRAPH_PERSISTENT && q8::step_grid(dev) <= 0) return Q8_ERR_MODE;
+
+  q8_step_graph *g = new (std::nothrow) q8_step_graph();
+  if (!g) return Q8_ERR_GRAPH;
+  g->magic = kGraphMagic;
+  g->device = dev;
+  g->mode = mode;
+  // one argmax slot per argmax descriptor
+  size_t ws = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
+  hipError_t e = hipMalloc(&g->workspace, ws);
+  if (e == hipSuccess) e = hipMemset(g->workspace, 0, ws);
+  if (e != hipSuccess) {
+    release_graph(g);
+    return hip_fail(e);
+  }
+  q8::ArgmaxSlot *slots = (q8::ArgmaxSlot *)g->workspace;
+
+  hipStream_t cs = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    release_graph(g);
+    return hip_fail(e);
+  }
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  hipError_t le = hipSuccess;
+  if (e == hipSuccess) {
+    if (mode == Q8_GRAPH_CHAIN) {
+      int a = 0;
+      for (int32_t i = 0; i < count && le == hipSuccess; i++) {
+        const q8_matvec_desc &d = descs[i];
+        q8::ArgmaxSlot *slot = d.idx ? &slots[a++] : nullptr;
+        le = q8::launch_matvec((const uint8_t *)d.w, d.x, d.y, m, d.n, d.p,
+                               slot, d.idx, cs);
+      }
+    } else {
+      le = hipErrorNotSupported;
+    }
+    if (le == hipSuccess && host_idx) {
+      int a = 0;
+      for (int32_t i = 0; i < count && le == hipSuccess; i++) {
+        if (!descs[i].idx) continue;
+        le = hipMemcpyAsync(host_idx + (size_t)a * m, descs[i].idx,
+                            sizeof(int32_t) * m, hipMemcpyDeviceToHost, cs);
+        a++;
+      }
+    }
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    g->graph = graph;
+  }
+  (void)hipStreamDestroy(cs);
+  if (le != hipSuccess || e != hipSuccess || !g->graph) {
+    g_last_hip = (int)(le != hipSuccess ? le : e);
+    release_graph(g);
+    return Q8_ERR_GRAPH;
+  }
+  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    release_graph(g);
+    return Q8_ERR_GRAPH;
+  }
+  st = count_nodes(g);
+  if (st) {
+    release_graph(g);
+    return st;
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_graphs.insert(g);
+  }
+  *out = g;
+  return Q8_OK;
+}
+
+int q8_step_graph_launch(q8_step_graph *g, void *stream) {
+  if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
+  hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_step_graph_info(const q8_step_graph *g, int32_t *kernel_nodes,
+                       int32_t *memcpy_nodes) {
+  if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
+  if (kernel_nodes) *kernel_nodes = g->kernel_nodes;
+  if (memcpy_nodes) *memcpy_nodes = g->memcpy_nodes;
+  return Q8_OK;
+}
+
+int q8_step_graph_destroy(q8_step_graph *g) {
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g || !g_graphs.count(g) || g->magic != kGraphMagic)
+      return Q8_ERR_BAD_HANDLE;
+    g_graphs.erase(g);
+  }
+  release_graph(g);
+  return Q8_OK;
+}
+
+}  // extern "C"

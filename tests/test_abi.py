@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/q8dec.h declares, names its status codes, and refuses bad arguments
+before any GPU work.  Every call here carries an invalid argument, so it can
+never reach a kernel launch, with or without a device."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import q8_block_quantized_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, ALIGN, NODEV = 0, 1, 2, 3, 4
+BAD_HANDLE, COUNT, MODE = 9, 10, 11
+
+# fake device addresses: aligned, never dereferenced (each call below fails
+# validation first)
+W, X, Y, I = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q8.load()
+
+
+def declared_functions():
+    with open(q8.HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", q8.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (q8_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+
+
+def test_status_names(lib):
+    want = {0: "q8_ok", 1: "q8_err_null", 2: "q8_err_shape", 3: "q8_err_align",
+            4: "q8_err_no_device", 5: "q8_err_arch", 6: "q8_err_code_object",
+            7: "q8_err_hip", 8: "q8_err_graph", 9: "q8_err_bad_handle",
+            10: "q8_err_count", 11: "q8_err_mode"}
+    for code, name in want.items():
+        assert q8.q8_status_name(code) == name
+    for code in (-1, 12, 99, 1 << 30):
+        assert q8.q8_status_name(code) == "q8_code_out_of_range"
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, X, Y, 32, 1), NULL),
+    ((W, None, Y, 32, 1), NULL),
+    ((W, X, None, 32, 1), NULL),
+    ((W, X, Y, 33, 1), SHAPE),
+    ((W, X, Y, -32, 1), SHAPE),
+    ((W, X, Y, 65536 + 32, 1), SHAPE),
+    ((W, X, Y, 32, -1), SHAPE),
+    ((W + 2, X, Y, 32, 1), ALIGN),
+    ((W + 8, X, Y, 32, 1), ALIGN),
+    ((W, X + 4, Y, 32, 1), ALIGN),
+    ((W, X, Y + 2, 32, 1), ALIGN),
+])
+def test_matvec_refusals(lib, args, want):
+    assert lib.q8_matvec(*args, None) == want
+
+
+@pytest.mark.parametrize("m,n,p,want", [
+    (0, 32, 1, SHAPE), (9, 32, 1, SHAPE), (-1, 32, 1, SHAPE),
+    (2, 31, 1, SHAPE), (2, 32, -5, SHAPE),
+])
+def test_batched_refusals(lib, m, n, p, want):
+    assert lib.q8_matvec_batched(W, X, Y, m, n, p, None) == want
+
+
+def test_argmax_refusals(lib):
+    assert lib.q8_argmax(X, 1, 0, I, None) == SHAPE
+    assert lib.q8_argmax(X, 0, 5, I, None) == SHAPE
+    assert lib.q8_argmax(X, 9, 5, I, None) == SHAPE
+    assert lib.q8_argmax(None, 1, 5, I, None) == NULL
+    assert lib.q8_argmax(X, 1, 5, None, None) == NULL
+    assert lib.q8_argmax(X + 2, 1, 5, I, None) == ALIGN
+    assert lib.q8_argmax(X, 1, 5, I + 1, None) == ALIGN
+
+
+def test_matvec_argmax_refusals(lib):
+    assert lib.q8_matvec_argmax(W, X, None, None, 1, 32, 4, None) == NULL
+    assert lib.q8_matvec_argmax(W, X, None, I, 1, 32, 0, None) == SHAPE
+    assert lib.q8_matvec_argmax(W, X, None, I, 9, 32, 4, None) == SHAPE
+    assert lib.q8_matvec_argmax(None, X, None, I, 1, 32, 4, None) == NULL
+    assert lib.q8_matvec_argmax(W, X, Y + 1, I, 1, 32, 4, None) == ALIGN
+
+
+def _descs(k, **over):
+    arr = (q8.MatvecDesc * k)()
+    for i in range(k):
+        d = dict(w=W, x=X, y=Y, idx=None, n=32, p=4)
+        d.update(over)
+        arr[i] = q8.MatvecDesc(d["w"], d["x"], d["y"], d["idx"], d["n"], d["p"])
+    return arr
+
+
+def test_step_graph_refusals(lib):
+    h = ctypes.c_void_p(None)
+    b = lib.q8_step_graph_build
+    assert b(_descs(1), 1, 1, None, 0, None, None) == NULL
+    assert b(None, 1, 1, None, 0, None, ctypes.byref(h)) == NULL
+    assert b(_descs(1), 0, 1, None, 0, None, ctypes.byref(h)) == COUNT
+    assert b(_descs(1), 4097, 1, None, 0, None, ctypes.byref(h)) == COUNT
+    assert b(_descs(1), 1, 1, None, 7, None, ctypes.byref(h)) == MODE
+    assert b(_descs(1), 1, 0, None, 0, None, ctypes.byref(h)) == SHAPE
+    assert b(_descs(1), 1, 9, None, 0, None, ctypes.byref(h)) == SHAPE
+    assert b(_descs(2, n=40), 2, 1, None, 0, None, ctypes.byref(h)) == SHAPE
+    assert b(_descs(2, y=None), 2, 1, None, 0, None, ctypes.byref(h)) == NULL
+    assert b(_descs(2, w=W + 4), 2, 1, None, 0, None, ctypes.byref(h)) == ALIGN
+    assert b(_descs(65, idx=I), 65, 1, None, 0, None, ctypes.byref(h)) == COUNT
+    assert b(_descs(1), 1, 1, I + 2, 0, None, ctypes.byref(h)) == ALIGN
+    assert h.value is None
+
+
+def test_graph_handle_refusals(lib):
+    fake = ctypes.c_void_p(0x12345678)
+    k = ctypes.c_int32(0)
+    assert lib.q8_step_graph_launch(None, None) == BAD_HANDLE
+    assert lib.q8_step_graph_launch(fake, None) == BAD_HANDLE
+    assert lib.q8_step_graph_info(None, ctypes.byref(k), None) == BAD_HANDLE
+    assert lib.q8_step_graph_info(fake, ctypes.byref(k), None) == BAD_HANDLE
+    assert lib.q8_step_graph_destroy(None) == BAD_HANDLE
+    assert lib.q8_step_graph_destroy(fake) == BAD_HANDLE
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import q8_block_quantized_amd as q8
+lib = q8.load()
+c = ctypes.c_int32(-1)
+assert lib.q8_device_count(ctypes.byref(c)) == 0
+if c.value != 0:
+    print("SKIP device visible")
+    sys.exit(0)
+W, X, Y, I = 0x10000, 0x20000, 0x30000, 0x40000
+codes = [lib.q8_init(),
+         lib.q8_matvec(W, X, Y, 32, 1, None),
+         lib.q8_matvec_batched(W, X, Y, 2, 32, 1, None),
+         lib.q8_argmax(X, 1, 4, I, None),
+         lib.q8_matvec_argmax(W, X, None, I, 1, 32, 4, None)]
+print("CODES", codes)
+"""
+
+
+def test_no_device_is_reported():
+    """With no visible device every valid call returns Q8_ERR_NO_DEVICE.
+    Runs in a child process with the devices hidden, and only proceeds past
+    the device count when that count is zero."""
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    out = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT, ROOT],
+                         capture_output=True, text=True, env=env, timeout=120)
+    assert out.returncode == 0, out.stderr
+    if "SKIP" in out.stdout:
+        pytest.skip("a device stayed visible")
+    assert f"CODES {[NODEV] * 5}" in out.stdout, out.stdout

@@ -1,0 +1,142 @@
+"""GPU tests of the recorded decode step (q8_step_graph_*).
+
+A step is the model-order sequence of matvecs (q, k, v, o, gate, up, down per
+layer, then the lm_head with its fused argmax), each with its own seeded x,
+recorded once and launched as one graph; one int32 per activation row comes
+back to pinned host memory."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from tests.gpu_helpers import assert_parity, cuda, say, to_dev  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+
+def step_inputs(layers: int, lm_p: int, m: int, seed: int = 0):
+    shapes = [(f"L{l}.{name}", n, p) for l in range(layers)
+              for name, n, p in gen.LAYER_SHAPES]
+    shapes.append(("lm_head", 1024, lm_p))
+    ws, xs = [], []
+    for i, (_, n, p) in enumerate(shapes):
+        ws.append(gen.weights(p, n, seed=seed, index=i))
+        xs.append(gen.activations(m, n, seed=seed, index=i))
+    return shapes, ws, xs
+
+
+def device_step(shapes, ws, xs, m, device, lm_logits=True):
+    import torch
+    descs = []
+    for i, (name, n, p) in enumerate(shapes):
+        last = i == len(shapes) - 1
+        d = dict(n=n, p=p, w=to_dev(ws[i].reshape(-1), device),
+                 x=to_dev(xs[i], device), idx=None,
+                 y=torch.full((m, p), float("nan"), dtype=torch.float32, device=device))
+        if last:
+            d["idx"] = torch.full((m,), -7, dtype=torch.int32, device=device)
+            if not lm_logits:
+                d["y"] = None
+        descs.append(d)
+    return descs
+
+
+def run_graph(descs, m, mode, device):
+    import torch
+    import q8_block_quantized_amd as q8
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, mode=mode, device=device)
+    return g, host
+
+
+@pytest.mark.parametrize("mode", [0])
+def test_small_step_matches_standalone_calls(cuda, mode):
+    """Graph outputs equal the standalone calls bit for bit, on every replay,
+    with eager work between replays; node counts match the descriptors."""
+    import torch
+    import q8_block_quantized_amd as q8
+    m = 1
+    shapes, ws, xs = step_inputs(2, 20000, m, seed=3)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, mode, cuda)
+    k, c = g.info()
+    assert (k, c) == ((len(shapes), 1) if mode == 0 else (1, 1))
+    # standalone results
+    want = []
+    for d in descs[:-1]:
+        y = torch.empty_like(d["y"])
+        q8.q8_matvec(d["w"], d["x"].view(-1), y.view(-1))
+        want.append(y)
+    lm = descs[-1]
+    idx_ref = torch.empty(m, dtype=torch.int32, device=cuda)
+    y_lm = torch.empty_like(lm["y"])
+    q8.q8_matvec_argmax(lm["w"], lm["x"], idx_ref, lm["p"], y=y_lm)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        lm["idx"].fill_(-9)
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        for i, d in enumerate(descs[:-1]):
+            assert torch.equal(d["y"], want[i]), f"rep {rep} desc {i}"
+        assert torch.equal(lm["y"], y_lm), f"rep {rep} lm logits"
+        assert lm["idx"].item() == idx_ref.item() == host[0].item(), f"rep {rep}"
+    g.close()
+
+
+@pytest.mark.parametrize("mode", [0])
+def test_full_step_against_oracle(cuda, mode):
+    """All 197 matvecs of a step (28 layers + lm_head), every output."""
+    import torch
+    m = 1
+    say("full step: generating 197 matvecs")
+    shapes, ws, xs = step_inputs(28, 151936, m, seed=0)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, mode, cuda)
+    assert g.info() == ((197, 1) if mode == 0 else (1, 1))
+    g.launch()
+    torch.cuda.synchronize()
+    say("full step: checking against the oracle")
+    for i, (name, n, p) in enumerate(shapes):
+        ref, tol = oracle.get().matvec_mt(ws[i], xs[i][0], 16)[:2]
+        y = descs[i]["y"].cpu().numpy()[0]
+        assert_parity(y, ref, tol, name)
+        if i == len(shapes) - 1:
+            assert oracle.argmax_accepted(int(host[0]), ref, tol)
+            assert int(host[0]) == oracle.argmax_f32(y)
+    g.close()
+
+
+@pytest.mark.parametrize("mode", [0])
+def test_batched_step(cuda, mode):
+    """m = 8 rows through every shape of a step (4 layers + lm_head here, the
+    full 28 layers in the benchmark), argmax per row."""
+    import torch
+    m = 8
+    shapes, ws, xs = step_inputs(4, 151936, m, seed=1)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, mode, cuda)
+    g.launch()
+    torch.cuda.synchronize()
+    for i, (name, n, p) in enumerate(shapes):
+        ref, tol = oracle.matvec_batched(ws[i], xs[i])
+        y = descs[i]["y"].cpu().numpy()
+        assert_parity(y, ref, tol, f"m=8 {name}")
+        if i == len(shapes) - 1:
+            for r in range(m):
+                assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+                assert int(host[r]) == oracle.argmax_f32(y[r])
+    g.close()
+
+
+def test_destroyed_handle_is_refused(cuda):
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(0, 64, 1, seed=4)
+    descs = device_step(shapes, ws, xs, 1, cuda)
+    g, _ = run_graph(descs, 1, 0, cuda)
+    h = g._h
+    g.close()
+    assert q8.load().q8_step_graph_launch(h, None) == 9
+    assert q8.load().q8_step_graph_destroy(h) == 9
