@@ -1,0 +1,325 @@
+"""Benchmark of the Q8_0 decode matvec path on one MI355X.
+
+A step is one full decode step's matvecs: 28 layers x (q, k, v, o, gate, up,
+down) plus the lm_head 1024 -> 151,936 with its fused argmax = 197 Q8_0
+matvecs, recorded once as a hipGraph and launched once, with one int32 read
+back to pinned host memory.  Inputs are seeded synthetic stand-ins for the
+Qwen3-0.6B weights (see gen/): two full weight sets (1.27 GB, beyond the
+256 MB Infinity Cache) are alternated step by step, so every step streams
+its weights from HBM.
+
+Prints one JSON line on stdout (progress goes to stderr).  The timed region
+is exactly --steps steps, bracketed by device synchronisation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = ("Q8_0 matvec HBM GB/s (% of peak) + 197-matvec decode-step "
+          "latency (µs)")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(n: int, p: int, m: int, logits: bool, argmax: bool) -> int:
+    """Algorithmic bytes of one matvec: weight blocks + x + outputs."""
+    return (p * (n // 32) * 34 + m * n * 4 + (m * p * 4 if logits else 0)
+            + (m * 4 if argmax else 0))
+
+
+class StepSet:
+    """Device buffers of one decode step's 197 matvecs (one weight set)."""
+
+    def __init__(self, torch, dev, seed: int, base: int, m: int, lm_logits: bool,
+                 weights=None):
+        self.shapes = gen.step_shapes()
+        self.descs = []
+        self.w = weights if weights is not None else []
+        for i, (name, n, p) in enumerate(self.shapes):
+            if weights is None:
+                w = gen.weights(p, n, seed=seed, index=base + i)
+                self.w.append(torch.from_numpy(w.reshape(-1)).to(dev))
+            x = torch.from_numpy(gen.activations(m, n, seed=seed, index=base + i)).to(dev)
+            last = i == len(self.shapes) - 1
+            y = None
+            if not last or lm_logits:
+                y = torch.empty((m, p), dtype=torch.float32, device=dev)
+            idx = torch.full((m,), -1, dtype=torch.int32, device=dev) if last else None
+            self.descs.append(dict(w=self.w[i], x=x, y=y, idx=idx, n=n, p=p))
+        self.bytes = sum(alg_bytes(d["n"], d["p"], m, d["y"] is not None,
+                                   d["idx"] is not None) for d in self.descs)
+        self.weight_bytes = sum(p * (n // 32) * 34 for _, n, p in self.shapes)
+
+
+def time_graph_steps(torch, graphs, host, steps: int, warmup: int):
+    """Launch + sync + read the token per step; returns wall seconds/step."""
+    stream = torch.cuda.current_stream()
+    for k in range(warmup):
+        graphs[k % len(graphs)].launch()
+        stream.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks = []
+    for k in range(steps):
+        graphs[k % len(graphs)].launch()
+        stream.synchronize()
+        toks.append(int(host[0]))
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, toks
+
+
+def event_time(torch, fn, count: int, warmup: int = 3) -> float:
+    """Average HIP-event time (s) per call of fn(k), k = 0..count-1, issued
+    back to back on torch's current stream between one pair of events (the
+    GPU never waits on the host inside the bracket)."""
+    for k in range(warmup):
+        fn(k)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(count):
+        fn(k)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / count
+
+
+def cpu_baseline(sets, m_host, threads_req: int, budget_s: float):
+    """The oracle on the host cores over the first weight set's step, and a
+    parity check of the GPU outputs of that step against it."""
+    import oracle
+    orc = oracle.get()
+    s0 = sets
+    ws = [w for w in m_host["w"]]
+    xs = m_host["x"]
+    times = []
+    used = 1
+    worst = 0.0
+    ok_idx = True
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        ys = []
+        for i, (name, n, p) in enumerate(s0.shapes):
+            y, tol, used = orc.matvec_mt(ws[i], xs[i][0], threads_req)
+            ys.append((y, tol))
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 or time.perf_counter() - t_start > budget_s:
+            break
+    # parity of the GPU step outputs (written by the last launch of set 0)
+    for i, d in enumerate(s0.descs):
+        y, tol = ys[i]
+        if d["y"] is not None:
+            g = d["y"].cpu().numpy()[0]
+            worst = max(worst, float(oracle.matvec_errors(g, y, tol).max()))
+        if d["idx"] is not None:
+            ok_idx = ok_idx and oracle.argmax_accepted(int(d["idx"][0].item()), y, tol)
+    return statistics.median(times), used, worst, ok_idx
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline step (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X "
+              "and has no multi-GPU path; use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import q8_block_quantized_amd as q8
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q8.q8_init()
+    log("generating two weight sets of a decode step (2 x 633 MB)")
+    sets = [StepSet(torch, dev, 0, 0, 1, False), StepSet(torch, dev, 0, 1000, 1, False)]
+    host = torch.zeros(1, dtype=torch.int32).pin_memory()
+    pers = [q8.StepGraph(s.descs, 1, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT)
+            for s in sets]
+    bare = [q8.StepGraph(s.descs, 1, mode=q8.Q8_GRAPH_PERSISTENT) for s in sets]
+    assert pers[0].info() == (1, 1)
+    step_bytes = sets[0].bytes
+
+    log(f"headline: {args.steps} persistent-graph steps")
+    sec, toks = time_graph_steps(torch, pers, host, args.steps, args.warmup)
+    # dominant kernel: the step kernel alone (graph without the readback)
+    k_avg = event_time(torch, lambda k: bare[k % 2].launch(), args.steps)
+    achieved = step_bytes / k_avg / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / sec / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("full decode step: 197 Q8_0 matvecs (28 layers x q,k,v,"
+                         "o,gate,up,down + lm_head 1024->151936 with fused argmax), "
+                         "m=1, one persistent-kernel hipGraph launch + one int32 "
+                         "readback per step, 2 weight sets alternated (1.27 GB)"),
+            "matvecs": 197,
+            "m": 1,
+            "weight_bytes_per_step": sets[0].weight_bytes,
+            "alg_bytes_per_step": step_bytes,
+            "graph_nodes": {"kernel": 1, "memcpy": 1},
+        },
+        "step_latency_us": round(sec * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * step_bytes / sec / 1e9 / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "step_kernel (persistent, 197 matvecs)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(k_avg * 1e6, 2),
+        },
+    }
+
+    extra = {}
+    if not args.no_extra:
+        steps2 = max(5, min(args.steps, 50))
+        log("chain graph (197 kernel nodes)")
+        chain = [q8.StepGraph(s.descs, 1, host_idx=host, mode=q8.Q8_GRAPH_CHAIN)
+                 for s in sets]
+        assert chain[0].info() == (197, 1)
+        csec, ctoks = time_graph_steps(torch, chain, host, steps2, 3)
+        extra["chain_graph_197_nodes"] = {
+            "step_latency_us": round(csec * 1e6, 2),
+            "GBps": round(step_bytes / csec / 1e9, 1),
+            "per_node_us": round(csec * 1e6 / 197, 3),
+        }
+        for g in chain:
+            g.close()
+
+        log("lm_head fused (4 copies rotated)")
+        lm_extra = [torch.from_numpy(gen.weights(151936, 1024, seed=0, index=2000 + c)
+                                     .reshape(-1)).to(dev) for c in range(2)]
+        lm_w = [sets[0].w[-1], sets[1].w[-1]] + lm_extra
+        lm_x = sets[0].descs[-1]["x"]
+        lm_idx = torch.empty(1, dtype=torch.int32, device=dev)
+        lt = event_time(torch, lambda k: q8.q8_matvec_argmax(
+            lm_w[k % 4], lm_x, lm_idx, 151936), 40)
+        lb = alg_bytes(1024, 151936, 1, False, True)
+        extra["lm_head_fused"] = {
+            "avg_us": round(lt * 1e6, 2),
+            "GBps": round(lb / lt / 1e9, 1),
+            "pct_of_peak": round(100 * lb / lt / 1e9 / HBM_PEAK_GBS, 2),
+            "alg_bytes": lb,
+        }
+        lm_y = torch.empty(151936, dtype=torch.float32, device=dev)
+        lt0 = event_time(torch, lambda k: q8.q8_matvec(
+            lm_w[k % 4], lm_x.view(-1), lm_y), 40)
+        lb0 = alg_bytes(1024, 151936, 1, True, False)
+        extra["lm_head_matvec_only"] = {
+            "avg_us": round(lt0 * 1e6, 2),
+            "GBps": round(lb0 / lt0 / 1e9, 1),
+        }
+
+        log("single matvec 1024->2048 (rotating 56 layer copies)")
+        qs = [d for s in sets for d in s.descs if d["p"] == 2048 and d["n"] == 1024]
+        qy = torch.empty(2048, dtype=torch.float32, device=dev)
+        st = event_time(torch, lambda k: q8.q8_matvec(
+            qs[k % len(qs)]["w"], qs[k % len(qs)]["x"].view(-1), qy), 112)
+        sb = alg_bytes(1024, 2048, 1, True, False)
+        extra["single_matvec_1024x2048"] = {
+            "avg_us": round(st * 1e6, 2),
+            "GBps": round(sb / st / 1e9, 1),
+            "note": "back-to-back launches, 56 distinct copies (125 MB) rotated",
+        }
+
+        log("one layer: 7 matvecs back to back (56 layers rotated)")
+        layers = [s.descs[7 * l:7 * l + 7] for s in sets for l in range(28)]
+
+        def run_layer(k):
+            for d in layers[k % len(layers)]:
+                q8.q8_matvec(d["w"], d["x"].view(-1), d["y"].view(-1))
+        lt2 = event_time(torch, run_layer, 56)
+        lyb = sum(alg_bytes(n, p, 1, True, False) for _, n, p in gen.LAYER_SHAPES)
+        extra["layer_7_matvecs_stream"] = {
+            "avg_us": round(lt2 * 1e6, 2),
+            "GBps": round(lyb / lt2 / 1e9, 1),
+        }
+
+        log("batched m=8 step (persistent graph)")
+        sets8 = [StepSet(torch, dev, 0, 5000 + 1000 * j, 8, False, weights=s.w)
+                 for j, s in enumerate(sets)]
+        host8 = torch.zeros(8, dtype=torch.int32).pin_memory()
+        p8 = [q8.StepGraph(s.descs, 8, host_idx=host8, mode=q8.Q8_GRAPH_PERSISTENT)
+              for s in sets8]
+        s8, _ = time_graph_steps(torch, p8, host8, steps2, 3)
+        b8 = sets8[0].bytes
+        extra["batched_m8_step"] = {
+            "step_latency_us": round(s8 * 1e6, 2),
+            "GBps": round(b8 / s8 / 1e9, 1),
+            "per_row_us": round(s8 * 1e6 / 8, 2),
+            "per_row_vs_m1": round((s8 / 8) / sec, 3),
+        }
+        for g in p8:
+            g.close()
+    if extra:
+        result["extra"] = extra
+
+    if not args.no_cpu:
+        log("cpu baseline: the oracle on the host cores")
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            ncpu = os.cpu_count() or 1
+        m_host = {"w": [], "x": []}
+        for i, (name, n, p) in enumerate(sets[0].shapes):
+            m_host["w"].append(gen.weights(p, n, seed=0, index=i))
+            m_host["x"].append(gen.activations(1, n, seed=0, index=i))
+        # the GPU outputs compared below come from one launch of set 0
+        pers[0].launch()
+        torch.cuda.synchronize()
+        csec_, used, worst, ok_idx = cpu_baseline(sets[0], m_host, ncpu, 20.0)
+        result["cpu_baseline"] = {
+            "value": round(step_bytes / csec_ / 1e9, 3),
+            "unit": "GB/s",
+            "cores": used,
+            "kind": "oracle",
+            "sample": ("the full 197-matvec step (set 0) computed by the oracle, "
+                       "rows split over the host cores; median of up to 3 runs"),
+            "step_latency_us": round(csec_ * 1e6, 1),
+            "gpu_parity_max_err_over_tol": round(worst, 5),
+            "gpu_argmax_accepted": bool(ok_idx),
+        }
+    print(json.dumps(result), flush=True)
+    for g in pers + bare:
+        g.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

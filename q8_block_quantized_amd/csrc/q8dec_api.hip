@@ -10,6 +10,7 @@
 // decoder slot remembers a failed start and never retries it).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -160,6 +161,102 @@ int count_nodes(q8_step_graph *g) {
 
 }  // namespace
 
+namespace q8 {
+
+// Plans a persistent step: tiles per descriptor (in descriptor order), the
+// dynamic LDS (staged tile and the widest x), the grid (the
+// resident workgroups, at most one per tile), groups of `group_size`
+// workgroups with contiguous tile ranges of about equal weight bytes, and
+// for every argmax descriptor the arrivals each argmax team waits for.
+int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
+              int group_size, StepPlan &plan) {
+  plan.descs.assign(count, StepDesc());
+  plan.all_staged = true;
+  int64_t tiles = 0;
+  size_t widest = 0;
+  for (int32_t i = 0; i < count; i++) {
+    const q8_matvec_desc &d = descs[i];
+    StepDesc &t = plan.descs[i];
+    std::memset(&t, 0, sizeof(t));
+    t.w = (const uint8_t *)d.w;
+    t.x = d.x;
+    t.y = d.y;
+    t.idx = d.idx;
+    t.n = d.n;
+    t.p = d.p;
+    t.rows_per_tile = step_rows_per_tile(d.n, m);
+    t.tile_begin = (int32_t)tiles;
+    tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
+    if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
+    const size_t l = step_lds_bytes(m, d.n);
+    if (l > widest) widest = l;
+    plan.all_staged = plan.all_staged && step_all_staged(m, d.n);
+  }
+  if (tiles < 1) return Q8_ERR_SHAPE;  // nothing to run
+  const int32_t ntiles = (int32_t)tiles;
+  plan.lds = widest;
+  int grid = step_grid(dev, m, plan.lds, plan.all_staged);
+  if (grid > ntiles) grid = ntiles;
+  if (grid < 1) grid = 1;
+  if (group_size < 1) group_size = 1;
+  if (group_size > grid) group_size = grid;
+  plan.grid = grid;
+  plan.group_size = group_size;
+  // prefix sums of tile weight bytes
+  std::vector<int64_t> pre((size_t)ntiles + 1, 0);
+  for (int32_t i = 0, t = 0; i < count; i++) {
+    const StepDesc &d = plan.descs[i];
+    const int64_t pitch = (int64_t)(d.n / 32) * 34;
+    for (int32_t r0 = 0; r0 < d.p; r0 += d.rows_per_tile, t++) {
+      const int32_t rows = d.p - r0 < d.rows_per_tile ? d.p - r0 : d.rows_per_tile;
+      pre[t + 1] = pre[t] + rows * pitch + 1;  // +1: zero-width tiles still count
+    }
+  }
+  const int ngroups = (grid + group_size - 1) / group_size;
+  plan.groups.resize(ngroups);
+  int32_t prev_end = 0;
+  for (int a = 0; a < ngroups; a++) {
+    WgGroup &gr = plan.groups[a];
+    gr.first = a * group_size;
+    gr.size = grid - gr.first < group_size ? grid - gr.first : group_size;
+    gr.t0 = prev_end;
+    const int64_t target =
+        (int64_t)((__int128)pre[ntiles] * (gr.first + gr.size) / grid);
+    int32_t e = a == ngroups - 1
+                    ? ntiles
+                    : (int32_t)(std::lower_bound(pre.begin(), pre.end(), target) -
+                                pre.begin());
+    if (e < gr.t0) e = gr.t0;
+    gr.t1 = e;
+    prev_end = e;
+  }
+  // arrivals of each argmax descriptor, by team
+  plan.expected.clear();
+  for (int32_t i = 0; i < count; i++) {
+    const StepDesc &d = plan.descs[i];
+    if (!d.idx) continue;
+    std::vector<uint32_t> team(kArgmaxTeams, 0);
+    const int32_t tb = d.tile_begin, te = tb + (d.p + d.rows_per_tile - 1) / d.rows_per_tile;
+    for (const WgGroup &gr : plan.groups) {
+      const int32_t u = gr.t0 > tb ? gr.t0 : tb, v = gr.t1 < te ? gr.t1 : te;
+      if (u >= v) continue;
+      for (int32_t j = 0; j < gr.size; j++) {
+        int32_t t = gr.t0 + j;
+        if (t < u) t += (u - t + gr.size - 1) / gr.size * gr.size;
+        if (t < v) team[(gr.first + j) % kArgmaxTeams]++;
+      }
+    }
+    plan.expected.push_back(team);
+  }
+  return Q8_OK;
+}
+
+}  // namespace q8
+
+namespace {
+
+}  // namespace
+
 extern "C" {
 
 const char *q8_status_name(int status) {
@@ -262,22 +359,62 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   int dev = 0;
   int st = ensure_device(&dev);
   if (st) return st;
-  if (mode == Q8_GRAPH_PERSISTENT && q8::step_grid(dev) <= 0) return Q8_ERR_MODE;
 
   q8_step_graph *g = new (std::nothrow) q8_step_graph();
   if (!g) return Q8_ERR_GRAPH;
   g->magic = kGraphMagic;
   g->device = dev;
   g->mode = mode;
-  // one argmax slot per argmax descriptor
-  size_t ws = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
-  hipError_t e = hipMalloc(&g->workspace, ws);
-  if (e == hipSuccess) e = hipMemset(g->workspace, 0, ws);
+
+  // workspace: one argmax slot per argmax descriptor, then (persistent mode)
+  // the device copies of the descriptor table and the workgroup ranges
+  const size_t slot_bytes = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
+  q8::StepPlan plan;
+  if (mode == Q8_GRAPH_PERSISTENT) {
+    st = q8::plan_step(descs, count, m, dev, q8::kStepGroupSize, plan);
+    if (st) {
+      release_graph(g);
+      return st;
+    }
+  }
+  const size_t table_bytes = plan.descs.size() * sizeof(q8::StepDesc);
+  const size_t group_bytes = plan.groups.size() * sizeof(q8::WgGroup);
+  const size_t total = slot_bytes + table_bytes + group_bytes;
+  hipError_t e = hipMalloc(&g->workspace, total);
+  if (e == hipSuccess) e = hipMemset(g->workspace, 0, total);
   if (e != hipSuccess) {
     release_graph(g);
     return hip_fail(e);
   }
   q8::ArgmaxSlot *slots = (q8::ArgmaxSlot *)g->workspace;
+  q8::StepDesc *table = (q8::StepDesc *)((char *)g->workspace + slot_bytes);
+  q8::WgGroup *groups =
+      (q8::WgGroup *)((char *)g->workspace + slot_bytes + table_bytes);
+  if (mode == Q8_GRAPH_PERSISTENT) {
+    // argmax slots: keys and counters zero, arrival counts from the plan
+    std::vector<q8::ArgmaxSlot> hs(nargmax ? nargmax : 1);
+    std::memset(hs.data(), 0, hs.size() * sizeof(q8::ArgmaxSlot));
+    int a = 0;
+    for (auto &t : plan.descs) {
+      if (!t.idx) continue;
+      uint32_t nteams = 0;
+      for (int j = 0; j < q8::kArgmaxTeams; j++) {
+        hs[a].team[j].expected = plan.expected[a][j];
+        nteams += plan.expected[a][j] ? 1u : 0u;
+      }
+      hs[a].top.expected = nteams;
+      t.slot = &slots[a++];
+    }
+    e = hipMemcpy(slots, hs.data(), slot_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(table, plan.descs.data(), table_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(groups, plan.groups.data(), group_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      release_graph(g);
+      return hip_fail(e);
+    }
+  }
 
   hipStream_t cs = nullptr;
   e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
@@ -297,7 +434,8 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                                slot, d.idx, cs);
       }
     } else {
-      le = hipErrorNotSupported;
+      le = q8::launch_step(table, count, groups, plan.group_size, m, plan.grid,
+                           plan.lds, plan.all_staged, cs);
     }
     if (le == hipSuccess && host_idx) {
       int a = 0;

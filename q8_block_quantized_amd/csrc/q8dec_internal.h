@@ -5,19 +5,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace q8 {
 
-// Cross-workgroup argmax workspace for one launch: one 64-bit key per
-// activation row and an arrival counter.  Zero between launches: the last
-// workgroup of every launch reads the keys and clears them and the counter.
-struct ArgmaxSlot {
+// One arrival group of the cross-workgroup argmax: a 64-bit key per
+// activation row, an arrival counter and the number of arrivals it waits
+// for (0: every workgroup of the grid arrives once, and the kernel works the
+// count out itself), padded to 256 bytes.
+struct ArgmaxGroup {
   unsigned long long keys[8];
   unsigned int counter;
-  unsigned int pad[15];
+  unsigned int expected;
+  unsigned int pad[46];
 };
-static_assert(sizeof(ArgmaxSlot) == 128, "slot layout");
+static_assert(sizeof(ArgmaxGroup) == 256, "group layout");
 
-// One matvec of a persistent step, as stored in device memory.
+constexpr int kArgmaxTeams = 64;
+
+// Argmax workspace of one matvec.  An arriving workgroup g joins team
+// g % kArgmaxTeams; the last arrival of a team forwards the team's keys to
+// the top group, and the last team writes the indices.  Keys and counters
+// are zero between launches: the arrival that completes a group reads and
+// clears them.
+struct ArgmaxSlot {
+  ArgmaxGroup top;
+  ArgmaxGroup team[kArgmaxTeams];
+};
+
+// One matvec of a launch, as the kernels see it.
 struct StepDesc {
   const uint8_t *w;
   const float *x;
@@ -25,8 +41,17 @@ struct StepDesc {
   int32_t *idx;
   ArgmaxSlot *slot;
   int32_t n, p;
-  int32_t tile_begin;  // first global tile index of this matvec
+  int32_t tile_begin;     // first tile of this matvec in the launch
   int32_t rows_per_tile;
+  int32_t pad[2];
+};
+static_assert(sizeof(StepDesc) == 64, "descriptor layout");
+
+// Workgroups g in [first, first + size) of a persistent step share the
+// contiguous tile range [t0, t1), interleaved: workgroup first + j takes
+// tiles t0 + j, t0 + j + size, ...
+struct WgGroup {
+  int32_t t0, t1, first, size;
 };
 
 // Launches y = W x (m rows) with an optional fused argmax.  slot/idx are
@@ -39,18 +64,49 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
                          int32_t *idx, hipStream_t s);
 
-// Persistent step: one launch over `ntiles` tiles described by `descs`
-// (device memory, `count` entries, sorted by tile_begin).
-hipError_t launch_step(const StepDesc *descs, int count, int ntiles, int m,
-                       int grid, hipStream_t s);
+// Persistent step: one launch of `grid` workgroups over the tiles of the
+// `descs` table (device memory, `count` entries in tile order); workgroup g
+// belongs to groups[g / group_size] (device memory).  `lds` bytes of dynamic
+// LDS: step_lds_bytes of the widest matvec.
+hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
+                       int group_size, int m, int grid, size_t lds,
+                       bool all_staged, hipStream_t s);
 
-// Rows per tile the persistent step uses for a matvec of width n and m rows.
+// True when a matvec of width n with m rows takes the staged path (the step
+// can then use the kernel variant without the other paths).
+bool step_all_staged(int m, int n);
+
+// Rows per tile the persistent step uses for a matvec of width n, m rows.
 int step_rows_per_tile(int n, int m);
 
-// Workgroups the persistent step launches on this device.
-int step_grid(int device);
+// Dynamic LDS the step needs for a matvec of width n with m rows.
+size_t step_lds_bytes(int m, int n);
+
+// Workgroups of the step kernel resident at once on `device` (the grid).
+int step_grid(int device, int m, size_t lds, bool all_staged);
+
+// Everything a persistent step launch needs, worked out on the host.
+struct StepPlan {
+  std::vector<StepDesc> descs;  // slot pointers filled in by the caller
+  std::vector<WgGroup> groups;
+  std::vector<std::vector<uint32_t>> expected;  // per argmax desc, per team
+  size_t lds = 0;
+  int grid = 0;
+  int group_size = 1;
+  bool all_staged = true;
+};
+
+// Workgroups per group of the persistent step.
+constexpr int kStepGroupSize = 2;
 
 // Host stub of one kernel, used to check that the code object loads.
 const void *probe_kernel();
 
+}  // namespace q8
+
+struct q8_matvec_desc;
+namespace q8 {
+// Plans a persistent step (q8dec_api.hip) with groups of `group_size`.
+int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
+              int group_size, StepPlan &plan);
 }  // namespace q8

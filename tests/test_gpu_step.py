@@ -49,7 +49,7 @@ def run_graph(descs, m, mode, device):
     return g, host
 
 
-@pytest.mark.parametrize("mode", [0])
+@pytest.mark.parametrize("mode", [0, 1], ids=["chain", "persistent"])
 def test_small_step_matches_standalone_calls(cuda, mode):
     """Graph outputs equal the standalone calls bit for bit, on every replay,
     with eager work between replays; node counts match the descriptors."""
@@ -86,7 +86,7 @@ def test_small_step_matches_standalone_calls(cuda, mode):
     g.close()
 
 
-@pytest.mark.parametrize("mode", [0])
+@pytest.mark.parametrize("mode", [0, 1], ids=["chain", "persistent"])
 def test_full_step_against_oracle(cuda, mode):
     """All 197 matvecs of a step (28 layers + lm_head), every output."""
     import torch
@@ -109,7 +109,7 @@ def test_full_step_against_oracle(cuda, mode):
     g.close()
 
 
-@pytest.mark.parametrize("mode", [0])
+@pytest.mark.parametrize("mode", [0, 1], ids=["chain", "persistent"])
 def test_batched_step(cuda, mode):
     """m = 8 rows through every shape of a step (4 layers + lm_head here, the
     full 28 layers in the benchmark), argmax per row."""
