@@ -36,6 +36,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ["q8dec_api.hip", "q8dec_internal.h", "q8dec_kernels.hip"]
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_kernel_decode_step_hbm_bytes.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the library sources with comments and white space removed
+    (a comment edit does not change the kernel the counters describe)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "q8_block_quantized_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """HBM bytes per step-kernel launch from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch:",
+                                          "kernel_source_sha256:")))
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256", "").strip() != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def alg_bytes(n: int, p: int, m: int, logits: bool, argmax: bool) -> int:
     """Algorithmic bytes of one matvec: weight blocks + x + outputs."""
     return (p * (n // 32) * 34 + m * n * 4 + (m * p * 4 if logits else 0)
@@ -141,6 +175,9 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times "
+                         "(reference for the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X "
@@ -152,6 +189,15 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+        return 0
     q8.q8_init()
     log("generating two weight sets of a decode step (2 x 633 MB)")
     sets = [StepSet(torch, dev, 0, 0, 1, False), StepSet(torch, dev, 0, 1000, 1, False)]
@@ -201,7 +247,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(),
             "avg_launch_us": round(k_avg * 1e6, 2),
         },
     }

@@ -92,7 +92,8 @@ int q8_init(void);
 
 /* ---- matvec ------------------------------------------------------------ */
 
-/* y[p] = W x for one activation row x[n] (the page's q8_matvec, m = 1).
+/* y[p] = W x for one activation row x[n] (inferno.rs "IV.4", "Eight kernels",
+ * the q8_matvec kernel; m = 1).
  * p == 0 or n == 0 is allowed (n == 0 writes zeros). */
 int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
               void *stream);

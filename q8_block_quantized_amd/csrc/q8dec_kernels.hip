@@ -17,15 +17,17 @@
 //    one v_perm_b32 per quant dword then realigns the quants (byte shift 2
 //    or 4) and a shift picks the scale half-word.  The quants convert to f32
 //    with sign extension (SDWA) and accumulate with x by FMA; the block sum
-//    is scaled once per block, as in the page's kernel.
+//    is scaled once per block (the q8_matvec listing of inferno.rs "IV.4:
+//    One command buffer per token", section "Eight kernels").
 //  * x is staged once per matvec in LDS with 4 pad floats after every 32,
 //    so the 128-byte per-lane reads of one block hit distinct banks.
 //  * The 32 lane partials of a row reduce with DPP (quad_perm, row mirrors,
-//    row_bcast15) without touching memory: the page's simd_sum step.
+//    row_bcast15) without touching memory (the simd_sum step of the same
+//    listing).
 //  * m = 1 is bandwidth-bound GEMV work, so no MFMA is used.
 // The fused argmax keeps a 64-bit key per lane, (order-preserving bits of
 // the logit) << 32 | (0xFFFFFFFF - row), so an unsigned max picks the
-// largest logit and, among equal logits, the lowest row (the page's argmax
+// largest logit and, among equal logits, the lowest row (the argmax_row
 // tie rule); NaN never enters and -0 is folded onto +0.  Each arrival (a
 // workgroup, or a tile of the step) adds its key with one 64-bit atomic max;
 // the last arrival (an arrival counter) writes the index and clears the
