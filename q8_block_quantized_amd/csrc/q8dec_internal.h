@@ -21,7 +21,10 @@ struct ArgmaxGroup {
 };
 static_assert(sizeof(ArgmaxGroup) == 256, "group layout");
 
-constexpr int kArgmaxTeams = 64;
+#ifndef Q8_ARGMAX_TEAMS
+#define Q8_ARGMAX_TEAMS 32
+#endif
+constexpr int kArgmaxTeams = Q8_ARGMAX_TEAMS;
 
 // Argmax workspace of one matvec.  An arriving workgroup g joins team
 // g % kArgmaxTeams; the last arrival of a team forwards the team's keys to
@@ -97,7 +100,7 @@ struct StepPlan {
 };
 
 // Workgroups per group of the persistent step.
-constexpr int kStepGroupSize = 2;
+constexpr int kStepGroupSize = 32;
 
 // Host stub of one kernel, used to check that the code object loads.
 const void *probe_kernel();
