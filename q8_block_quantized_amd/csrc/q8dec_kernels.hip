@@ -281,14 +281,18 @@ __device__ void argmax_finish(const unsigned long long *best, int m,
 // ---- matvec geometry ---------------------------------------------------------
 
 // How the tiles of a matvec are processed.
-//  kStaged : the tile's rows are streamed with coalesced, 16-byte aligned
-//            loads (whole rows are contiguous) into registers one tile ahead,
-//            written to LDS, and each lane reads its blocks' windows from LDS.
-//            Needs a row pitch that is a multiple of 16 (n/32 % 8 == 0).
+//  kStaged : m = 1.  The tile's rows are streamed with coalesced, 16-byte
+//            aligned loads (whole rows are contiguous) into registers one
+//            tile ahead, written to LDS, and each lane reads its blocks'
+//            windows from LDS.  Needs a row pitch that is a multiple of 16
+//            (n/32 % 8 == 0).
+//  kMfma   : 1 < m <= 8 and n in {1024, 2048, 3072}: same staging (rows
+//            padded in LDS); the products run on the matrix cores (see
+//            mfma_tile).
 //  kDirect : each lane loads its blocks' windows straight from global
 //            memory (dword aligned, 34-byte lane stride); any row pitch.
 //  kGeneric: as kDirect, but x is read from global memory (large m * n).
-enum Path : int { kStaged = 0, kDirect = 1, kGeneric = 2 };
+enum Path : int { kStaged = 0, kDirect = 1, kGeneric = 2, kMfma = 3 };
 
 #ifndef Q8_TILE_BYTES
 #define Q8_TILE_BYTES 26112  // 8 rows of 3072 columns
@@ -301,21 +305,36 @@ constexpr int kStageChunks = (kTileMaxBytes + 16 * kWG - 1) / (16 * kWG);
 constexpr int kXMaxFloats = 8192;     // m * n of x kept in LDS (32 KB)
 constexpr int kMaxLdsBlocks = 96;     // n <= 3072 for the LDS paths
 
+// Batched tiles: 16-row groups; each staged row is followed by kMfmaRowPad
+// bytes of LDS so that the 16 rows of a group start in different banks.
+constexpr int kMfmaRowPad = 16;
+constexpr int kMfmaTileBytes = 53248;  // LDS of a batched tile, pads included
+constexpr int kMfmaChunks = (kMfmaTileBytes + 16 * kWG - 1) / (16 * kWG);
+constexpr int kMfmaMaxBlocks = kMaxLdsBlocks / kWaves;  // x blocks per wave
+constexpr int kRedFloats = 2 * kWaves * 256;  // two sets of 16 x 16 partials per wave
+
 __host__ __device__ inline int path_of(int m, int n) {
   const int bpr = n >> 5;
-  if (bpr == 0 || bpr > kMaxLdsBlocks || m * n > kXMaxFloats) return kGeneric;
-  return (bpr % 8 == 0) ? kStaged : kDirect;
+  if (bpr == 0 || bpr > kMaxLdsBlocks) return kGeneric;
+  if (m == 1) return bpr % 8 == 0 ? kStaged : kDirect;
+  if (bpr == 32 || bpr == 64 || bpr == 96) return kMfma;
+  return m * n > kXMaxFloats ? kGeneric : kDirect;
 }
 
 __host__ __device__ inline int nbl_of(int n) { return ((n >> 5) + 31) >> 5; }
 
 // Rows per tile: staged tiles fill up to kTileMaxBytes (at least one pass of
-// 8 rows); direct and generic tiles are two or four passes.
+// 8 rows), batched tiles up to kMfmaTileBytes in 16-row groups; direct and
+// generic tiles are two or four passes.
 __host__ __device__ inline int tile_rows_of(int m, int n) {
   const int path = path_of(m, n);
   if (path == kStaged) {
     const int r = kTileMaxBytes / ((n >> 5) * 34);
     return r >= 64 ? 64 : (r < 1 ? 1 : r);
+  }
+  if (path == kMfma) {
+    const int g = kMfmaTileBytes / (16 * ((n >> 5) * 34 + kMfmaRowPad));
+    return 16 * (g < 1 ? 1 : g);
   }
   return path == kDirect && m == 1 ? 32 : 16;
 }
@@ -548,61 +567,165 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
   }
 }
 
-// Same for 1 < m <= 8: each block's quants convert once and serve m rows of
-// x from LDS (row j at float offset j * 36 * bpr).
-template <int NBL>
-__device__ __forceinline__ void staged_mb(const uint32_t *tl, int32_t bpr,
+// ---- batched path: matrix cores -----------------------------------------------
+//
+// For 1 < m <= 8 a 16-row group of a staged tile against one block is one
+// v_mfma_f32_16x16x32_bf16, with k running over the block's 32 quants:
+//  * operand A is x: column i < 8 holds x row i rounded to bf16 ("hi"),
+//    column i + 8 the bf16 of what that rounding left ("lo"), so hi + lo
+//    carries x to about 2^-17 relative; rows i >= m are zero;
+//  * operand B holds the 16 weight rows' quants as bf16 (exact for int8);
+//  * D[i][j] = sum over the block of x_i * q_j exactly rounded products,
+//    accumulated in f32; the block's scale for row j multiplies it once
+//    (the dequantise-in-the-dot order of the q8_matvec listing in inferno.rs
+//    "IV.4: One command buffer per token", section "Eight kernels") and the
+//    result adds into an f32 accumulator.
+// Lane l of a wave holds A[l % 16][8 (l / 16) .. + 7], B[8 (l / 16) .. + 7]
+// [l % 16] and D[4 (l / 16) + r][l % 16] for r < 4, so each lane scales its
+// four D values by the scale of weight row l % 16.  The four waves of a
+// workgroup split each row's blocks into four contiguous slices and keep their
+// slice of x in registers for the whole matvec; their 16 x 16 partials meet
+// in LDS, where y[i][row] = sum over waves of column i plus column i + 8.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Two int8 quants (bytes lo, lo + 1 of q) as a pair of bf16 (exact): the f32
+// of a small integer has zero low halves, so the high halves are the bf16.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t q, int lo) {
+  const float f0 = (float)(int8_t)(q >> (8 * lo));
+  const float f1 = (float)(int8_t)(q >> (8 * lo + 8));
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                               __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 quants_bf16(uint32_t qa, uint32_t qb) {
+  u32x4 r;
+  r.x = bf16_pair(qa, 0);
+  r.y = bf16_pair(qa, 2);
+  r.z = bf16_pair(qb, 0);
+  r.w = bf16_pair(qb, 2);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// This lane's operand A for the blocks of its wave's slice of one matvec:
+// x row (lane % 16) & 7, hi or lo part, elements 8 (lane / 16) .. + 7 of each
+// block; NBW = n / 128 blocks per wave.  Lanes i and i + 8 of a 16-lane row
+// need the same eight floats: each loads four and a DPP rotation by 8 within
+// the row swaps the halves.
+template <int NBW>
+__device__ __forceinline__ void load_xa(u32x4 (&xa)[kMfmaMaxBlocks],
+                                        const float *x, int32_t m, int32_t n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, xr = i & 7, g = lane >> 4;
+  const bool lo = i >= 8, live = xr < m;
+  const __attribute__((address_space(1))) f32x4 *src =
+      (const __attribute__((address_space(1))) f32x4 *)gp(
+          x + (int64_t)(live ? xr : 0) * n + 32 * wave * NBW + 8 * g + 4 * lo);
+  f32x4 v[NBW];
+#pragma unroll
+  for (int t = 0; t < NBW; t++) v[t] = src[8 * t];
+#pragma unroll
+  for (int t = 0; t < NBW; t++) {
+    f32x4 w;
+#pragma unroll
+    for (int c = 0; c < 4; c++) w[c] = dpp_shift<0x128, 0xF>(v[t][c]);  // row_ror:8
+    float e[8];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      e[c] = lo ? w[c] : v[t][c];
+      e[c + 4] = lo ? v[t][c] : w[c];
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const float hi = (float)(__bf16)e[c];
+      h[c] = lo ? bf16_bits(e[c] - hi) : bf16_bits(e[c]);
+    }
+    u32x4 r;
+    r.x = h[0] | (h[1] << 16);
+    r.y = h[2] | (h[3] << 16);
+    r.z = h[4] | (h[5] << 16);
+    r.w = h[6] | (h[7] << 16);
+    xa[t] = live ? r : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Rows [0, rows) of a batched tile in LDS (row pitch 34 * bpr + kMfmaRowPad
+// bytes, bpr = 4 * NBW): y[i][r0 + row] for i < m.  `red` is kRedFloats of LDS.  Keys of
+// x row threadIdx.x / 16 (threads below 128) go to `kb`.
+template <int NBW>
+__device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
                                           int32_t rows, int32_t m, int32_t p,
-                                          const float *xs, float *y, int32_t r0,
-                                          bool keys, unsigned long long *best) {
-  const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
-  const int wave = threadIdx.x >> 6;
-  const int32_t pitch = bpr * 34;
-  const int32_t xstride = 36 * bpr;
-  for (int32_t rr0 = 2 * wave; rr0 < rows; rr0 += kRowsPerPass) {
-    const int32_t rr = rr0 + half;
-    const int32_t rc = rr < rows ? rr : rows - 1;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    asm volatile("" ::: "memory");
+                                          const u32x4 (&xa)[kMfmaMaxBlocks],
+                                          float *red, float *y, int32_t r0,
+                                          bool keys, unsigned long long &kb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int32_t lpd = (bpr * 34 + kMfmaRowPad) >> 2;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  int buf = 0;
+  for (int32_t rg = 0; rg < rows; rg += 16) {
+    const int32_t row = min(rg + j, rows - 1);
+    // the slice starts at an even block, so at a dword boundary
+    const uint32_t *rp = tl + row * lpd + ((34 * wave * NBW) >> 2);
+    f32x4 acc = zero;
 #pragma unroll
-    for (int i = 0; i < NBL; i++) {
-      const int32_t b = min(k + 32 * i, bpr - 1);
-      const int32_t o = rc * pitch + 34 * b;
-      const uint32_t *wp = tl + (o >> 2);
-      uint32_t d[9];
+    for (int t = 0; t < NBW; t += 2) {
+      {
+        // blocks t (byte 0 of wp, quants from byte 2) and t + 1 (byte 34,
+        // quants from byte 36) of the slice
+        const uint32_t *wp = rp + 17 * (t >> 1);
+        const uint32_t *wq = wp + 2 * g;
+        const uint32_t e0 = wq[0], e1 = wq[1], e2 = wq[2];
+        const uint32_t o0 = wq[9], o1 = wq[10];
+        const uint32_t s01 = wp[0], s23 = wp[8];
+        const bf16x8 qe = quants_bf16(__builtin_amdgcn_perm(e1, e0, 0x05040302u),
+                                      __builtin_amdgcn_perm(e2, e1, 0x05040302u));
+        const bf16x8 qo = quants_bf16(o0, o1);
+        const f32x4 de = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xa[t]), qe, zero, 0, 0, 0);
+        const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, xa[t + 1]), qo, zero, 0, 0, 0);
+        const float se = (float)__builtin_bit_cast(_Float16, (uint16_t)(s01 & 0xFFFFu));
+        const float so = (float)__builtin_bit_cast(_Float16, (uint16_t)(s23 >> 16));
 #pragma unroll
-      for (int q = 0; q < 9; q++) d[q] = wp[q];
-      const uint32_t amod = (uint32_t)o & 2u;
-      const float s = (k + 32 * i < bpr) ? scale_of(d, amod) : 0.f;
-      float qf[32];
-      block_quants(d, quant_sel(amod), qf);
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        if (j < m) {
-          float xb[32];
-          load_x32(xs + j * xstride + 36 * b, xb);
-          acc[j] = fmaf(s, dot32(qf, xb), acc[j]);
+        for (int r = 0; r < 4; r++) {
+          acc[r] = fmaf(se, de[r], acc[r]);
+          acc[r] = fmaf(so, dd[r], acc[r]);
         }
       }
     }
+    float *rb = red + buf * (kWaves * 256);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      if (j < m) {
-        const float v = half_wave_sum(acc[j]);
-        if (k == 31 && rr < rows) {
-          if (y) gpw(y)[(int64_t)j * p + r0 + rr] = v;
-          if (keys) best[j] = umax64(best[j], argmax_key(v, (uint32_t)(r0 + rr)));
-        }
+    for (int r = 0; r < 4; r++) rb[wave * 256 + (4 * g + r) * 16 + j] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int xr = threadIdx.x >> 4, jj = threadIdx.x & 15;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; w++)
+        v += rb[w * 256 + xr * 16 + jj] + rb[w * 256 + (xr + 8) * 16 + jj];
+      const int32_t rr = rg + jj;
+      if (xr < m && rr < rows) {
+        if (y) gpw(y)[(int64_t)xr * p + r0 + rr] = v;
+        if (keys) kb = umax64(kb, argmax_key(v, (uint32_t)(r0 + rr)));
       }
     }
+    // the other buffer serves the next group; the barrier after its writes
+    // orders this group's reads before the one after reuses this buffer
+    buf ^= 1;
   }
 }
 
 // Registers that carry the next tile's weights (and x, when the next tile
 // belongs to another matvec) while the current tile is computed.
-template <int XC>
+template <int XC, int CH>
 struct Prefetch {
-  u32x4 w[kStageChunks];
+  u32x4 w[CH];
   f32x4 x[XC];
 
   // `bytes` (a multiple of 16, >= 16) contiguous bytes at base (16-aligned).
@@ -611,7 +734,7 @@ struct Prefetch {
   __device__ __forceinline__ void load_w(const uint8_t *base, int32_t bytes) {
     const __attribute__((address_space(1))) uint8_t *b = gp(base);
 #pragma unroll
-    for (int j = 0; j < kStageChunks; j++) {
+    for (int j = 0; j < CH; j++) {
       int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
       off = off < bytes - 16 ? off : bytes - 16;
       w[j] = __builtin_nontemporal_load(
@@ -620,10 +743,26 @@ struct Prefetch {
   }
   __device__ __forceinline__ void store_w(uint32_t *tl, int32_t bytes) const {
 #pragma unroll
-    for (int j = 0; j < kStageChunks; j++) {
+    for (int j = 0; j < CH; j++) {
       int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
       off = off < bytes - 16 ? off : bytes - 16;  // repeats write equal data
       *(u32x4 *)((uint8_t *)tl + off) = w[j];
+    }
+  }
+  // Same, with kMfmaRowPad bytes after every row of `pitch` bytes (a
+  // multiple of 16, so no chunk straddles two rows).
+  __device__ __forceinline__ void store_w_rows(uint32_t *tl, int32_t bytes,
+                                               int32_t pitch) const {
+    const int32_t cpr = pitch >> 4;  // chunks per row
+    // chunk c of row c / cpr: c < 2^12 and c / cpr is at least 1 / (2 cpr)
+    // from an integer, far above the rounding of the product
+    const float rcp = 1.0f / (float)cpr;
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
+      off = off < bytes - 16 ? off : bytes - 16;
+      const int32_t row = (int32_t)(((float)(off >> 4) + 0.5f) * rcp);
+      *(u32x4 *)((uint8_t *)tl + off + row * kMfmaRowPad) = w[j];
     }
   }
   // m rows of n floats (m * n <= 4 * XC * kWG), [m][n] contiguous.
@@ -703,25 +842,37 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
 // tile's weights (and x, when the tile opens another matvec) are loaded into
 // registers while the previous tile is computed.  Tiles of one matvec are
 // contiguous, so a workgroup meets each matvec in one run of tiles; the run
-// adds its argmax keys, if any, as one arrival.  LDS: the staged tile, then
-// the padded x.
+// adds its argmax keys, if any, as one arrival.  M1: the launch has m = 1;
+// ANY: some matvec of the launch takes the direct or generic path.
+// LDS: the staged tile, then (batched) the partial sums, then the padded x.
 template <bool M1, bool ANY, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
-                          float *tl_lds, float *xs) {
-  constexpr int XC = M1 ? 3 : 8;  // float4 chunks of x per thread
-  uint32_t *tl = (uint32_t *)tl_lds;
+                          float *lds) {
+  constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
+  constexpr int CH = M1 ? kStageChunks : kMfmaChunks;
+  uint32_t *tl = (uint32_t *)lds;
+  float *red = lds + (M1 ? kTileMaxBytes : kMfmaTileBytes) / 4;
+  float *xs = M1 ? red : red + kRedFloats;
+  // which path a tile takes; without ANY every tile takes the staged one
+  auto staged = [&](const Job &j) { return M1 && (!ANY || j.path == kStaged); };
+  auto mfma = [&](const Job &j) { return !M1 && (!ANY || j.path == kMfma); };
+  auto x_in_lds = [&](const Job &j) {
+    return M1 ? (!ANY || j.path != kGeneric) : (ANY && j.path == kDirect);
+  };
   int32_t t = first;
   if (t >= end) return;
-  Prefetch<XC> pf;
+  Prefetch<XC, CH> pf;
   int32_t di = src.find(t, d_hint);
   Job cur = job_at(di, src.get(di), t, m);
-  if (cur.path == kStaged)
+  if (staged(cur) || mfma(cur))
     pf.load_w(cur.d.w + (uint64_t)cur.r0 * (cur.d.n >> 5) * 34u,
               cur.rows * (cur.d.n >> 5) * 34);
-  if (cur.path != kGeneric) pf.load_x(cur.d.x, m * cur.d.n);
-  int32_t xdesc = -1;
+  if (x_in_lds(cur)) pf.load_x(cur.d.x, m * cur.d.n);
+  int32_t xdesc = -1, xadesc = -1;
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
+  unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
+  u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
   for (;;) {
     const int32_t tn = t + stride;
     const bool more = tn < end;
@@ -735,31 +886,41 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       }
     }
     const int32_t bpr = cur.d.n >> 5;
-    const bool new_x = cur.path != kGeneric && cur.desc != xdesc;
+    const bool new_x = x_in_lds(cur) && cur.desc != xdesc;
     __syncthreads();  // the previous tile's readers of LDS are done
-    if (cur.path == kStaged) pf.store_w(tl, cur.rows * bpr * 34);
+    if (staged(cur)) pf.store_w(tl, cur.rows * bpr * 34);
+    else if (mfma(cur)) pf.store_w_rows(tl, cur.rows * bpr * 34, bpr * 34);
     if (new_x) pf.store_x(xs, m, cur.d.n);
     __syncthreads();
     if (new_x) xdesc = cur.desc;
+    // a new matvec's operand A is loaded before the next tile's bytes are
+    // requested, so waiting for it does not wait for them
+    if (mfma(cur) && cur.desc != xadesc) {
+      if (bpr == 32) load_xa<8>(xa, cur.d.x, m, cur.d.n);
+      else if (bpr == 64) load_xa<16>(xa, cur.d.x, m, cur.d.n);
+      else load_xa<24>(xa, cur.d.x, m, cur.d.n);
+      xadesc = cur.desc;
+    }
     if (more) {  // next tile's bytes go out before this tile is computed
-      if (nxt.path == kStaged)
+      if (staged(nxt) || mfma(nxt))
         pf.load_w(nxt.d.w + (uint64_t)nxt.r0 * (nxt.d.n >> 5) * 34u,
                   nxt.rows * (nxt.d.n >> 5) * 34);
-      if (nxt.path != kGeneric && nxt.desc != cur.desc)
+      if (x_in_lds(nxt) && nxt.desc != cur.desc)
         pf.load_x(nxt.d.x, m * nxt.d.n);
     }
     const bool keys = cur.d.idx != nullptr;
-    if (cur.path == kStaged) {
+    if (staged(cur)) {
       const int nbl = nbl_of(cur.d.n);
-      if (M1) {
-        if (nbl == 1) staged_m1<1>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else if (nbl == 2) staged_m1<2>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else staged_m1<3>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-      } else {
-        if (nbl == 1) staged_mb<1>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-        else if (nbl == 2) staged_mb<2>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-        else staged_mb<3>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-      }
+      if (nbl == 1) staged_m1<1>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+      else if (nbl == 2) staged_m1<2>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+      else staged_m1<3>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+    } else if (mfma(cur)) {
+      if (bpr == 32)
+        mfma_tile<8>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+      else if (bpr == 64)
+        mfma_tile<16>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+      else
+        mfma_tile<24>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
     } else if (ANY) {
       Tile c;
       c.w = cur.d.w;
@@ -776,7 +937,13 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       run_direct<M1>(c, cur.path, best, keys);
     }
     if (keys && (!more || nxt.desc != cur.desc)) {
-      argmax_finish(best, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x, tl_lds);
+      if (!M1) {
+        const int xr = threadIdx.x < 128 ? (int)(threadIdx.x >> 4) : 8;
+#pragma unroll
+        for (int r = 0; r < 8; r++) best[r] = umax64(best[r], r == xr ? kb : 0ull);
+        kb = 0ull;
+      }
+      argmax_finish(best, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x, lds);
 #pragma unroll
       for (int r = 0; r < 8; r++) best[r] = 0ull;
     }
@@ -786,142 +953,6 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   }
 }
 
-// Two-deep variant of run_tiles: two register sets carry the weights of the
-// next two tiles, so each workgroup keeps two tiles of HBM reads in flight
-// while it computes a third from LDS (x stays one tile ahead).
-struct WStage {
-  u32x4 w[kStageChunks];
-  __device__ __forceinline__ void load(const uint8_t *base, int32_t bytes) {
-    const __attribute__((address_space(1))) uint8_t *b = gp(base);
-#pragma unroll
-    for (int j = 0; j < kStageChunks; j++) {
-      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
-      off = off < bytes - 16 ? off : bytes - 16;
-      w[j] = __builtin_nontemporal_load(
-          (const __attribute__((address_space(1))) u32x4 *)(b + off));
-    }
-  }
-  __device__ __forceinline__ void store(uint32_t *tl, int32_t bytes) const {
-#pragma unroll
-    for (int j = 0; j < kStageChunks; j++) {
-      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
-      off = off < bytes - 16 ? off : bytes - 16;
-      *(u32x4 *)((uint8_t *)tl + off) = w[j];
-    }
-  }
-};
-
-__device__ __forceinline__ const uint8_t *tile_base(const Job &j) {
-  return j.d.w + (uint64_t)j.r0 * (j.d.n >> 5) * 34u;
-}
-__device__ __forceinline__ int32_t tile_bytes(const Job &j) {
-  return j.rows * (j.d.n >> 5) * 34;
-}
-
-template <class Src>
-__device__ __forceinline__ Job next_job(const Src &src, const Job &cur, int32_t t,
-                                        int32_t m) {
-  if (t < cur.d.tile_begin + tiles_of(cur.d)) return job_at(cur.desc, cur.d, t, m);
-  const int32_t dn = src.find(t, cur.desc + 1);
-  return job_at(dn, src.get(dn), t, m);
-}
-
-template <bool M1, bool ANY, class Src, int XC>
-__device__ __forceinline__ bool tile_step(const Src &src, WStage &wuse,
-                                          Prefetch<XC> &xp, Job &cur, Job &nxt,
-                                          int32_t &t, int32_t end, int32_t stride,
-                                          int32_t m, int32_t &xdesc,
-                                          unsigned long long *best, uint32_t *tl,
-                                          float *xs) {
-  const bool has_next = t + stride < end;
-  const int32_t t2 = t + 2 * stride;
-  const bool has2 = t2 < end;
-  Job j2 = nxt;
-  if (has2) j2 = next_job(src, nxt, t2, m);
-  const int32_t bpr = cur.d.n >> 5;
-  const bool new_x = cur.path != kGeneric && cur.desc != xdesc;
-  __syncthreads();  // the previous tile's readers of LDS are done
-  if (cur.path == kStaged) wuse.store(tl, tile_bytes(cur));
-  if (new_x) xp.store_x(xs, m, cur.d.n);
-  __syncthreads();
-  if (new_x) xdesc = cur.desc;
-  if (has2 && j2.path == kStaged) wuse.load(tile_base(j2), tile_bytes(j2));
-  if (has_next && nxt.path != kGeneric && nxt.desc != cur.desc)
-    xp.load_x(nxt.d.x, m * nxt.d.n);
-  const bool keys = cur.d.idx != nullptr;
-  if (cur.path == kStaged) {
-    const int nbl = nbl_of(cur.d.n);
-    if (M1) {
-      if (nbl == 1) staged_m1<1>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-      else if (nbl == 2) staged_m1<2>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-      else staged_m1<3>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-    } else {
-      if (nbl == 1) staged_mb<1>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-      else if (nbl == 2) staged_mb<2>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-      else staged_mb<3>(tl, bpr, cur.rows, m, cur.d.p, xs, cur.d.y, cur.r0, keys, best);
-    }
-  } else if (ANY) {
-    Tile c;
-    c.w = cur.d.w;
-    c.bpr = bpr;
-    c.wbytes = (uint64_t)cur.d.p * (uint64_t)bpr * 34u;
-    c.xg = cur.d.x;
-    c.xs = xs;
-    c.y = cur.d.y;
-    c.n = cur.d.n;
-    c.p = cur.d.p;
-    c.m = m;
-    c.r0 = cur.r0;
-    c.r1 = cur.r0 + cur.rows;
-    run_direct<M1>(c, cur.path, best, keys);
-  }
-  if (keys && (!has_next || nxt.desc != cur.desc)) {
-    argmax_finish(best, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x, tl);
-#pragma unroll
-    for (int r = 0; r < 8; r++) best[r] = 0ull;
-  }
-  if (!has_next) return true;
-  t += stride;
-  cur = nxt;
-  nxt = j2;
-  return false;
-}
-
-template <bool M1, bool ANY, class Src>
-__device__ void run_tiles2(const Src &src, int32_t first, int32_t end,
-                           int32_t stride, int32_t d_hint, int32_t m,
-                           float *tl_lds, float *xs) {
-  constexpr int XC = M1 ? 3 : 8;
-  uint32_t *tl = (uint32_t *)tl_lds;
-  if (first >= end) return;
-  WStage wa, wb;
-  Prefetch<XC> xp;
-  int32_t t = first;
-  const int32_t d0 = src.find(t, d_hint);
-  Job cur = job_at(d0, src.get(d0), t, m);
-  Job nxt = cur;
-  if (t + stride < end) nxt = next_job(src, cur, t + stride, m);
-  if (cur.path == kStaged) wa.load(tile_base(cur), tile_bytes(cur));
-  if (cur.path != kGeneric) xp.load_x(cur.d.x, m * cur.d.n);
-  if (t + stride < end && nxt.path == kStaged) wb.load(tile_base(nxt), tile_bytes(nxt));
-  int32_t xdesc = -1;
-  unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
-  for (;;) {
-    if (tile_step<M1, ANY>(src, wa, xp, cur, nxt, t, end, stride, m, xdesc, best, tl, xs))
-      break;
-    if (tile_step<M1, ANY>(src, wb, xp, cur, nxt, t, end, stride, m, xdesc, best, tl, xs))
-      break;
-  }
-}
-
-#ifndef Q8_PREFETCH_DEPTH
-#define Q8_PREFETCH_DEPTH 1
-#endif
-#if Q8_PREFETCH_DEPTH == 2
-#define Q8_RUN_TILES run_tiles2
-#else
-#define Q8_RUN_TILES run_tiles
-#endif
 
 // ---- kernels -----------------------------------------------------------------
 
@@ -929,27 +960,25 @@ __device__ void run_tiles2(const Src &src, int32_t first, int32_t end,
 // grid (gridDim.x <= tiles, so every workgroup arrives at the argmax): at
 // any moment the grid streams one contiguous window of the weights.
 template <bool M1, bool ANY>
-__global__ void __launch_bounds__(kWG, Q8_MIN_WGS_PER_CU)
+__global__ void __launch_bounds__(kWG, M1 ? Q8_MIN_WGS_PER_CU : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
-  Q8_RUN_TILES<M1, ANY>(src, blockIdx.x, tiles_of(d), gridDim.x, 0, m, lds,
-                        lds + kTileMaxBytes / 4);
+  run_tiles<M1, ANY>(src, blockIdx.x, tiles_of(d), gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
 // (count entries in tile order), with no ordering between descriptors.
 // Workgroups form groups; a group interleaves its contiguous tile range.
 template <bool M1, bool ANY>
-__global__ void __launch_bounds__(kWG, Q8_MIN_WGS_PER_CU)
+__global__ void __launch_bounds__(kWG, M1 ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  Q8_RUN_TILES<M1, ANY>(src, g.t0 + j, g.t1, g.size, 0, m, lds,
-                        lds + kTileMaxBytes / 4);
+  run_tiles<M1, ANY>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
 }
 
 // ---- argmax over f32 logits ---------------------------------------------
@@ -974,9 +1003,14 @@ argmax_rows(const float *__restrict__ logits, int32_t m, int32_t p,
 
 // Dynamic LDS of a launch whose matvecs have widths up to n_max.
 size_t lds_bytes_for(int m, int n) {
-  // the x region starts after the tile region
-  const size_t x = path_of(m, n) == kGeneric ? 0 : (size_t)x_lds_floats(m, n);
-  return kTileMaxBytes + x * sizeof(float);
+  const int path = path_of(m, n);
+  if (m == 1) {  // the x region starts after the tile region
+    const size_t x = path == kGeneric ? 0 : (size_t)x_lds_floats(m, n);
+    return kTileMaxBytes + x * sizeof(float);
+  }
+  // tile, partial sums, then x for the direct path
+  const size_t x = path == kDirect ? (size_t)x_lds_floats(m, n) : 0;
+  return kMfmaTileBytes + (kRedFloats + x) * sizeof(float);
 }
 
 int device_cus(int dev) {
@@ -1008,8 +1042,9 @@ int mv_grid_cap(int dev) {
   static int cache[64] = {0};
   int &c = cache[dev & 63];
   if (!c) {
-    const size_t lds = kTileMaxBytes + (M1 ? (size_t)kMaxLdsBlocks * 36 * 4
-                                           : (size_t)kXMaxFloats / 32 * 36 * 4);
+    const size_t lds = M1 ? kTileMaxBytes + (size_t)kMaxLdsBlocks * 36 * 4
+                          : kMfmaTileBytes + (size_t)kRedFloats * 4 +
+                                (ANY ? (size_t)kXMaxFloats / 32 * 36 * 4 : 0);
     c = resident_wgs(mv_kernel<M1, ANY>, lds, dev);
   }
   return c;
@@ -1033,7 +1068,9 @@ int step_rows_per_tile(int n, int m) { return tile_rows_of(m, n); }
 
 size_t step_lds_bytes(int m, int n) { return lds_bytes_for(m, n); }
 
-bool step_all_staged(int m, int n) { return path_of(m, n) == kStaged; }
+bool step_all_staged(int m, int n) {
+  return path_of(m, n) == (m == 1 ? kStaged : kMfma);
+}
 
 int step_grid(int device, int m, size_t lds, bool all_staged) {
   if (m == 1)
@@ -1057,11 +1094,18 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
   d.p = p;
   d.tile_begin = 0;
   d.rows_per_tile = tile_rows_of(m, n);
-  // small matvecs: shorter tiles spread them over more workgroups
-  while (d.rows_per_tile > kRowsPerPass &&
-         (p + d.rows_per_tile - 1) / d.rows_per_tile < 512)
-    d.rows_per_tile >>= 1;
-  const bool staged = path_of(m, n) == kStaged;
+  const int path = path_of(m, n);
+  // small matvecs: shorter tiles spread them over more workgroups (batched
+  // tiles stay whole 16-row groups)
+  if (path == kMfma) {
+    while (d.rows_per_tile > 16 && (p + d.rows_per_tile - 1) / d.rows_per_tile < 512)
+      d.rows_per_tile = d.rows_per_tile % 32 == 0 ? d.rows_per_tile >> 1 : 16;
+  } else {
+    while (d.rows_per_tile > kRowsPerPass &&
+           (p + d.rows_per_tile - 1) / d.rows_per_tile < 512)
+      d.rows_per_tile >>= 1;
+  }
+  const bool staged = path == kStaged || path == kMfma;
   if (m == 1)
     return staged ? launch_mv<true, false>(d, m, s) : launch_mv<true, true>(d, m, s);
   return staged ? launch_mv<false, false>(d, m, s) : launch_mv<false, true>(d, m, s);

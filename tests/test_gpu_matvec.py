@@ -155,3 +155,114 @@ def test_batched_m1_equals_matvec(cuda):
     yb = gpu_batched(w, x[None, :], cuda)[0]
     y = gpu_matvec(w, x, cuda)
     assert np.array_equal(yb, y)
+
+
+# ---- batched (1 < m <= 8) -----------------------------------------------------
+# Widths 1024, 2048 and 3072 take the matrix-core path (x split into two
+# bf16 parts); other widths the direct or generic paths.
+
+@pytest.mark.parametrize("m", [2, 7, 8])
+@pytest.mark.parametrize("p,n", [(1000, 1024), (333, 2048), (170, 3072),
+                                 (40, 4096), (21, 1056), (37, 256)])
+def test_batched_tiles_and_paths(cuda, m, p, n):
+    say(f"batched tiles m={m} p={p} n={n}")
+    w, _ = rich_case(p, n, seed=m + p)
+    x = gen.activations(m, n, seed=p, index=m)
+    y = gpu_batched(w, x, cuda)
+    ref, tol = oracle.matvec_batched(w, x)
+    assert_parity(y, ref, tol, f"m={m} p={p} n={n}")
+
+
+def test_batched_many_tiles(cuda):
+    """Enough rows that each workgroup takes several 48-row tiles, ragged end."""
+    m, p, n = 8, 30011, 1024
+    w = gen.weights(p, n, seed=4, index=4)
+    x = gen.activations(m, n, seed=4, index=4)
+    y = gpu_batched(w, x, cuda)
+    ref, tol = oracle.matvec_batched(w, x)
+    assert_parity(y, ref, tol, "m=8 p=30011")
+
+
+@pytest.mark.parametrize("p,n", [(40, 1024), (17, 2048), (6, 3072), (11, 160)])
+def test_batched_pow2_scales_integer_x_exact(cuda, p, n):
+    # integers in [-4, 4] are exact in the high bf16 part, so the products,
+    # block sums and the 2^-3-grid row sums are all exact
+    m = 8
+    rng = np.random.default_rng(p * n)
+    quants = rng.integers(-128, 128, size=(p, n // 32, 32))
+    expo = rng.integers(-3, 1, size=(p, n // 32))
+    w = make_blocks(((15 + expo).astype(np.uint16) << 10), quants)
+    x = rng.integers(-4, 5, size=(m, n)).astype(np.float32)
+    y = gpu_batched(w, x, cuda)
+    ref, _ = oracle.matvec_batched(w, x)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("n", [1024, 2048, 3072])
+def test_batched_one_hot_is_exact(cuda, n):
+    p, m = 48, 8
+    w, _ = rich_case(p, n, seed=n)
+    blk = w.reshape(p, n // 32, 34)
+    scale = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2")[..., 0].astype(np.float32)
+    q = np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).astype(np.float32)
+    ks = [0, 1, 33, 100, n // 2 + 7, n - 33, n - 2, n - 1]
+    x = np.zeros((m, n), dtype=np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = gpu_batched(w, x, cuda)
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], scale[:, k // 32] * q[:, k // 32, k % 32]), (r, k)
+
+
+@pytest.mark.parametrize("n", [1024, 3072])
+def test_batched_rows_independent_and_homogeneous(cuda, n):
+    """Each output row depends on its own x row only (bit for bit), and
+    scaling x by 4 scales y exactly.  Negating x negates y to the oracle's
+    bound only: the matrix cores' block sums are not rounded symmetrically
+    about zero, so -x may differ from x in the last bits."""
+    p = 200
+    w, _ = rich_case(p, n, seed=11)
+    x = gen.activations(8, n, seed=11, index=n)
+    y8 = gpu_batched(w, x, cuda)
+    y3 = gpu_batched(w, x[[5, 0, 2]], cuda)
+    assert np.array_equal(y3, y8[[5, 0, 2]])
+    y4 = gpu_batched(w, x * np.float32(4.0), cuda)
+    assert np.array_equal(y4, y8 * np.float32(4.0))
+    yn = gpu_batched(w, -x, cuda)
+    ref, tol = oracle.matvec_batched(w, -x)
+    assert_parity(yn, ref, tol, "-x")
+    assert np.all(np.abs(yn + y8) <= tol)
+
+
+def test_batched_wide_dynamic_range(cuda):
+    """x spread over twelve decades: the two bf16 parts still carry each
+    value to the f32 bound."""
+    m, p, n = 8, 96, 2048
+    w, _ = rich_case(p, n, seed=12)
+    rng = np.random.default_rng(12)
+    mag = 10.0 ** rng.uniform(-6, 6, size=(m, n))
+    x = (mag * rng.choice([-1.0, 1.0], size=(m, n))).astype(np.float32)
+    y = gpu_batched(w, x, cuda)
+    ref, tol = oracle.matvec_batched(w, x)
+    assert_parity(y, ref, tol, "wide range")
+
+
+def test_batched_special_scales(cuda):
+    """Subnormal scales everywhere, one NaN scale in row 3 of x row 0's
+    matrix: NaN reaches every x row of output row 3 only."""
+    m, p, n = 4, 64, 1024
+    rng = np.random.default_rng(13)
+    quants = rng.integers(-127, 128, size=(p, n // 32, 32))
+    sb = rng.integers(1, 0x400, size=(p, n // 32)).astype(np.uint16)
+    w = make_blocks(sb, quants)
+    x = gen.activations(m, n, seed=13, index=13)
+    y = gpu_batched(w, x, cuda)
+    ref, tol = oracle.matvec_batched(w, x)
+    assert_parity(y, ref, tol, "subnormal scales")
+    assert np.all(np.abs(y) > 0)
+    blk = w.reshape(p, n // 32, 34)
+    blk[3, 7, 0], blk[3, 7, 1] = 0x00, 0x7E
+    y = gpu_batched(w, x, cuda)
+    ref, tol = oracle.matvec_batched(w, x)
+    assert np.all(np.isnan(y[:, 3])) and np.all(np.isnan(ref[:, 3]))
+    assert_parity(y, ref, tol, "nan scale")
