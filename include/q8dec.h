@@ -19,7 +19,8 @@
  *   whose logits are all NaN yields -1.
  * The step (sections "One command buffer" and "The seam"): the 197 matvecs
  *   of one decode step (7 projections x 28 layers, then the lm_head and its
- *   argmax) are recorded once and submitted once, and one int32 comes back.
+ *   argmax) are recorded once and submitted once, and one int32 comes back
+ *   (written by the kernel into pinned host memory).
  *
  * Conventions for every entry point
  *   - Pointers named w, x, y, logits, idx are DEVICE pointers owned by the
@@ -132,21 +133,26 @@ typedef struct q8_step_graph q8_step_graph;
 /* How a step graph is recorded.
  *  Q8_GRAPH_CHAIN: one kernel node per descriptor, in descriptor order, each
  *    depending on the previous one (the in-order semantics of one command
- *    buffer), then the readback copy.
+ *    buffer).
  *  Q8_GRAPH_PERSISTENT: one kernel node that walks a device-side table of
  *    all descriptors with no ordering between them (valid when no
- *    descriptor reads another's output), then the readback copy. */
+ *    descriptor reads another's output). */
 #define Q8_GRAPH_CHAIN 0
 #define Q8_GRAPH_PERSISTENT 1
 
 /* Records the descriptors (1 <= count <= Q8_MAX_DESCS, at most
  * Q8_MAX_ARGMAX_DESCS with idx) for m activation rows into an instantiated
- * hipGraph.  If host_idx is non-NULL the graph ends with one device-to-host
- * copy of every argmax result (m int32 per argmax descriptor, in descriptor
- * order) into host_idx.  The descriptors' pointers are baked in: to change
- * inputs, write new values into the same x buffers.  `stream` only names the
- * device context; nothing is enqueued on it.  *out receives a handle owned
- * by the caller (free with q8_step_graph_destroy). */
+ * hipGraph.  If host_idx is non-NULL (pinned memory from hipHostMalloc,
+ * m int32 per argmax descriptor, in descriptor order) the kernel that
+ * finishes each argmax also stores its result there with system-scope
+ * stores, so the token reaches host memory with no copy node: the graph
+ * holds kernel nodes only.  Each host_idx entry is written once per launch,
+ * with its final value; the other outputs are valid once the stream is
+ * synchronised.  The descriptors' pointers are baked in: to change inputs,
+ * write new values into the same x buffers.  `stream` only names the device
+ * context; nothing is enqueued on it.  *out receives a handle owned by the
+ * caller (free with q8_step_graph_destroy).  A host_idx that is not pinned
+ * host memory is refused with Q8_ERR_HIP. */
 int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                         int32_t *host_idx, int32_t mode, void *stream,
                         q8_step_graph **out);
@@ -154,7 +160,8 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
 /* Enqueues the whole step with one hipGraphLaunch on `stream`. */
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
-/* Node counts of the instantiated graph (kernel nodes, memcpy nodes): the
+/* Node counts of the instantiated graph (kernel nodes, memcpy nodes; the
+ * latter are 0 since results reach host memory from the kernels): the
  * per-step dispatch budget. */
 int q8_step_graph_info(const q8_step_graph *g, int32_t *kernel_nodes,
                        int32_t *memcpy_nodes);

@@ -25,8 +25,12 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
+// Records a HIP failure for q8_last_hip_error and clears the runtime's
+// sticky last-error state, so that the failure is reported once, here, and
+// not again by the caller's next unrelated HIP call.
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
+  (void)hipGetLastError();
   return Q8_ERR_HIP;
 }
 
@@ -67,7 +71,7 @@ int ensure_device(int *dev_out) {
   hipFuncAttributes attr;
   e = hipFuncGetAttributes(&attr, q8::probe_kernel());
   if (e != hipSuccess) {
-    g_last_hip = (int)e;
+    hip_fail(e);
     st.status = Q8_ERR_CODE_OBJECT;
     return st.status;
   }
@@ -359,6 +363,12 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   int dev = 0;
   int st = ensure_device(&dev);
   if (st) return st;
+  // the kernels store the indices straight into the pinned host buffer
+  int32_t *host_dev = nullptr;
+  if (host_idx) {
+    hipError_t he = hipHostGetDevicePointer((void **)&host_dev, host_idx, 0);
+    if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
+  }
 
   q8_step_graph *g = new (std::nothrow) q8_step_graph();
   if (!g) return Q8_ERR_GRAPH;
@@ -390,25 +400,31 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   q8::StepDesc *table = (q8::StepDesc *)((char *)g->workspace + slot_bytes);
   q8::WgGroup *groups =
       (q8::WgGroup *)((char *)g->workspace + slot_bytes + table_bytes);
-  if (mode == Q8_GRAPH_PERSISTENT) {
+  {
     // argmax slots: keys and counters zero, arrival counts from the plan
+    // (persistent mode; the chain's kernels count their own grids), host
+    // copy of argmax descriptor a at host_idx + a * m
     std::vector<q8::ArgmaxSlot> hs(nargmax ? nargmax : 1);
     std::memset(hs.data(), 0, hs.size() * sizeof(q8::ArgmaxSlot));
-    int a = 0;
-    for (auto &t : plan.descs) {
-      if (!t.idx) continue;
-      uint32_t nteams = 0;
-      for (int j = 0; j < q8::kArgmaxTeams; j++) {
-        hs[a].team[j].expected = plan.expected[a][j];
-        nteams += plan.expected[a][j] ? 1u : 0u;
+    for (int a = 0; a < nargmax; a++)
+      hs[a].host = host_dev ? host_dev + (size_t)a * m : nullptr;
+    if (mode == Q8_GRAPH_PERSISTENT) {
+      int a = 0;
+      for (auto &t : plan.descs) {
+        if (!t.idx) continue;
+        uint32_t nteams = 0;
+        for (int j = 0; j < q8::kArgmaxTeams; j++) {
+          hs[a].team[j].expected = plan.expected[a][j];
+          nteams += plan.expected[a][j] ? 1u : 0u;
+        }
+        hs[a].top.expected = nteams;
+        t.slot = &slots[a++];
       }
-      hs[a].top.expected = nteams;
-      t.slot = &slots[a++];
     }
     e = hipMemcpy(slots, hs.data(), slot_bytes, hipMemcpyHostToDevice);
-    if (e == hipSuccess)
+    if (e == hipSuccess && table_bytes)
       e = hipMemcpy(table, plan.descs.data(), table_bytes, hipMemcpyHostToDevice);
-    if (e == hipSuccess)
+    if (e == hipSuccess && group_bytes)
       e = hipMemcpy(groups, plan.groups.data(), group_bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       release_graph(g);
@@ -437,28 +453,19 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
       le = q8::launch_step(table, count, groups, plan.group_size, m, plan.grid,
                            plan.lds, plan.all_staged, cs);
     }
-    if (le == hipSuccess && host_idx) {
-      int a = 0;
-      for (int32_t i = 0; i < count && le == hipSuccess; i++) {
-        if (!descs[i].idx) continue;
-        le = hipMemcpyAsync(host_idx + (size_t)a * m, descs[i].idx,
-                            sizeof(int32_t) * m, hipMemcpyDeviceToHost, cs);
-        a++;
-      }
-    }
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     g->graph = graph;
   }
   (void)hipStreamDestroy(cs);
   if (le != hipSuccess || e != hipSuccess || !g->graph) {
-    g_last_hip = (int)(le != hipSuccess ? le : e);
+    hip_fail(le != hipSuccess ? le : e);
     release_graph(g);
     return Q8_ERR_GRAPH;
   }
   e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    g_last_hip = (int)e;
+    hip_fail(e);
     release_graph(g);
     return Q8_ERR_GRAPH;
   }

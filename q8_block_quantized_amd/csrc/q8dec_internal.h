@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <vector>
@@ -12,14 +13,17 @@ namespace q8 {
 // One arrival group of the cross-workgroup argmax: a 64-bit key per
 // activation row, an arrival counter and the number of arrivals it waits
 // for (0: every workgroup of the grid arrives once, and the kernel works the
-// count out itself), padded to 256 bytes.
+// count out itself).  The keys and the counter sit in different 128-byte
+// lines, so atomics on one do not queue behind atomics on the other.
 struct ArgmaxGroup {
   unsigned long long keys[8];
+  unsigned int pad0[16];
   unsigned int counter;
   unsigned int expected;
-  unsigned int pad[46];
+  unsigned int pad1[30];
 };
 static_assert(sizeof(ArgmaxGroup) == 256, "group layout");
+static_assert(offsetof(ArgmaxGroup, counter) == 128, "counter line");
 
 #ifndef Q8_ARGMAX_TEAMS
 #define Q8_ARGMAX_TEAMS 32
@@ -30,10 +34,14 @@ constexpr int kArgmaxTeams = Q8_ARGMAX_TEAMS;
 // g % kArgmaxTeams; the last arrival of a team forwards the team's keys to
 // the top group, and the last team writes the indices.  Keys and counters
 // are zero between launches: the arrival that completes a group reads and
-// clears them.
+// clears them.  When `host` is set, the indices are also stored there with
+// system-scope stores, so they reach host memory without a copy.
 struct ArgmaxSlot {
   ArgmaxGroup top;
   ArgmaxGroup team[kArgmaxTeams];
+  int32_t *host;  // device address of pinned host memory that also receives
+                  // the indices, or NULL
+  unsigned long long pad[7];
 };
 
 // One matvec of a launch, as the kernels see it.

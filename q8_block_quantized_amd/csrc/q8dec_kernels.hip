@@ -180,15 +180,6 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned long long u = __shfl_xor(v, o);
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
 // ---- argmax keys --------------------------------------------------------
 
 __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t row) {
@@ -208,33 +199,62 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a,
   return a > b ? a : b;
 }
 
-// Adds this workgroup's keys best[0..m-1] to the slot.  Workgroup `wg` of a
-// grid of `nwg` joins team wg % kArgmaxTeams; the team's last arrival moves
-// the team keys to the top group, and the top group's last arrival writes
-// idx[0..m-1].  Arrival counts come from the groups' `expected` fields, or,
-// when those are 0, from "every workgroup arrives once".  Atomics are
-// relaxed: each counter increment is issued only after the key updates
-// before it have returned (performed at the memory side), which orders them
-// without L2 write-back or invalidation.  Called by every thread of the
-// workgroup.
-// `scratch` is kWaves * 8 * 8 bytes of LDS that no thread reads or writes
-// meanwhile.
-__device__ void argmax_finish(const unsigned long long *best, int m,
+// A 64-bit value of lane l (l uniform).
+__device__ __forceinline__ unsigned long long readlane64(unsigned long long v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Unsigned max over each 16-lane row, left in the row's last lane (lanes
+// shifted in from outside the row read 0, the empty key).
+__device__ __forceinline__ unsigned long long row16_max(unsigned long long v) {
+  v = umax64(v, dpp64<0x111>(v));  // row_shr:1
+  v = umax64(v, dpp64<0x112>(v));  // row_shr:2
+  v = umax64(v, dpp64<0x114>(v));  // row_shr:4
+  v = umax64(v, dpp64<0x118>(v));  // row_shr:8
+  return v;
+}
+
+// Maximum over the wave.
+__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
+  v = row16_max(v);
+  return umax64(umax64(readlane64(v, 15), readlane64(v, 31)),
+                umax64(readlane64(v, 47), readlane64(v, 63)));
+}
+
+// Adds a workgroup's keys to the slot.  lk[w][r] (LDS) holds wave w's key of
+// activation row r < m (0: none); every wave writes its entries before the
+// call, which every thread makes.  Workgroup `wg` of a grid of `nwg` joins
+// team wg % kArgmaxTeams: it raises the team keys with atomic max and then
+// counts itself in.  The team's last arrival counts the team into the top
+// group; the top group's last arrival takes (and clears) every team's keys
+// and writes idx[0..m-1] (and the slot's host copy, if any).  Arrival
+// counts come from the groups' `expected`
+// fields, or, when those are 0, from "every workgroup arrives once".
+// Atomics are relaxed: each counter increment is issued only after the
+// updates before it have returned (performed at the memory side), which
+// orders them without L2 write-back or invalidation.  Four dependent round
+// trips separate the last arrival from the result.
+__device__ void argmax_arrive(const unsigned long long (*lk)[8], int m,
                               ArgmaxSlot *__restrict__ slot,
                               int32_t *__restrict__ idx, uint32_t wg,
-                              uint32_t nwg, void *scratch) {
-  unsigned long long(*red)[8] = (unsigned long long(*)[8])scratch;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int r = 0; r < 8; r++) {
-    if (r < m) {
-      unsigned long long v = wave_max_u64(best[r]);
-      if (lane == 0) red[wave][r] = v;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t T = kArgmaxTeams;
+                              uint32_t nwg) {
+  __syncthreads();  // lk is complete
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const uint32_t T = kArgmaxTeams;
+  uint32_t last = 0;
+  int32_t *host = nullptr;
+  if (lane == 0) {
+    host = gp(&slot->host)[0];  // read early: it is needed at the very end
     const uint32_t j = wg % T;
     ArgmaxGroup *g = &slot->team[j];
     uint32_t size = gp(&g->expected)[0], nteams = gp(&slot->top.expected)[0];
@@ -242,40 +262,47 @@ __device__ void argmax_finish(const unsigned long long *best, int m,
       size = (nwg - j + T - 1) / T;
       nteams = nwg < T ? nwg : T;
     }
-    unsigned long long v[8];
     unsigned long long dep = 0ull;
     for (int r = 0; r < m; r++) {
-      v[r] = red[0][r];
-      for (int w = 1; w < kWaves; w++) v[r] = umax64(v[r], red[w][r]);
-      dep |= __hip_atomic_fetch_max(&g->keys[r], v[r], __ATOMIC_RELAXED,
+      unsigned long long v = lk[0][r];
+      for (int w = 1; w < kWaves; w++) v = umax64(v, lk[w][r]);
+      dep |= __hip_atomic_fetch_max(&g->keys[r], v, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("" ::"v"(dep));  // the maxima have returned
     const uint32_t prev = __hip_atomic_fetch_add(&g->counter, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev == size - 1u) {
-      dep = 0ull;
-      for (int r = 0; r < m; r++) {
-        const unsigned long long tk = __hip_atomic_exchange(
-            &g->keys[r], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        dep |= __hip_atomic_fetch_max(&slot->top.keys[r], tk, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-      }
       __hip_atomic_store(&g->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("" ::"v"(dep));
       const uint32_t p2 = __hip_atomic_fetch_add(&slot->top.counter, 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (p2 == nteams - 1u) {
-        for (int r = 0; r < m; r++)
-          idx[r] = key_index(__hip_atomic_exchange(&slot->top.keys[r], 0ull,
-                                                   __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-        __hip_atomic_store(&slot->top.counter, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      last = p2 == nteams - 1u;
+    }
+  }
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
+  // Every team is complete: lane j takes team j's keys in one round trip.
+  unsigned long long v[8];
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    v[r] = 0ull;
+    if (r < m && lane < (int)T)
+      v[r] = __hip_atomic_exchange(&slot->team[lane].keys[r], 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    if (r < m) {
+      const unsigned long long k = wave_max64(v[r]);
+      if (lane == 0) {
+        idx[r] = key_index(k);
+        if (host)
+          __hip_atomic_store(&host[r], key_index(k), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
-  __syncthreads();  // the scratch is free again
+  if (lane == 0)
+    __hip_atomic_store(&slot->top.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- matvec geometry ---------------------------------------------------------
@@ -937,15 +964,34 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       run_direct<M1>(c, cur.path, best, keys);
     }
     if (keys && (!more || nxt.desc != cur.desc)) {
-      if (!M1) {
-        const int xr = threadIdx.x < 128 ? (int)(threadIdx.x >> 4) : 8;
+      // each wave's keys (the batched path holds x row r's in 16-lane row
+      // r & 3 of wave r / 4) go to the start of the tile buffer once every
+      // wave is done reading it (a static LDS array measured slower)
+      __syncthreads();
+      unsigned long long(*lk)[8] = (unsigned long long(*)[8])lds;
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      if (mfma(cur)) {
+        const unsigned long long rm = row16_max(kb);
 #pragma unroll
-        for (int r = 0; r < 8; r++) best[r] = umax64(best[r], r == xr ? kb : 0ull);
+        for (int r = 0; r < 8; r++) {
+          if (r < m) {
+            const unsigned long long k =
+                (r >> 2) == wave ? readlane64(rm, 16 * (r & 3) + 15) : 0ull;
+            if (lane == 0) lk[wave][r] = k;
+          }
+        }
         kb = 0ull;
-      }
-      argmax_finish(best, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x, lds);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 8; r++) best[r] = 0ull;
+        for (int r = 0; r < 8; r++) {
+          if (r < m) {
+            const unsigned long long k = wave_max64(best[r]);
+            if (lane == 0) lk[wave][r] = k;
+          }
+          best[r] = 0ull;
+        }
+      }
+      argmax_arrive(lk, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x);
     }
     if (!more) break;
     t = tn;
@@ -990,13 +1036,12 @@ argmax_rows(const float *__restrict__ logits, int32_t m, int32_t p,
   unsigned long long key = 0ull;
   for (int32_t e = blockIdx.x * kWG + threadIdx.x; e < p; e += gridDim.x * kWG)
     key = umax64(key, argmax_key(row[e], (uint32_t)e));
-  unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
-#pragma unroll
-  for (int i = 0; i < 8; i++)
-    if (i == (int)blockIdx.y) best[i] = key;
-  __shared__ unsigned long long red[kWaves * 8];
-  argmax_finish(best, m, slot, idx, blockIdx.y * gridDim.x + blockIdx.x,
-                gridDim.x * gridDim.y, red);
+  __shared__ unsigned long long lk[kWaves][8];
+  key = wave_max64(key);
+  if ((threadIdx.x & 63) == 0)
+    for (int r = 0; r < m; r++) lk[threadIdx.x >> 6][r] = r == (int)blockIdx.y ? key : 0ull;
+  argmax_arrive(lk, m, slot, idx, blockIdx.y * gridDim.x + blockIdx.x,
+                gridDim.x * gridDim.y);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -1051,11 +1096,26 @@ int mv_grid_cap(int dev) {
 }
 
 template <bool M1, bool ANY>
-hipError_t launch_mv(const StepDesc &d, int m, hipStream_t s) {
+hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  const int32_t ntiles = tiles_of(d);
   const int cap = mv_grid_cap<M1, ANY>(dev);
+  // Every workgroup takes whole rounds of tiles, so the last round may be
+  // part-empty.  Among tile heights from the largest down to three quarters
+  // of it, take the one whose busiest workgroup costs least, counting a
+  // tile as its rows plus four rows' worth of fixed work (barriers, LDS
+  // staging).  Batched tiles stay whole 16-row groups.
+  if (path_of(m, d.n) != kMfma && tiles_of(d) > cap) {
+    int32_t best_rows = d.rows_per_tile;
+    int64_t best_cost = INT64_MAX;
+    for (int32_t r = d.rows_per_tile; r >= (3 * d.rows_per_tile + 3) / 4; r--) {
+      const int64_t tiles = ((int64_t)d.p + r - 1) / r;
+      const int64_t cost = (tiles + cap - 1) / cap * (r + 4);
+      if (cost < best_cost) best_cost = cost, best_rows = r;
+    }
+    d.rows_per_tile = best_rows;
+  }
+  const int32_t ntiles = tiles_of(d);
   const int grid = ntiles < cap ? ntiles : cap;
   hipLaunchKernelGGL((mv_kernel<M1, ANY>), dim3(grid), dim3(kWG),
                      lds_bytes_for(m, d.n), s, d, m);

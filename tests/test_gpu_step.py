@@ -60,7 +60,7 @@ def test_small_step_matches_standalone_calls(cuda, mode):
     descs = device_step(shapes, ws, xs, m, cuda)
     g, host = run_graph(descs, m, mode, cuda)
     k, c = g.info()
-    assert (k, c) == ((len(shapes), 1) if mode == 0 else (1, 1))
+    assert (k, c) == ((len(shapes), 0) if mode == 0 else (1, 0))
     # standalone results
     want = []
     for d in descs[:-1]:
@@ -95,7 +95,7 @@ def test_full_step_against_oracle(cuda, mode):
     shapes, ws, xs = step_inputs(28, 151936, m, seed=0)
     descs = device_step(shapes, ws, xs, m, cuda)
     g, host = run_graph(descs, m, mode, cuda)
-    assert g.info() == ((197, 1) if mode == 0 else (1, 1))
+    assert g.info() == ((197, 0) if mode == 0 else (1, 0))
     g.launch()
     torch.cuda.synchronize()
     say("full step: checking against the oracle")
@@ -140,3 +140,45 @@ def test_destroyed_handle_is_refused(cuda):
     g.close()
     assert q8.load().q8_step_graph_launch(h, None) == 9
     assert q8.load().q8_step_graph_destroy(h) == 9
+
+
+def test_unpinned_host_idx_is_refused(cuda):
+    """The token is stored by the kernel into host_idx, so host_idx must be
+    pinned host memory; ordinary pageable memory is refused before any GPU
+    work (Q8_ERR_HIP), straight through the C ABI."""
+    import ctypes
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(0, 64, 1, seed=5)
+    descs = device_step(shapes, ws, xs, 1, cuda)
+    d = descs[0]
+    arr = (q8.MatvecDesc * 1)()
+    arr[0] = q8.MatvecDesc(d["w"].data_ptr(), d["x"].data_ptr(), d["y"].data_ptr(),
+                           d["idx"].data_ptr(), d["n"], d["p"])
+    pageable = (ctypes.c_int32 * 4)()
+    out = ctypes.c_void_p()
+    st = q8.load().q8_step_graph_build(arr, 1, 1, ctypes.addressof(pageable), 1, None,
+                                       ctypes.byref(out))
+    assert st == 7 and not out.value
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["chain", "persistent"])
+def test_token_reaches_host_without_copy(cuda, mode):
+    """The argmax's last arrival stores each row's token into pinned host
+    memory itself: the graph has no copy node, and the host value equals the
+    device idx after the stream is synchronised, for every launch."""
+    import torch
+    m = 3
+    shapes, ws, xs = step_inputs(1, 5000, m, seed=6)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, mode, cuda)
+    assert g.info()[1] == 0
+    for k in range(3):
+        host[:] = -9
+        g.launch()
+        torch.cuda.synchronize()
+        dev_idx = descs[-1]["idx"].cpu()
+        assert torch.equal(host, dev_idx), (k, host, dev_idx)
+    ref, tol = oracle.matvec_batched(ws[-1], xs[-1])
+    for r in range(m):
+        assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+    g.close()
