@@ -381,7 +381,8 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   const size_t slot_bytes = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
   q8::StepPlan plan;
   if (mode == Q8_GRAPH_PERSISTENT) {
-    st = q8::plan_step(descs, count, m, dev, q8::kStepGroupSize, plan);
+    st = q8::plan_step(descs, count, m, dev,
+                       m == 1 ? q8::kStepGroupSize : q8::kStepGroupSizeBatched, plan);
     if (st) {
       release_graph(g);
       return st;

@@ -107,8 +107,13 @@ struct StepPlan {
   bool all_staged = true;
 };
 
-// Workgroups per group of the persistent step.
+// Workgroups per group of the persistent step.  m = 1: groups of 32
+// streaming neighbouring tiles were fastest on MI355X (a sweep of 1..4096).
+// Batched: a workgroup reloads its slice of x at every new matvec, so each
+// keeps a contiguous range of its own (groups of 2: 165 us per m = 8 step
+// against 206 us with 32).
 constexpr int kStepGroupSize = 32;
+constexpr int kStepGroupSizeBatched = 2;
 
 // Host stub of one kernel, used to check that the code object loads.
 const void *probe_kernel();

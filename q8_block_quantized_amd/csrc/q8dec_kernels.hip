@@ -338,7 +338,8 @@ constexpr int kMfmaRowPad = 16;
 constexpr int kMfmaTileBytes = 53248;  // LDS of a batched tile, pads included
 constexpr int kMfmaChunks = (kMfmaTileBytes + 16 * kWG - 1) / (16 * kWG);
 constexpr int kMfmaMaxBlocks = kMaxLdsBlocks / kWaves;  // x blocks per wave
-constexpr int kRedFloats = 2 * kWaves * 256;  // two sets of 16 x 16 partials per wave
+constexpr int kRedStride = 80;  // floats between a wave's partial-sum entries
+constexpr int kRedFloats = 2 * kWaves * 4 * kRedStride;  // two sets per wave
 
 __host__ __device__ inline int path_of(int m, int n) {
   const int bpr = n >> 5;
@@ -565,13 +566,17 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
   const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
   const int wave = threadIdx.x >> 6;
   const int32_t pitch = bpr * 34;
+  // With one block per lane (n <= 1024) the lane's 32 x values are the same
+  // for every row: they are read from LDS once per tile.
+  float xk[32];
+  if (NBL == 1) load_x32(xs + 36 * min(k, bpr - 1), xk);
   for (int32_t rr0 = 2 * wave; rr0 < rows; rr0 += kRowsPerPass) {
     const int32_t rr = rr0 + half;
     const int32_t rc = rr < rows ? rr : rows - 1;
     float acc = 0.f;
     // keeps the x reads inside the loop (hoisted, they would pin 32 * NBL
     // registers for the whole tile)
-    asm volatile("" ::: "memory");
+    if (NBL > 1) asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NBL; i++) {
       const int32_t b = min(k + 32 * i, bpr - 1);
@@ -582,7 +587,12 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
       for (int q = 0; q < 9; q++) d[q] = wp[q];
       const uint32_t amod = (uint32_t)o & 2u;
       float xb[32];
-      load_x32(xs + 36 * b, xb);
+      if (NBL == 1) {
+#pragma unroll
+        for (int t = 0; t < 32; t++) xb[t] = xk[t];
+      } else {
+        load_x32(xs + 36 * b, xb);
+      }
       const float v = scale_of(d, amod) * block_dot(d, quant_sel(amod), xb);
       acc += (k + 32 * i < bpr) ? v : 0.f;
     }
@@ -726,16 +736,22 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
         }
       }
     }
-    float *rb = red + buf * (kWaves * 256);
+    // partials: entry r of lane l at kRedStride * r + l, so a wave's
+    // writes (fixed r) and its reads below (four r, sixteen lanes each)
+    // both fall in 64 different banks; column i of row jj is entry i % 4
+    // of lane 16 (i / 4) + jj
+    float *rb = red + buf * (kWaves * 4 * kRedStride);
 #pragma unroll
-    for (int r = 0; r < 4; r++) rb[wave * 256 + (4 * g + r) * 16 + j] = acc[r];
+    for (int r = 0; r < 4; r++) rb[(wave * 4 + r) * kRedStride + lane] = acc[r];
     __syncthreads();
     if (threadIdx.x < 128) {
       const int xr = threadIdx.x >> 4, jj = threadIdx.x & 15;
+      const int hi = (xr & 3) * kRedStride + 16 * (xr >> 2) + jj;  // column xr
+      const int lo = hi + 32;                                      // column xr + 8
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; w++)
-        v += rb[w * 256 + xr * 16 + jj] + rb[w * 256 + (xr + 8) * 16 + jj];
+        v += rb[w * 4 * kRedStride + hi] + rb[w * 4 * kRedStride + lo];
       const int32_t rr = rg + jj;
       if (xr < m && rr < rows) {
         if (y) gpw(y)[(int64_t)xr * p + r0 + rr] = v;
