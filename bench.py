@@ -183,6 +183,34 @@ def cpu_baseline(sets, m_host, threads_req: int, budget_s: float):
     return statistics.median(times), used, worst, ok_idx
 
 
+def only_workload(args, torch, q8, dev) -> int:
+    """One configuration alone, for a kernel trace or counters of its kernel."""
+    out = {"workload": args.only, "steps": args.steps}
+    if args.only == "lm_head":
+        # 4 weight copies (661 MB, beyond the Infinity Cache) rotated
+        ws = [torch.from_numpy(gen.weights(151936, 1024, seed=0, index=3000 + c)
+                               .reshape(-1)).to(dev) for c in range(4)]
+        x = torch.from_numpy(gen.activations(1, 1024, seed=0, index=3000)).to(dev)
+        idx = torch.empty(1, dtype=torch.int32, device=dev)
+        t = event_time(torch, lambda k: q8.q8_matvec_argmax(ws[k % 4], x, idx, 151936),
+                       args.steps, args.warmup)
+        b = alg_bytes(1024, 151936, 1, False, True)
+        out.update(avg_us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), alg_bytes=b)
+    else:
+        sets8 = [StepSet(torch, dev, 0, 5000 + 1000 * j, 8, False) for j in range(2)]
+        host8 = torch.zeros(8, dtype=torch.int32).pin_memory()
+        p8 = [q8.StepGraph(s.descs, 8, host_idx=host8, mode=q8.Q8_GRAPH_PERSISTENT)
+              for s in sets8]
+        s8, _ = time_graph_steps(torch, p8, host8, args.steps, args.warmup, poll=True)
+        b8 = sets8[0].bytes
+        out.update(step_latency_us=round(s8 * 1e6, 2), GBps=round(b8 / s8 / 1e9, 1),
+                   alg_bytes=b8)
+        for g in p8:
+            g.close()
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +219,10 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--only", choices=["lm_head", "batched"], default=None,
+                    help="only time one other configuration (for profiling runs): "
+                         "the fused lm_head (1024 -> 151,936 + argmax, m = 1) or "
+                         "the m = 8 step; prints one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
@@ -215,6 +247,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
         return 0
     q8.q8_init()
+    if args.only:
+        return only_workload(args, torch, q8, dev)
     log("generating two weight sets of a decode step (2 x 633 MB)")
     sets = [StepSet(torch, dev, 0, 0, 1, False), StepSet(torch, dev, 0, 1000, 1, False)]
     host = torch.zeros(1, dtype=torch.int32).pin_memory()

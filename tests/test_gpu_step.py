@@ -131,6 +131,34 @@ def test_batched_step(cuda, mode):
     g.close()
 
 
+def test_full_batched_step_sampled(cuda):
+    """m = 8 through all 197 shapes of a step (28 layers + lm_head), in the
+    persistent launch the benchmark times: every matvec checked on 64
+    sampled rows (first, last, and a seeded spread) for all 8 x rows, and
+    the lm_head's 8 tokens against the oracle's full logits."""
+    import torch
+    m = 8
+    say("full m=8 step: generating 197 matvecs")
+    shapes, ws, xs = step_inputs(28, 151936, m, seed=2)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, 1, cuda)
+    g.launch()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    say("full m=8 step: checking sampled rows against the oracle")
+    for i, (name, n, p) in enumerate(shapes):
+        y = descs[i]["y"].cpu().numpy()
+        rows = np.unique(np.concatenate([[0, p - 1], rng.integers(0, p, 62)]))
+        ref, tol = oracle.matvec_batched(ws[i][rows], xs[i])
+        assert_parity(y[:, rows], ref, tol, f"m=8 {name}")
+    ref, tol = oracle.matvec_batched(ws[-1], xs[-1])
+    y = descs[-1]["y"].cpu().numpy()
+    for r in range(m):
+        assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+        assert int(host[r]) == oracle.argmax_f32(y[r])
+    g.close()
+
+
 def test_destroyed_handle_is_refused(cuda):
     import q8_block_quantized_amd as q8
     shapes, ws, xs = step_inputs(0, 64, 1, seed=4)
