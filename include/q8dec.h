@@ -160,6 +160,15 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
 /* Enqueues the whole step with one hipGraphLaunch on `stream`. */
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
+/* Q8_GRAPH_PERSISTENT only: enqueues the same recorded step (its one
+ * kernel, with the arguments fixed at build time) with a single kernel
+ * launch instead of hipGraphLaunch: the same work, results and host_idx
+ * writes.  Runs on the graph's device whatever device is current; `stream`
+ * must belong to that device.  On MI355X with ROCm 7.2 a hipGraphLaunch
+ * costs ~10 us more launch latency than a kernel launch (measured).
+ * Q8_ERR_MODE for a chain graph. */
+int q8_step_graph_launch_kernel(q8_step_graph *g, void *stream);
+
 /* Node counts of the instantiated graph (kernel nodes, memcpy nodes; the
  * latter are 0 since results reach host memory from the kernels): the
  * per-step dispatch budget. */

@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH):
                                                i32, vp, i32, vp,
                                                ctypes.POINTER(vp)]),
         "q8_step_graph_launch": (ctypes.c_int, [vp, vp]),
+        "q8_step_graph_launch_kernel": (ctypes.c_int, [vp, vp]),
         "q8_step_graph_info": (ctypes.c_int, [vp, pi32, pi32]),
         "q8_step_graph_destroy": (ctypes.c_int, [vp]),
     }
@@ -259,6 +260,10 @@ class StepGraph:
 
     def launch(self, stream=None) -> None:
         _check(load().q8_step_graph_launch(self._h, _stream(stream, self.device)))
+
+    def launch_kernel(self, stream=None) -> None:
+        """The same recorded step as one kernel launch (persistent mode)."""
+        _check(load().q8_step_graph_launch_kernel(self._h, _stream(stream, self.device)))
 
     def info(self) -> tuple[int, int]:
         k, c = ctypes.c_int32(0), ctypes.c_int32(0)

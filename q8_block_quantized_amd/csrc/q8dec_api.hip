@@ -123,6 +123,12 @@ struct q8_step_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;
   void *workspace;  // argmax slots (+ descriptor table in persistent mode)
+  // persistent mode: the recorded kernel launch, for q8_step_graph_launch_kernel
+  const q8::StepDesc *table;
+  const q8::WgGroup *groups;
+  int32_t count, m, group_size, grid;
+  size_t lds;
+  bool all_staged;
 };
 
 namespace {
@@ -453,6 +459,14 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
     } else {
       le = q8::launch_step(table, count, groups, plan.group_size, m, plan.grid,
                            plan.lds, plan.all_staged, cs);
+      g->table = table;
+      g->groups = groups;
+      g->count = count;
+      g->m = m;
+      g->group_size = plan.group_size;
+      g->grid = plan.grid;
+      g->lds = plan.lds;
+      g->all_staged = plan.all_staged;
     }
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
@@ -486,6 +500,19 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
 int q8_step_graph_launch(q8_step_graph *g, void *stream) {
   if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
   hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_step_graph_launch_kernel(q8_step_graph *g, void *stream) {
+  if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
+  if (g->mode != Q8_GRAPH_PERSISTENT) return Q8_ERR_MODE;
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cur != g->device && (e = hipSetDevice(g->device)) != hipSuccess) return hip_fail(e);
+  e = q8::launch_step(g->table, g->count, g->groups, g->group_size, g->m, g->grid,
+                      g->lds, g->all_staged, (hipStream_t)stream);
+  if (cur != g->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 

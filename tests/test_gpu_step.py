@@ -159,6 +159,35 @@ def test_full_batched_step_sampled(cuda):
     g.close()
 
 
+@pytest.mark.parametrize("m", [1, 8])
+def test_kernel_launch_equals_graph_launch(cuda, m):
+    """q8_step_graph_launch_kernel enqueues the recorded persistent step with
+    one kernel launch: every output and the host tokens equal the graph
+    launch's bit for bit; a chain graph refuses it (Q8_ERR_MODE)."""
+    import torch
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(2, 20000, m, seed=7)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, 1, cuda)
+    g.launch()
+    torch.cuda.synchronize()
+    want = [d["y"].clone() for d in descs]
+    want_tok = host.clone()
+    for _ in range(3):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        host[:] = -9
+        g.launch_kernel()
+        torch.cuda.synchronize()
+        for d, w in zip(descs, want):
+            assert torch.equal(d["y"], w)
+        assert torch.equal(host, want_tok)
+    g.close()
+    gc, _ = run_graph(descs, m, 0, cuda)
+    assert q8.load().q8_step_graph_launch_kernel(gc._h, None) == 11
+    gc.close()
+
+
 def test_destroyed_handle_is_refused(cuda):
     import q8_block_quantized_amd as q8
     shapes, ws, xs = step_inputs(0, 64, 1, seed=4)
