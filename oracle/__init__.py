@@ -50,6 +50,10 @@ def _bind(lib):
     lib.q8o_argmax_f64.argtypes = [vp, i64]
     lib.q8o_argmax_f32.restype = i64
     lib.q8o_argmax_f32.argtypes = [vp, i64]
+    lib.q8o_quantize_x.argtypes = [vp, i64, vp, vp]
+    lib.q8o_quantize_x.restype = None
+    lib.q8o_matvec_i8x.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+    lib.q8o_matvec_i8x.restype = None
     return lib
 
 
@@ -109,6 +113,33 @@ class Oracle:
                                       y.ctypes.data, tol.ctypes.data, threads)
         return y, tol, used
 
+    def quantize_x(self, x: np.ndarray):
+        """Q8_0 activation blocks of x[n]: d (float32 [n/32]), q (int8 [n])."""
+        x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+        n = x.size
+        if n % 32:
+            raise ValueError("n must be a multiple of 32")
+        d = np.empty(n // 32, dtype=np.float32)
+        q = np.empty(n, dtype=np.int8)
+        self.lib.q8o_quantize_x(x.ctypes.data, n, d.ctypes.data, q.ctypes.data)
+        return d, q
+
+    def matvec_i8x(self, w: np.ndarray, x: np.ndarray, p: int | None = None):
+        """y, tol (float64 [m, p]) of the int8-activation product, x [m, n]
+        (or [n]: then [p]); each x row is quantised by quantize_x."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        flat = x.ndim == 1
+        x2 = x.reshape(1, -1) if flat else x
+        m, n = x2.shape
+        w, p = self._check_w(w, n, p)
+        y = np.empty((m, p), dtype=np.float64)
+        tol = np.empty((m, p), dtype=np.float64)
+        for i in range(m):
+            d, q = self.quantize_x(x2[i])
+            self.lib.q8o_matvec_i8x(w.ctypes.data, d.ctypes.data, q.ctypes.data, n, p,
+                                    y[i].ctypes.data, tol[i].ctypes.data)
+        return (y[0], tol[0]) if flat else (y, tol)
+
     def argmax_f64(self, v) -> int:
         v = np.ascontiguousarray(v, dtype=np.float64).ravel()
         return int(self.lib.q8o_argmax_f64(v.ctypes.data, v.size))
@@ -137,6 +168,14 @@ def matvec(w, x, p=None):
 
 def matvec_batched(w, x, p=None):
     return get().matvec_batched(w, x, p)
+
+
+def quantize_x(x):
+    return get().quantize_x(x)
+
+
+def matvec_i8x(w, x, p=None):
+    return get().matvec_i8x(w, x, p)
 
 
 def argmax_f64(v) -> int:

@@ -23,6 +23,17 @@
  * exactly; quant byte 0x80 is the int8 value -128; NaN logits never win the
  * argmax and an all-NaN row gives -1; -0 and +0 compare equal.
  *
+ * The int8-activation variant (inferno.rs "IV.4", the prose after the
+ * q8_matvec listing in "Eight kernels" and "The correctness ladder": the
+ * CPU's sdot kernel quantises the activations and multiplies integers).  The
+ * pages do not give the quantiser; the reading used here is the Q8_0 rule
+ * applied to x, per block of 32, in binary32: amax = max |x_j|, d = amax/127,
+ * q_j = x_j * (1/d) rounded to the nearest integer, ties to even (so
+ * |q_j| <= 127); d = 0 gives q = 0; a block holding a NaN or an infinity gets
+ * d = NaN and q = 0.  The product is then
+ *   y[r] = sum_b scale_b * d_b * sum_j qw_bj * qx_bj
+ * with the integer sums exact and the rest in binary64, natural order.
+ *
  * Build: plain C11, no -ffast-math, floating contraction off.
  */
 #include <math.h>
@@ -148,4 +159,55 @@ int64_t q8o_argmax_f32(const float *v, int64_t p) {
     }
   }
   return best;
+}
+
+/* ---- int8-activation variant ---------------------------------------------- */
+
+/* Q8_0 quantisation of n activations (n % 32 == 0): d[n/32], q[n]. */
+void q8o_quantize_x(const float *x, int64_t n, float *d, int8_t *q) {
+  for (int64_t b = 0; b < n / 32; b++) {
+    const float *xb = x + 32 * b;
+    float amax = 0.0f;
+    int bad = 0;
+    for (int j = 0; j < 32; j++) {
+      float a = fabsf(xb[j]);
+      if (!isfinite(a)) bad = 1;
+      else if (a > amax) amax = a;
+    }
+    if (bad) {
+      d[b] = NAN;
+      for (int j = 0; j < 32; j++) q[32 * b + j] = 0;
+      continue;
+    }
+    float db = amax / 127.0f;
+    float inv = db != 0.0f ? 1.0f / db : 0.0f;
+    d[b] = db;
+    for (int j = 0; j < 32; j++) q[32 * b + j] = (int8_t)rintf(xb[j] * inv);
+  }
+}
+
+/* y[p] (and tol[p] if non-NULL) from quantised activations d[n/32], q[n]:
+ * y = sum_b scale*d*isum, isum = sum_j qw*qx (exact integer); tol =
+ * 1e-4 * sum_b |scale*d| * sum_j |qw*qx| + 1e-6. */
+void q8o_matvec_i8x(const uint8_t *w, const float *d, const int8_t *q,
+                    int64_t n, int64_t p, double *y, double *tol) {
+  const int64_t blocks = n / 32;
+  for (int64_t r = 0; r < p; r++) {
+    const uint8_t *row = w + (size_t)r * (size_t)blocks * 34u;
+    double acc = 0.0, size = 0.0;
+    for (int64_t b = 0; b < blocks; b++) {
+      const uint8_t *blk = row + (size_t)b * 34u;
+      const double sd = q8o_half_to_double((uint16_t)(blk[0] | (blk[1] << 8))) * (double)d[b];
+      int64_t isum = 0, iabs = 0;
+      for (int j = 0; j < 32; j++) {
+        const int64_t prod = (int64_t)(int8_t)blk[2 + j] * (int64_t)q[32 * b + j];
+        isum += prod;
+        iabs += prod < 0 ? -prod : prod;
+      }
+      acc += sd * (double)isum;
+      size += fabs(sd) * (double)iabs;
+    }
+    y[r] = acc;
+    if (tol) tol[r] = 1e-4 * size + 1e-6;
+  }
 }

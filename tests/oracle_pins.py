@@ -289,6 +289,127 @@ def pin_argmax_rules(orc):
         assert orc.argmax_f32(np.array(vals, dtype=np.float32)) == want, vals
 
 
+# ---- int8-activation variant -----------------------------------------------
+
+def _golden_q8x():
+    d, rows = None, []
+    for line in open(os.path.join(GOLDEN, "q8x_quantize.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        if line[0] == "d":
+            d = float(line[1])
+        else:
+            rows.append((int(line[0]), int(line[1])))
+    return d, rows
+
+
+def pin_q8x_quantize_golden(orc):
+    """A block whose exact quantisation follows by hand: ties go to even."""
+    d_want, rows = _golden_q8x()
+    x = np.zeros(32, dtype=np.float32)
+    for j, (k, _) in enumerate(rows):
+        x[j] = k * 2.0 ** -7
+    d, q = orc.quantize_x(x)
+    assert float(d[0]) == d_want
+    for j, (_, qw) in enumerate(rows):
+        assert int(q[j]) == qw, (j, int(q[j]), qw)
+    assert np.all(q[len(rows):] == 0)
+
+
+def pin_q8x_quantize_properties(orc):
+    """Every code lies within half a step of x/d, |q| <= 127, the largest |x|
+    of a block maps to +-127, and d * 127 is amax to binary32 rounding."""
+    rng = np.random.default_rng(21)
+    for scale in (1.0, 1e-3, 1e4):
+        x = (rng.standard_normal(32 * 40) * scale).astype(np.float32)
+        x[::97] *= 50.0  # outliers
+        d, q = orc.quantize_x(x)
+        xb = x.reshape(-1, 32).astype(np.float64)
+        qb = q.reshape(-1, 32).astype(np.float64)
+        dd = d.astype(np.float64)[:, None]
+        assert np.all(np.abs(qb) <= 127)
+        assert np.all(np.abs(xb - dd * qb) <= dd * (0.5 + 1e-6))
+        top = np.argmax(np.abs(xb), axis=1)
+        assert np.all(np.abs(qb[np.arange(len(top)), top]) == 127)
+        amax = np.abs(xb).max(axis=1)
+        assert np.all(np.abs(dd[:, 0] * 127 - amax) <= amax * 2.0 ** -22)
+
+
+def pin_q8x_quantize_special(orc):
+    """A zero block quantises to d = 0, q = 0; a block holding a NaN or an
+    infinity to d = NaN, q = 0, and its neighbours are unaffected."""
+    x = np.ones(32 * 4, dtype=np.float32)
+    x[32:64] = 0.0
+    x[64 + 5] = np.nan
+    x[96 + 31] = -np.inf
+    d, q = orc.quantize_x(x)
+    assert d[1] == 0.0 and np.all(q[32:64] == 0)
+    assert np.isnan(d[2]) and np.all(q[64:96] == 0)
+    assert np.isnan(d[3]) and np.all(q[96:] == 0)
+    assert d[0] == np.float32(1.0) / np.float32(127.0) and np.all(q[:32] == 127)
+
+
+def _dense_i8x(w, x, orc_quant):
+    d, q = orc_quant
+    xd = np.repeat(d.astype(np.float64), 32) * q.astype(np.float64)
+    return dense_dequant(w, x.size) @ xd
+
+
+def pin_q8x_bruteforce_dense(orc):
+    """The int8-activation product against numpy: the dequantised weights
+    times the dequantised activations, in binary64."""
+    for p, n, seed in [(5, 64, 1), (7, 96, 2), (3, 256, 3)]:
+        w, x = rich_case(p, n, seed)
+        y, _ = orc.matvec_i8x(w, x)
+        want = _dense_i8x(w, x, orc.quantize_x(x))
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-300), (p, n)
+
+
+def pin_q8x_exact_on_grid(orc):
+    """When x already sits on its quantisation grid (d = 2^-k, integer codes,
+    one code of each block at 127) the quantisation is exact and the product
+    equals the f32-activation oracle's."""
+    rng = np.random.default_rng(5)
+    p, n = 9, 128
+    w, _ = rich_case(p, n, 5)
+    codes = rng.integers(-127, 128, size=n)
+    codes[::32] = 127
+    expo = rng.integers(-9, -2, size=n // 32)
+    x = (codes * np.repeat(2.0 ** expo, 32)).astype(np.float32)
+    y, _ = orc.matvec_i8x(w, x)
+    ref, _ = orc.matvec(w, x)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-300)
+
+
+def pin_q8x_quantization_bound(orc):
+    """|y_int8x - y_exact| <= sum_b |scale| * d/2 * sum_j |q_w|: the error
+    quantising x may add, with y_exact from the f32-activation oracle."""
+    for seed in (11, 12):
+        w, x = rich_case(40, 512, seed)
+        d, _ = orc.quantize_x(x)
+        y, _ = orc.matvec_i8x(w, x)
+        ref, _ = orc.matvec(w, x)
+        blk = np.ascontiguousarray(w).reshape(40, 16, 34)
+        scale = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2")[..., 0].astype(np.float64)
+        qabs = np.abs(np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).astype(np.float64)).sum(axis=2)
+        bound = (np.abs(scale) * (d.astype(np.float64) / 2)[None, :] * qabs).sum(axis=1)
+        assert np.all(np.abs(y - ref) <= bound * (1 + 1e-9) + 1e-12)
+
+
+def pin_q8x_tolerance_hand_case(orc):
+    """One block by hand: scale 1, weight codes 1 and -2, activation codes
+    127 and 127 (x = 1 and 1), so y = d*(127 - 254), tolerance
+    1e-4 * d * 381 + 1e-6 with d = 1/127 in binary32."""
+    w = make_blocks(np.array([[0x3C00]]), np.array([[[1, -2] + [0] * 30]]))
+    x = np.zeros(32, dtype=np.float32)
+    x[0] = x[1] = 1.0
+    y, tol = orc.matvec_i8x(w, x)
+    d = float(np.float32(1.0) / np.float32(127.0))
+    assert y[0] == d * (127 - 254)
+    assert abs(tol[0] - (1e-4 * d * 381 + 1e-6)) <= 1e-18
+
+
 ALL_PINS = [
     pin_f16_golden,
     pin_f16_exhaustive,
@@ -304,4 +425,11 @@ ALL_PINS = [
     pin_tolerance_hand_case,
     pin_argmax_page_tie,
     pin_argmax_rules,
+    pin_q8x_quantize_golden,
+    pin_q8x_quantize_properties,
+    pin_q8x_quantize_special,
+    pin_q8x_bruteforce_dense,
+    pin_q8x_exact_on_grid,
+    pin_q8x_quantization_bound,
+    pin_q8x_tolerance_hand_case,
 ]

@@ -49,6 +49,21 @@ MUTANTS = [
      "if (isnan(v[i])) continue;", ""),
     ("argmax never updates the best value",
      "bv = v[i];", ""),
+    ("activation codes truncated",
+     "rintf(xb[j] * inv)", "truncf(xb[j] * inv)"),
+    ("activation codes rounded half away from zero",
+     "rintf(xb[j] * inv)", "roundf(xb[j] * inv)"),
+    ("activation step amax / 128",
+     "amax / 127.0f", "amax / 128.0f"),
+    ("non-finite activations quantised",
+     "if (!isfinite(a)) bad = 1;\n      else if (a > amax) amax = a;",
+     "if (a > amax) amax = a;"),
+    ("activation step dropped from the product",
+     " * (double)d[b];", ";"),
+    ("activation codes read unsigned",
+     "(int64_t)q[32 * b + j]", "(int64_t)(uint8_t)q[32 * b + j]"),
+    ("int8-activation tolerance uses signed products",
+     "iabs += prod < 0 ? -prod : prod;", "iabs += prod;"),
 ]
 
 
