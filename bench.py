@@ -391,6 +391,29 @@ def main() -> int:
             "GBps": round(lyb / lt2 / 1e9, 1),
         }
 
+        log("int8-activation step (persistent graph, x quantised per 32-block)")
+        pi8 = [q8.StepGraph(s.descs, 1, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X)
+               for s in sets]
+        isec, _ = time_graph_steps(torch, pi8, host, steps2, 3, poll=True)
+        ik = event_time(torch, lambda k: pi8[k % 2].launch_kernel(), steps2)
+        extra["i8x_step"] = {
+            "step_latency_us": round(isec * 1e6, 2),
+            "GBps": round(step_bytes / isec / 1e9, 1),
+            "kernel_avg_us": round(ik * 1e6, 2),
+            "kernel_GBps": round(step_bytes / ik / 1e9, 1),
+            "note": "int8 activations: a separate operation with its own bound, "
+                    "not the headline",
+        }
+        for g in pi8:
+            g.close()
+        li = event_time(torch, lambda k: q8.q8_matvec_argmax_i8x(
+            lm_w[k % 4], lm_x, lm_idx, 151936), 40)
+        extra["lm_head_fused_i8x"] = {
+            "avg_us": round(li * 1e6, 2),
+            "GBps": round(lb / li / 1e9, 1),
+            "pct_of_peak": round(100 * lb / li / 1e9 / HBM_PEAK_GBS, 2),
+        }
+
         log("batched m=8 step (persistent graph)")
         sets8 = [StepSet(torch, dev, 0, 5000 + 1000 * j, 8, False, weights=s.w)
                  for j, s in enumerate(sets)]

@@ -115,6 +115,31 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
                      int32_t *idx, int32_t m, int32_t n, int32_t p,
                      void *stream);
 
+/* ---- int8-activation variant ----------------------------------------------- */
+
+/* The CPU's sdot form (inferno.rs "IV.4", the prose after the q8_matvec
+ * listing in "Eight kernels", and "The correctness ladder": activations
+ * quantised to int8, integer products).  Each row of x is quantised per
+ * block of 32 in binary32 by the Q8_0 rule: amax = max |x_j|, d = amax/127,
+ * q_j = x_j * (1/d) rounded to nearest, ties to even; d = 0 gives q = 0; a
+ * block holding a NaN or an infinity gets d = NaN and q = 0.  Then
+ *   y[i][r] = sum_b scale(r,b) * d(i,b) * sum_j q(r,b,j) * q_x(i,b,j)
+ * with exact integer block sums and binary32 scaling and accumulation.  The
+ * result differs from q8_matvec by the quantisation of x, at most
+ * sum_b |scale| * d/2 * sum_j |q| per output; it is a separate operation
+ * with its own bound, never a replacement for q8_matvec.
+ * Widths: n a multiple of 256 with n <= 3072 (n == 0 writes zeros); other
+ * widths give Q8_ERR_SHAPE.  1 <= m <= Q8_MAX_M; layouts, alignment,
+ * ownership and errors as q8_matvec_batched. */
+int q8_matvec_i8x(const void *w, const float *x, float *y, int32_t m, int32_t n,
+                  int32_t p, void *stream);
+
+/* q8_matvec_i8x followed by the argmax of each output row (as
+ * q8_matvec_argmax: ties to the lowest index, NaN skipped). */
+int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
+                         int32_t *idx, int32_t m, int32_t n, int32_t p,
+                         void *stream);
+
 /* ---- decode step graph --------------------------------------------------- */
 
 /* One matvec of a step.  x is [m][n], y is [m][p]; idx != NULL asks for the
@@ -136,9 +161,13 @@ typedef struct q8_step_graph q8_step_graph;
  *    buffer).
  *  Q8_GRAPH_PERSISTENT: one kernel node that walks a device-side table of
  *    all descriptors with no ordering between them (valid when no
- *    descriptor reads another's output). */
+ *    descriptor reads another's output).
+ *  Q8_GRAPH_PERSISTENT_I8X: as Q8_GRAPH_PERSISTENT, every matvec computed
+ *    as q8_matvec_i8x (every width must be one it takes, else
+ *    Q8_ERR_SHAPE). */
 #define Q8_GRAPH_CHAIN 0
 #define Q8_GRAPH_PERSISTENT 1
+#define Q8_GRAPH_PERSISTENT_I8X 2
 
 /* Records the descriptors (1 <= count <= Q8_MAX_DESCS, at most
  * Q8_MAX_ARGMAX_DESCS with idx) for m activation rows into an instantiated
@@ -160,7 +189,7 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
 /* Enqueues the whole step with one hipGraphLaunch on `stream`. */
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
-/* Q8_GRAPH_PERSISTENT only: enqueues the same recorded step (its one
+/* Persistent modes only: enqueues the same recorded step (its one
  * kernel, with the arguments fixed at build time) with a single kernel
  * launch instead of hipGraphLaunch: the same work, results and host_idx
  * writes.  Runs on the graph's device whatever device is current; `stream`

@@ -21,6 +21,7 @@ Q8_MAX_M = 8
 Q8_MAX_N = 65536
 Q8_GRAPH_CHAIN = 0
 Q8_GRAPH_PERSISTENT = 1
+Q8_GRAPH_PERSISTENT_I8X = 2
 BLOCK = 32
 BLOCK_BYTES = 34
 
@@ -64,6 +65,8 @@ def load(path: str = LIB_PATH):
         "q8_matvec_batched": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         "q8_argmax": (ctypes.c_int, [vp, i32, i32, vp, vp]),
         "q8_matvec_argmax": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
+        "q8_matvec_i8x": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
+        "q8_matvec_argmax_i8x": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
         "q8_step_graph_build": (ctypes.c_int, [ctypes.POINTER(MatvecDesc), i32,
                                                i32, vp, i32, vp,
                                                ctypes.POINTER(vp)]),
@@ -203,6 +206,40 @@ def q8_matvec_argmax(w, x, idx, p: int, y=None, stream=None) -> None:
     _check_w(w, n, p, x.device)
     _check(load().q8_matvec_argmax(_ptr(w), _ptr(x2), _ptr(y), _ptr(idx),
                                    m, n, p, _stream(stream, x.device)))
+
+
+def q8_matvec_i8x(w, x, y, stream=None) -> None:
+    """y[m, p] = x[m, n] W^T with x quantised per 32-block to int8 (the
+    int8-activation variant; n a multiple of 256, n <= 3072)."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y", x.device)
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    m, n = x2.shape
+    p = y.numel() // m if m else 0
+    if y.numel() != m * p:
+        raise ValueError("y must be [m, p]")
+    _check_w(w, n, p, x.device)
+    _check(load().q8_matvec_i8x(_ptr(w), _ptr(x2), _ptr(y), m, n, p,
+                                _stream(stream, x.device)))
+
+
+def q8_matvec_argmax_i8x(w, x, idx, p: int, y=None, stream=None) -> None:
+    """q8_matvec_i8x with the argmax of each row; y [m, p] optional."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    _need(idx, torch.int32, "idx", x.device)
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    m, n = x2.shape
+    if idx.numel() != m:
+        raise ValueError("idx must hold one int32 per row")
+    if y is not None:
+        _need(y, torch.float32, "y", x.device)
+        if y.numel() != m * p:
+            raise ValueError("y must hold m * p floats")
+    _check_w(w, n, p, x.device)
+    _check(load().q8_matvec_argmax_i8x(_ptr(w), _ptr(x2), _ptr(y), _ptr(idx),
+                                       m, n, p, _stream(stream, x.device)))
 
 
 class StepGraph:

@@ -129,6 +129,7 @@ struct q8_step_graph {
   int32_t count, m, group_size, grid;
   size_t lds;
   bool all_staged;
+  bool i8x;
 };
 
 namespace {
@@ -179,9 +180,10 @@ namespace q8 {
 // workgroups with contiguous tile ranges of about equal weight bytes, and
 // for every argmax descriptor the arrivals each argmax team waits for.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan) {
+              int group_size, StepPlan &plan, bool i8x) {
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
+  plan.i8x = i8x;
   int64_t tiles = 0;
   size_t widest = 0;
   for (int32_t i = 0; i < count; i++) {
@@ -194,18 +196,19 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     t.idx = d.idx;
     t.n = d.n;
     t.p = d.p;
-    t.rows_per_tile = step_rows_per_tile(d.n, m);
+    t.rows_per_tile = step_rows_per_tile(d.n, m, i8x);
     t.tile_begin = (int32_t)tiles;
     tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
     if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
-    const size_t l = step_lds_bytes(m, d.n);
+    const size_t l = step_lds_bytes(m, d.n, i8x);
     if (l > widest) widest = l;
-    plan.all_staged = plan.all_staged && step_all_staged(m, d.n);
+    plan.all_staged = plan.all_staged && step_all_staged(m, d.n, i8x);
   }
   if (tiles < 1) return Q8_ERR_SHAPE;  // nothing to run
   const int32_t ntiles = (int32_t)tiles;
   plan.lds = widest;
-  int grid = step_grid(dev, m, plan.lds, plan.all_staged);
+  if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;
+  int grid = step_grid(dev, m, plan.lds, plan.all_staged, i8x);
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
   if (group_size < 1) group_size = 1;
@@ -348,6 +351,31 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
+int q8_matvec_i8x(const void *w, const float *x, float *y, int32_t m, int32_t n,
+                  int32_t p, void *stream) {
+  int st = check_matvec(w, x, y, nullptr, m, n, p, true);
+  if (st) return st;
+  if (n > 0 && !q8::i8x_shape_ok(n)) return Q8_ERR_SHAPE;
+  if ((st = ensure_device(nullptr))) return st;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, m, n, p, nullptr,
+                                   nullptr, (hipStream_t)stream, n > 0);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
+                         int32_t *idx, int32_t m, int32_t n, int32_t p,
+                         void *stream) {
+  if (!idx) return Q8_ERR_NULL;
+  int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
+  if (st) return st;
+  if (n > 0 && !q8::i8x_shape_ok(n)) return Q8_ERR_SHAPE;
+  int dev = 0;
+  if ((st = ensure_device(&dev))) return st;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
+                                   g_dev[dev].slot, idx, (hipStream_t)stream, n > 0);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
 int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                         int32_t *host_idx, int32_t mode, void *stream,
                         q8_step_graph **out) {
@@ -355,13 +383,18 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   if (!out || !descs) return Q8_ERR_NULL;
   *out = nullptr;
   if (count < 1 || count > Q8_MAX_DESCS) return Q8_ERR_COUNT;
-  if (mode != Q8_GRAPH_CHAIN && mode != Q8_GRAPH_PERSISTENT) return Q8_ERR_MODE;
+  if (mode != Q8_GRAPH_CHAIN && mode != Q8_GRAPH_PERSISTENT &&
+      mode != Q8_GRAPH_PERSISTENT_I8X)
+    return Q8_ERR_MODE;
   if (m < 1 || m > Q8_MAX_M) return Q8_ERR_SHAPE;
+  const bool i8x = mode == Q8_GRAPH_PERSISTENT_I8X;
+  const bool persistent = mode != Q8_GRAPH_CHAIN;
   int nargmax = 0;
   for (int32_t i = 0; i < count; i++) {
     const q8_matvec_desc &d = descs[i];
     int st = check_matvec(d.w, d.x, d.y, d.idx, m, d.n, d.p, d.idx == nullptr);
     if (st) return st;
+    if (i8x && !q8::i8x_shape_ok(d.n)) return Q8_ERR_SHAPE;
     if (d.idx) nargmax++;
   }
   if (nargmax > Q8_MAX_ARGMAX_DESCS) return Q8_ERR_COUNT;
@@ -386,9 +419,9 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   // the device copies of the descriptor table and the workgroup ranges
   const size_t slot_bytes = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
   q8::StepPlan plan;
-  if (mode == Q8_GRAPH_PERSISTENT) {
+  if (persistent) {
     st = q8::plan_step(descs, count, m, dev,
-                       m == 1 ? q8::kStepGroupSize : q8::kStepGroupSizeBatched, plan);
+                       m == 1 ? q8::kStepGroupSize : q8::kStepGroupSizeBatched, plan, i8x);
     if (st) {
       release_graph(g);
       return st;
@@ -415,7 +448,7 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
     std::memset(hs.data(), 0, hs.size() * sizeof(q8::ArgmaxSlot));
     for (int a = 0; a < nargmax; a++)
       hs[a].host = host_dev ? host_dev + (size_t)a * m : nullptr;
-    if (mode == Q8_GRAPH_PERSISTENT) {
+    if (persistent) {
       int a = 0;
       for (auto &t : plan.descs) {
         if (!t.idx) continue;
@@ -458,7 +491,8 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
       }
     } else {
       le = q8::launch_step(table, count, groups, plan.group_size, m, plan.grid,
-                           plan.lds, plan.all_staged, cs);
+                           plan.lds, plan.all_staged, cs, i8x);
+      g->i8x = i8x;
       g->table = table;
       g->groups = groups;
       g->count = count;
@@ -505,13 +539,13 @@ int q8_step_graph_launch(q8_step_graph *g, void *stream) {
 
 int q8_step_graph_launch_kernel(q8_step_graph *g, void *stream) {
   if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
-  if (g->mode != Q8_GRAPH_PERSISTENT) return Q8_ERR_MODE;
+  if (g->mode == Q8_GRAPH_CHAIN) return Q8_ERR_MODE;
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e);
   if (cur != g->device && (e = hipSetDevice(g->device)) != hipSuccess) return hip_fail(e);
   e = q8::launch_step(g->table, g->count, g->groups, g->group_size, g->m, g->grid,
-                      g->lds, g->all_staged, (hipStream_t)stream);
+                      g->lds, g->all_staged, (hipStream_t)stream, g->i8x);
   if (cur != g->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }

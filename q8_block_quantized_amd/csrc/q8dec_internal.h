@@ -66,10 +66,15 @@ struct WgGroup {
 };
 
 // Launches y = W x (m rows) with an optional fused argmax.  slot/idx are
-// both NULL for a plain matvec.  y may be NULL only when idx is set.
+// both NULL for a plain matvec.  y may be NULL only when idx is set.  i8x:
+// the int8-activation variant (x quantised per 32-block; i8x_shape_ok(n)).
 hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
                          int n, int p, ArgmaxSlot *slot, int32_t *idx,
-                         hipStream_t s);
+                         hipStream_t s, bool i8x = false);
+
+// Widths the int8-activation variant takes: the staged ones (n/32 a
+// multiple of 8, n <= 3072).
+bool i8x_shape_ok(int n);
 
 // Launches idx[i] = argmax(logits[i][:p]) for i < m.
 hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
@@ -81,20 +86,20 @@ hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
 // LDS: step_lds_bytes of the widest matvec.
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
-                       bool all_staged, hipStream_t s);
+                       bool all_staged, hipStream_t s, bool i8x = false);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
-bool step_all_staged(int m, int n);
+bool step_all_staged(int m, int n, bool i8x = false);
 
 // Rows per tile the persistent step uses for a matvec of width n, m rows.
-int step_rows_per_tile(int n, int m);
+int step_rows_per_tile(int n, int m, bool i8x = false);
 
 // Dynamic LDS the step needs for a matvec of width n with m rows.
-size_t step_lds_bytes(int m, int n);
+size_t step_lds_bytes(int m, int n, bool i8x = false);
 
 // Workgroups of the step kernel resident at once on `device` (the grid).
-int step_grid(int device, int m, size_t lds, bool all_staged);
+int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x = false);
 
 // Everything a persistent step launch needs, worked out on the host.
 struct StepPlan {
@@ -105,6 +110,7 @@ struct StepPlan {
   int grid = 0;
   int group_size = 1;
   bool all_staged = true;
+  bool i8x = false;
 };
 
 // Workgroups per group of the persistent step.  m = 1: groups of 32
@@ -124,5 +130,5 @@ struct q8_matvec_desc;
 namespace q8 {
 // Plans a persistent step (q8dec_api.hip) with groups of `group_size`.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan);
+              int group_size, StepPlan &plan, bool i8x = false);
 }  // namespace q8

@@ -338,6 +338,8 @@ constexpr int kMfmaRowPad = 16;
 constexpr int kMfmaTileBytes = 53248;  // LDS of a batched tile, pads included
 constexpr int kMfmaChunks = (kMfmaTileBytes + 16 * kWG - 1) / (16 * kWG);
 constexpr int kMfmaMaxBlocks = kMaxLdsBlocks / kWaves;  // x blocks per wave
+constexpr int kMaxM = 8;  // activation rows per launch (the ABI's limit)
+constexpr int kI8xMaxBlocks = kMaxM * kMaxLdsBlocks;  // int8-activation steps
 constexpr int kRedStride = 80;  // floats between a wave's partial-sum entries
 constexpr int kRedFloats = 2 * kWaves * 4 * kRedStride;  // two sets per wave
 
@@ -604,6 +606,162 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
   }
 }
 
+// ---- int8-activation variant -----------------------------------------------
+//
+// The CPU's sdot kernel quantises the activations and multiplies integers
+// (inferno.rs "IV.4: One command buffer per token", the prose after the
+// q8_matvec listing in "Eight kernels", and "The correctness ladder").  Here
+// x is quantised per 32-value block by the Q8_0 rule, in binary32: amax =
+// max |x_j|, d = amax / 127, q_j = x_j * (1/d) rounded to nearest even; a
+// block holding a NaN or an infinity gets d = NaN and zero codes.  Each
+// block's product is then an exact integer sum of eight v_dot4_i32_i8, and
+// only scale * d * sum is floating point.
+
+// Codes of four consecutive x values (packed int8, lowest byte first) and
+// the block's step d.  The 32 values of a block sit in 8 consecutive lanes
+// (aligned to 8), which exchange their maxima with DPP.
+__device__ __forceinline__ float q8x_chunk(const f32x4 v, uint32_t &codes) {
+  float a = 0.f;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const float t = fabsf(v[k]);
+    bad = bad || !(t <= 3.402823466e38f);  // NaN or infinity
+    a = fmaxf(a, t);
+  }
+  float e = bad ? __builtin_inff() : a;
+  e = fmaxf(e, dpp_shift<0xB1, 0xF>(e));   // quad_perm [1,0,3,2]
+  e = fmaxf(e, dpp_shift<0x4E, 0xF>(e));   // quad_perm [2,3,0,1]
+  e = fmaxf(e, dpp_shift<0x141, 0xF>(e));  // row_half_mirror: 8 lanes
+  const bool block_bad = e == __builtin_inff();
+  const float d = block_bad ? __builtin_nanf("") : e / 127.0f;
+  const float inv = (block_bad || d == 0.f) ? 0.f : 1.0f / d;
+  codes = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int32_t q = block_bad ? 0 : (int32_t)rintf(v[k] * inv);
+    codes |= ((uint32_t)q & 0xFFu) << (8 * k);
+  }
+  return d;
+}
+
+// m rows of x ([m][n] f32 in global memory) quantised into LDS: xq (packed
+// codes, row i block b at dword 8 (i * n/32 + b)) and xd (the steps, block
+// i * n/32 + b).  Loaded directly (the batched form, once per matvec).
+template <int NT>
+__device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
+                               uint32_t *xq, float *xd) {
+  const int32_t chunks = (m * n) >> 2;  // a multiple of 8: no block is split
+  for (int32_t c0 = 0; c0 < chunks; c0 += NT) {
+    const int32_t c = c0 + (int32_t)threadIdx.x;
+    const f32x4 v = gp((const f32x4 *)x)[c < chunks ? c : chunks - 1];
+    uint32_t codes;
+    const float d = q8x_chunk(v, codes);
+    if (c < chunks) {
+      xq[c] = codes;
+      if ((c & 7) == 0) xd[c >> 3] = d;
+    }
+  }
+}
+
+// Rows [0, rows) of a staged tile against int8 activations, m = 1: as
+// staged_m1, with the block product an integer dot.
+template <int NBL>
+__device__ __forceinline__ void staged_m1_i8(const uint32_t *tl, int32_t bpr,
+                                             int32_t rows, const uint32_t *xq,
+                                             const float *xd, float *y, int32_t r0,
+                                             bool keys, unsigned long long &best) {
+  const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int32_t pitch = bpr * 34;
+  for (int32_t rr0 = 2 * wave; rr0 < rows; rr0 += kRowsPerPass) {
+    const int32_t rr = rr0 + half;
+    const int32_t rc = rr < rows ? rr : rows - 1;
+    float acc = 0.f;
+    // keeps each pass's LDS reads inside the pass (four workgroups per CU
+    // need the kernel within 128 registers)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NBL; i++) {
+      const int32_t b = min(k + 32 * i, bpr - 1);
+      const int32_t o = rc * pitch + 34 * b;
+      const uint32_t *wp = tl + (o >> 2);
+      uint32_t d[9];
+#pragma unroll
+      for (int q = 0; q < 9; q++) d[q] = wp[q];
+      const uint32_t amod = (uint32_t)o & 2u, sel = quant_sel(amod);
+      const uint32_t *xc = xq + 8 * b;
+      int32_t isum = 0;
+#pragma unroll
+      for (int t = 0; t < 8; t++)
+        isum = __builtin_amdgcn_sdot4((int)__builtin_amdgcn_perm(d[t + 1], d[t], sel),
+                                      (int)xc[t], isum, false);
+      const float v = (float)isum * (scale_of(d, amod) * xd[b]);
+      acc += (k + 32 * i < bpr) ? v : 0.f;
+    }
+    acc = half_wave_sum(acc);
+    if (k == 31 && rr < rows) {
+      if (y) gpw(y)[r0 + rr] = acc;
+      if (keys) best = umax64(best, argmax_key(acc, (uint32_t)(r0 + rr)));
+    }
+  }
+}
+
+// Same for 1 < m <= 8: each block's quant dwords are realigned once and
+// dotted with m rows of codes.
+template <int NBL>
+__device__ __forceinline__ void staged_mb_i8(const uint32_t *tl, int32_t bpr,
+                                             int32_t rows, int32_t m, int32_t p,
+                                             const uint32_t *xq, const float *xd,
+                                             float *y, int32_t r0, bool keys,
+                                             unsigned long long *best) {
+  const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int32_t pitch = bpr * 34;
+  for (int32_t rr0 = 2 * wave; rr0 < rows; rr0 += kRowsPerPass) {
+    const int32_t rr = rr0 + half;
+    const int32_t rc = rr < rows ? rr : rows - 1;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBL; i++) {
+      const int32_t b = min(k + 32 * i, bpr - 1);
+      const int32_t o = rc * pitch + 34 * b;
+      const uint32_t *wp = tl + (o >> 2);
+      uint32_t d[9];
+#pragma unroll
+      for (int q = 0; q < 9; q++) d[q] = wp[q];
+      const uint32_t amod = (uint32_t)o & 2u, sel = quant_sel(amod);
+      uint32_t qw[8];
+#pragma unroll
+      for (int t = 0; t < 8; t++) qw[t] = __builtin_amdgcn_perm(d[t + 1], d[t], sel);
+      const bool live = k + 32 * i < bpr;
+      const float s = scale_of(d, amod);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if (j < m) {
+          const uint32_t *xc = xq + 8 * (j * bpr + b);
+          int32_t isum = 0;
+#pragma unroll
+          for (int t = 0; t < 8; t++)
+            isum = __builtin_amdgcn_sdot4((int)qw[t], (int)xc[t], isum, false);
+          const float v = fmaf((float)isum, s * xd[j * bpr + b], acc[j]);
+          acc[j] = live ? v : acc[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      if (j < m) {
+        const float v = half_wave_sum(acc[j]);
+        if (k == 31 && rr < rows) {
+          if (y) gpw(y)[(int64_t)j * p + r0 + rr] = v;
+          if (keys) best[j] = umax64(best[j], argmax_key(v, (uint32_t)(r0 + rr)));
+        }
+      }
+    }
+  }
+}
+
 // ---- batched path: matrix cores -----------------------------------------------
 //
 // For 1 < m <= 8 a 16-row group of a staged tile against one block is one
@@ -820,6 +978,26 @@ struct Prefetch {
       }
     }
   }
+  // Quantised into LDS (int8-activation variant): packed codes xq and steps
+  // xd, laid out as quantize_x_lds does.  Chunks of one block sit in 8
+  // consecutive lanes, and chunk counts are multiples of 8, so every lane
+  // of a block takes part in its DPP maximum.
+  __device__ __forceinline__ void store_xq(uint32_t *xq, float *xd, int32_t m,
+                                           int32_t n) const {
+    const int32_t chunks = (m * n) >> 2;
+#pragma unroll
+    for (int j = 0; j < XC; j++) {
+      if (j * kWG < chunks) {
+        const int32_t c = j * kWG + (int32_t)threadIdx.x;
+        uint32_t codes;
+        const float d = q8x_chunk(x[j], codes);
+        if (c < chunks) {
+          xq[c] = codes;
+          if ((c & 7) == 0) xd[c >> 3] = d;
+        }
+      }
+    }
+  }
   // Into the padded LDS layout: row i, block b at i*36*bpr + 36*b.
   __device__ __forceinline__ void store_x(float *xs, int32_t m, int32_t n) const {
     const int32_t chunks = (m * n) >> 2, row_chunks = n >> 2;
@@ -888,18 +1066,23 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
 // adds its argmax keys, if any, as one arrival.  M1: the launch has m = 1;
 // ANY: some matvec of the launch takes the direct or generic path.
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
-template <bool M1, bool ANY, class Src>
+template <bool M1, bool ANY, bool I8X, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds) {
+  static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
-  constexpr int CH = M1 ? kStageChunks : kMfmaChunks;
+  constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
   uint32_t *tl = (uint32_t *)lds;
-  float *red = lds + (M1 ? kTileMaxBytes : kMfmaTileBytes) / 4;
+  float *red = lds + ((M1 || I8X) ? kTileMaxBytes : kMfmaTileBytes) / 4;
   float *xs = M1 ? red : red + kRedFloats;
+  // int8 activations: the steps, then the packed codes, after the tile
+  float *xd = red;
+  uint32_t *xq = (uint32_t *)(red + kI8xMaxBlocks);
   // which path a tile takes; without ANY every tile takes the staged one
-  auto staged = [&](const Job &j) { return M1 && (!ANY || j.path == kStaged); };
-  auto mfma = [&](const Job &j) { return !M1 && (!ANY || j.path == kMfma); };
+  auto staged = [&](const Job &j) { return I8X || (M1 && (!ANY || j.path == kStaged)); };
+  auto mfma = [&](const Job &j) { return !I8X && !M1 && (!ANY || j.path == kMfma); };
+  // x prefetched into registers and staged in LDS with the tile
   auto x_in_lds = [&](const Job &j) {
     return M1 ? (!ANY || j.path != kGeneric) : (ANY && j.path == kDirect);
   };
@@ -933,7 +1116,14 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     __syncthreads();  // the previous tile's readers of LDS are done
     if (staged(cur)) pf.store_w(tl, cur.rows * bpr * 34);
     else if (mfma(cur)) pf.store_w_rows(tl, cur.rows * bpr * 34, bpr * 34);
-    if (new_x) pf.store_x(xs, m, cur.d.n);
+    if (new_x) {
+      if (I8X) pf.store_xq(xq, xd, m, cur.d.n);
+      else pf.store_x(xs, m, cur.d.n);
+    }
+    if (I8X && !M1 && cur.desc != xdesc) {  // batched: quantised straight from memory
+      quantize_x_lds<kWG>(cur.d.x, m, cur.d.n, xq, xd);
+      xdesc = cur.desc;
+    }
     __syncthreads();
     if (new_x) xdesc = cur.desc;
     // a new matvec's operand A is loaded before the next tile's bytes are
@@ -952,7 +1142,18 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         pf.load_x(nxt.d.x, m * nxt.d.n);
     }
     const bool keys = cur.d.idx != nullptr;
-    if (staged(cur)) {
+    if (I8X) {
+      const int nbl = nbl_of(cur.d.n);
+      if (M1) {
+        if (nbl == 1) staged_m1_i8<1>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
+        else if (nbl == 2) staged_m1_i8<2>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
+        else staged_m1_i8<3>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
+      } else {
+        if (nbl == 1) staged_mb_i8<1>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
+        else if (nbl == 2) staged_mb_i8<2>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
+        else staged_mb_i8<3>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
+      }
+    } else if (staged(cur)) {
       const int nbl = nbl_of(cur.d.n);
       if (nbl == 1) staged_m1<1>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
       else if (nbl == 2) staged_m1<2>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
@@ -1021,26 +1222,26 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
 // One matvec (descriptor passed by value), its tiles round-robin over the
 // grid (gridDim.x <= tiles, so every workgroup arrives at the argmax): at
 // any moment the grid streams one contiguous window of the weights.
-template <bool M1, bool ANY>
-__global__ void __launch_bounds__(kWG, M1 ? Q8_MIN_WGS_PER_CU : 2)
+template <bool M1, bool ANY, bool I8X>
+__global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
-  run_tiles<M1, ANY>(src, blockIdx.x, tiles_of(d), gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X>(src, blockIdx.x, tiles_of(d), gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
 // (count entries in tile order), with no ordering between descriptors.
 // Workgroups form groups; a group interleaves its contiguous tile range.
-template <bool M1, bool ANY>
-__global__ void __launch_bounds__(kWG, M1 ? Q8_MIN_WGS_PER_CU : 2)
+template <bool M1, bool ANY, bool I8X>
+__global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
+  run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
 }
 
 // ---- argmax over f32 logits ---------------------------------------------
@@ -1063,6 +1264,11 @@ argmax_rows(const float *__restrict__ logits, int32_t m, int32_t p,
 // ---- host side ---------------------------------------------------------------
 
 // Dynamic LDS of a launch whose matvecs have widths up to n_max.
+// int8 activations: tile, steps, packed codes (m * n bytes).
+size_t lds_bytes_i8x(int m, int n) {
+  return kTileMaxBytes + (size_t)kI8xMaxBlocks * 4 + (size_t)m * n;
+}
+
 size_t lds_bytes_for(int m, int n) {
   const int path = path_of(m, n);
   if (m == 1) {  // the x region starts after the tile region
@@ -1098,30 +1304,31 @@ int resident_wgs(K kernel, size_t lds, int dev) {
 
 // Occupancy-limited grid of a single-matvec kernel variant, cached per
 // device, for the largest LDS a launch of that variant can ask for.
-template <bool M1, bool ANY>
+template <bool M1, bool ANY, bool I8X>
 int mv_grid_cap(int dev) {
   static int cache[64] = {0};
   int &c = cache[dev & 63];
   if (!c) {
-    const size_t lds = M1 ? kTileMaxBytes + (size_t)kMaxLdsBlocks * 36 * 4
-                          : kMfmaTileBytes + (size_t)kRedFloats * 4 +
-                                (ANY ? (size_t)kXMaxFloats / 32 * 36 * 4 : 0);
-    c = resident_wgs(mv_kernel<M1, ANY>, lds, dev);
+    const size_t lds = I8X ? lds_bytes_i8x(M1 ? 1 : kMaxM, kMaxLdsBlocks * 32)
+                       : M1 ? kTileMaxBytes + (size_t)kMaxLdsBlocks * 36 * 4
+                            : kMfmaTileBytes + (size_t)kRedFloats * 4 +
+                                  (ANY ? (size_t)kXMaxFloats / 32 * 36 * 4 : 0);
+    c = resident_wgs(mv_kernel<M1, ANY, I8X>, lds, dev);
   }
   return c;
 }
 
-template <bool M1, bool ANY>
+template <bool M1, bool ANY, bool I8X>
 hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  const int cap = mv_grid_cap<M1, ANY>(dev);
+  const int cap = mv_grid_cap<M1, ANY, I8X>(dev);
   // Every workgroup takes whole rounds of tiles, so the last round may be
   // part-empty.  Among tile heights from the largest down to three quarters
   // of it, take the one whose busiest workgroup costs least, counting a
   // tile as its rows plus four rows' worth of fixed work (barriers, LDS
   // staging).  Batched tiles stay whole 16-row groups.
-  if (path_of(m, d.n) != kMfma && tiles_of(d) > cap) {
+  if ((I8X || path_of(m, d.n) != kMfma) && tiles_of(d) > cap) {
     int32_t best_rows = d.rows_per_tile;
     int64_t best_cost = INT64_MAX;
     for (int32_t r = d.rows_per_tile; r >= (3 * d.rows_per_tile + 3) / 4; r--) {
@@ -1133,32 +1340,42 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   }
   const int32_t ntiles = tiles_of(d);
   const int grid = ntiles < cap ? ntiles : cap;
-  hipLaunchKernelGGL((mv_kernel<M1, ANY>), dim3(grid), dim3(kWG),
-                     lds_bytes_for(m, d.n), s, d, m);
+  hipLaunchKernelGGL((mv_kernel<M1, ANY, I8X>), dim3(grid), dim3(kWG),
+                     I8X ? lds_bytes_i8x(m, d.n) : lds_bytes_for(m, d.n), s, d, m);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int step_rows_per_tile(int n, int m) { return tile_rows_of(m, n); }
+int step_rows_per_tile(int n, int m, bool i8x) {
+  return tile_rows_of(i8x ? 1 : m, n);  // int8 activations: staged tiles for any m
+}
 
-size_t step_lds_bytes(int m, int n) { return lds_bytes_for(m, n); }
+size_t step_lds_bytes(int m, int n, bool i8x) {
+  return i8x ? lds_bytes_i8x(m, n) : lds_bytes_for(m, n);
+}
 
-bool step_all_staged(int m, int n) {
+bool step_all_staged(int m, int n, bool i8x) {
+  if (i8x) return i8x_shape_ok(n);
   return path_of(m, n) == (m == 1 ? kStaged : kMfma);
 }
 
-int step_grid(int device, int m, size_t lds, bool all_staged) {
+bool i8x_shape_ok(int n) { return path_of(1, n) == kStaged; }
+
+int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x) {
+  if (i8x)
+    return m == 1 ? resident_wgs(step_kernel<true, false, true>, lds, device)
+                  : resident_wgs(step_kernel<false, false, true>, lds, device);
   if (m == 1)
-    return all_staged ? resident_wgs(step_kernel<true, false>, lds, device)
-                      : resident_wgs(step_kernel<true, true>, lds, device);
-  return all_staged ? resident_wgs(step_kernel<false, false>, lds, device)
-                    : resident_wgs(step_kernel<false, true>, lds, device);
+    return all_staged ? resident_wgs(step_kernel<true, false, false>, lds, device)
+                      : resident_wgs(step_kernel<true, true, false>, lds, device);
+  return all_staged ? resident_wgs(step_kernel<false, false, false>, lds, device)
+                    : resident_wgs(step_kernel<false, true, false>, lds, device);
 }
 
 hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
                          int n, int p, ArgmaxSlot *slot, int32_t *idx,
-                         hipStream_t s) {
+                         hipStream_t s, bool i8x) {
   if (p <= 0) return hipSuccess;
   StepDesc d;
   d.w = w;
@@ -1169,8 +1386,8 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
   d.n = n;
   d.p = p;
   d.tile_begin = 0;
-  d.rows_per_tile = tile_rows_of(m, n);
-  const int path = path_of(m, n);
+  d.rows_per_tile = tile_rows_of(i8x ? 1 : m, n);
+  const int path = i8x ? (int)kStaged : path_of(m, n);
   // small matvecs: shorter tiles spread them over more workgroups (batched
   // tiles stay whole 16-row groups)
   if (path == kMfma) {
@@ -1181,28 +1398,41 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
            (p + d.rows_per_tile - 1) / d.rows_per_tile < 512)
       d.rows_per_tile >>= 1;
   }
+  if (i8x)
+    return m == 1 ? launch_mv<true, false, true>(d, m, s) : launch_mv<false, false, true>(d, m, s);
   const bool staged = path == kStaged || path == kMfma;
   if (m == 1)
-    return staged ? launch_mv<true, false>(d, m, s) : launch_mv<true, true>(d, m, s);
-  return staged ? launch_mv<false, false>(d, m, s) : launch_mv<false, true>(d, m, s);
+    return staged ? launch_mv<true, false, false>(d, m, s)
+                  : launch_mv<true, true, false>(d, m, s);
+  return staged ? launch_mv<false, false, false>(d, m, s)
+                : launch_mv<false, true, false>(d, m, s);
 }
 
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
-                       bool all_staged, hipStream_t s) {
-  if (m == 1) {
-    if (all_staged)
-      hipLaunchKernelGGL((step_kernel<true, false>), dim3(grid), dim3(kWG), lds,
+                       bool all_staged, hipStream_t s, bool i8x) {
+  if (i8x) {
+    if (m == 1)
+      hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,
                          s, descs, count, groups, group_size, m);
     else
-      hipLaunchKernelGGL((step_kernel<true, true>), dim3(grid), dim3(kWG), lds,
+      hipLaunchKernelGGL((step_kernel<false, false, true>), dim3(grid), dim3(kWG), lds,
+                         s, descs, count, groups, group_size, m);
+    return hipGetLastError();
+  }
+  if (m == 1) {
+    if (all_staged)
+      hipLaunchKernelGGL((step_kernel<true, false, false>), dim3(grid), dim3(kWG), lds,
+                         s, descs, count, groups, group_size, m);
+    else
+      hipLaunchKernelGGL((step_kernel<true, true, false>), dim3(grid), dim3(kWG), lds,
                          s, descs, count, groups, group_size, m);
   } else {
     if (all_staged)
-      hipLaunchKernelGGL((step_kernel<false, false>), dim3(grid), dim3(kWG), lds,
+      hipLaunchKernelGGL((step_kernel<false, false, false>), dim3(grid), dim3(kWG), lds,
                          s, descs, count, groups, group_size, m);
     else
-      hipLaunchKernelGGL((step_kernel<false, true>), dim3(grid), dim3(kWG), lds,
+      hipLaunchKernelGGL((step_kernel<false, true, false>), dim3(grid), dim3(kWG), lds,
                          s, descs, count, groups, group_size, m);
   }
   return hipGetLastError();

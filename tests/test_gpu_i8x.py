@@ -1,0 +1,209 @@
+"""GPU parity of the int8-activation variant (q8_matvec_i8x,
+q8_matvec_argmax_i8x, Q8_GRAPH_PERSISTENT_I8X) against the oracle's
+quantised product.  Both sides quantise x by the same binary32 rule, so the
+GPU is held to the f32 bar against the oracle's quantised result; separately
+it must stay within the quantisation bound of the exact-x result."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import q8_block_quantized_amd as q8
+from tests.gpu_helpers import assert_parity, cuda, say, to_dev  # noqa: F401
+from tests.oracle_pins import make_blocks, rich_case
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_i8x(w, x, device):
+    import torch
+    x2 = np.atleast_2d(x).astype(np.float32)
+    m, p = x2.shape[0], w.shape[0]
+    wd = to_dev(w.reshape(-1), device)
+    xd = to_dev(x2, device)
+    yd = torch.full((m, p), float("nan"), dtype=torch.float32, device=device)
+    q8.q8_matvec_i8x(wd, xd, yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+def quant_bound(w, x):
+    """sum_b |scale| * d_b / 2 * sum_j |q|: what quantising x may change."""
+    p = w.shape[0]
+    n = x.size
+    d, _ = oracle.quantize_x(x)
+    blk = np.ascontiguousarray(w).reshape(p, n // 32, 34)
+    scale = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2")[..., 0].astype(np.float64)
+    qabs = np.abs(np.ascontiguousarray(blk[:, :, 2:]).view(np.int8).astype(np.float64)).sum(axis=2)
+    return (np.abs(scale) * (d.astype(np.float64) / 2)[None, :] * qabs).sum(axis=1)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("p,n", [(1000, 1024), (333, 2048), (170, 3072),
+                                 (7, 256), (64, 512)])
+def test_i8x_matches_oracle(cuda, m, p, n):
+    say(f"i8x m={m} p={p} n={n}")
+    w, _ = rich_case(p, n, seed=p + n + m)
+    x = gen.activations(m, n, seed=m, index=n)
+    y = gpu_i8x(w, x, cuda)
+    ref, tol = oracle.matvec_i8x(w, x)
+    assert_parity(y, ref, tol, f"i8x m={m} p={p} n={n}")
+    for i in range(m):
+        exact, etol = oracle.matvec(w, x[i])
+        assert np.all(np.abs(y[i] - exact) <= quant_bound(w, x[i]) + etol)
+
+
+def test_i8x_lm_head_many_tiles(cuda):
+    w = gen.weights(151936, 1024, seed=0, index=196)
+    x = gen.activations(1, 1024, seed=0, index=196)
+    y = gpu_i8x(w, x, cuda)
+    ref, tol = oracle.matvec_i8x(w, x)
+    assert_parity(y, ref, tol, "i8x lm_head")
+
+
+def test_i8x_special_blocks(cuda):
+    """A zero block adds nothing; a block of x holding a NaN (or an
+    infinity) makes every output NaN, as in the oracle; subnormal scales."""
+    p, n = 40, 1024
+    rng = np.random.default_rng(8)
+    quants = rng.integers(-127, 128, size=(p, n // 32, 32))
+    sb = rng.integers(1, 0x400, size=(p, n // 32)).astype(np.uint16)
+    w = make_blocks(sb, quants)
+    x = gen.activations(2, n, seed=8, index=8)
+    x[0, 64:96] = 0.0
+    y = gpu_i8x(w, x, cuda)
+    ref, tol = oracle.matvec_i8x(w, x)
+    assert_parity(y, ref, tol, "zero block, subnormal scales")
+    x[1, 300] = np.nan
+    x[0, 900] = np.inf
+    y = gpu_i8x(w, x, cuda)
+    ref, tol = oracle.matvec_i8x(w, x)
+    assert np.all(np.isnan(y)) and np.all(np.isnan(ref))
+
+
+def test_i8x_exact_on_grid(cuda):
+    """x already on its grid (power-of-two steps, one code 127 per block):
+    quantising changes nothing and the result meets the f32 oracle's bar."""
+    rng = np.random.default_rng(9)
+    p, n = 77, 2048
+    w, _ = rich_case(p, n, seed=9)
+    codes = rng.integers(-127, 128, size=n)
+    codes[::32] = 127
+    x = (codes * np.repeat(2.0 ** rng.integers(-9, -2, size=n // 32), 32)).astype(np.float32)
+    y = gpu_i8x(w, x, cuda)[0]
+    ref, tol = oracle.matvec(w, x)
+    assert_parity(y, ref, tol, "on grid")
+
+
+def test_i8x_widths(cuda):
+    """Widths other than multiples of 256 up to 3072 are refused before any
+    GPU work; n = 0 writes zeros."""
+    import torch
+    for n in (96, 1056, 4096):
+        w, _ = rich_case(4, n, seed=1)
+        with pytest.raises(q8.Q8Error) as e:
+            gpu_i8x(w, np.ones(n, dtype=np.float32), cuda)
+        assert e.value.name == "q8_err_shape"
+    x = torch.empty((1, 0), dtype=torch.float32, device=cuda)
+    y = torch.full((1, 5), float("nan"), dtype=torch.float32, device=cuda)
+    q8.q8_matvec_i8x(torch.empty(0, dtype=torch.uint8, device=cuda), x, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0).item()
+
+
+@pytest.mark.parametrize("m,p,n", [(1, 151936, 1024), (2, 4097, 1024), (5, 999, 3072)])
+def test_i8x_fused_argmax(cuda, m, p, n):
+    import torch
+    w = gen.weights(p, n, seed=m, index=p) if p > 10000 else rich_case(p, n, seed=p)[0]
+    x = gen.activations(m, n, seed=m, index=n)
+    wd = to_dev(w.reshape(-1), cuda)
+    xd = to_dev(x, cuda)
+    idx = torch.full((m,), -5, dtype=torch.int32, device=cuda)
+    y = torch.empty((m, p), dtype=torch.float32, device=cuda)
+    q8.q8_matvec_argmax_i8x(wd, xd, idx, p, y=y)
+    torch.cuda.synchronize()
+    ref, tol = oracle.matvec_i8x(w, x)
+    yh = y.cpu().numpy()
+    assert_parity(yh, ref, tol, f"fused i8x m={m}")
+    for r in range(m):
+        g = int(idx[r])
+        assert g == oracle.argmax_f32(yh[r])
+        assert oracle.argmax_accepted(g, ref[r], tol[r])
+    idx2 = torch.full((m,), -5, dtype=torch.int32, device=cuda)
+    q8.q8_matvec_argmax_i8x(wd, xd, idx2, p)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+
+
+def _step(layers, lm_p, m, seed, device):
+    import torch
+    shapes = [(f"L{l}.{name}", n, p) for l in range(layers)
+              for name, n, p in gen.LAYER_SHAPES] + [("lm_head", 1024, lm_p)]
+    ws, xs, descs = [], [], []
+    for i, (_, n, p) in enumerate(shapes):
+        ws.append(gen.weights(p, n, seed=seed, index=i))
+        xs.append(gen.activations(m, n, seed=seed, index=i))
+        last = i == len(shapes) - 1
+        descs.append(dict(n=n, p=p, w=to_dev(ws[i].reshape(-1), device),
+                          x=to_dev(xs[i], device),
+                          y=torch.full((m, p), float("nan"), dtype=torch.float32,
+                                       device=device),
+                          idx=torch.full((m,), -7, dtype=torch.int32, device=device)
+                          if last else None))
+    return shapes, ws, xs, descs
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_i8x_step_equals_standalone(cuda, m):
+    """The int8-activation persistent step gives, bit for bit, what
+    q8_matvec_i8x gives for each descriptor, through the graph and through
+    the kernel launch, on three launches."""
+    import torch
+    shapes, ws, xs, descs = _step(2, 20000, m, 4, cuda)
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X, device=cuda)
+    assert g.info() == (1, 0)
+    want = []
+    for d in descs:
+        y = torch.empty_like(d["y"])
+        q8.q8_matvec_i8x(d["w"], d["x"], y)
+        want.append(y)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        (g.launch if k != 1 else g.launch_kernel)()
+        torch.cuda.synchronize()
+        for d, w_ in zip(descs, want):
+            assert torch.equal(d["y"], w_)
+        yl = descs[-1]["y"].cpu().numpy()
+        for r in range(m):
+            assert int(host[r]) == oracle.argmax_f32(yl[r])
+    g.close()
+
+
+def test_i8x_full_step_against_oracle(cuda):
+    """All 197 matvecs of a step with int8 activations, every output."""
+    import torch
+    shapes, ws, xs, descs = _step(28, 151936, 1, 0, cuda)
+    host = torch.full((1,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, 1, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X, device=cuda)
+    g.launch()
+    torch.cuda.synchronize()
+    for i, (name, n, p) in enumerate(shapes):
+        ref, tol = oracle.matvec_i8x(ws[i], xs[i])
+        assert_parity(descs[i]["y"].cpu().numpy(), ref, tol, name)
+    ref, tol = oracle.matvec_i8x(ws[-1], xs[-1])
+    assert oracle.argmax_accepted(int(host[0]), ref[0], tol[0])
+    g.close()
+
+
+def test_i8x_step_refuses_other_widths(cuda):
+    import torch
+    shapes, ws, xs, descs = _step(0, 64, 1, 5, cuda)
+    descs.append(dict(n=96, p=8, w=to_dev(rich_case(8, 96, 1)[0].reshape(-1), cuda),
+                      x=to_dev(np.ones((1, 96), np.float32), cuda),
+                      y=torch.empty((1, 8), dtype=torch.float32, device=cuda), idx=None))
+    with pytest.raises(q8.Q8Error) as e:
+        q8.StepGraph(descs, 1, mode=q8.Q8_GRAPH_PERSISTENT_I8X, device=cuda)
+    assert e.value.name == "q8_err_shape"
