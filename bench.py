@@ -206,6 +206,17 @@ def only_workload(args, torch, q8, dev) -> int:
                        args.steps, args.warmup)
         b = alg_bytes(1024, 151936, 1, False, True)
         out.update(avg_us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), alg_bytes=b)
+    elif args.only == "i8x_step":
+        sets1 = [StepSet(torch, dev, 0, 1000 * j, 1, False) for j in range(2)]
+        host = torch.zeros(1, dtype=torch.int32).pin_memory()
+        gs = [q8.StepGraph(s.descs, 1, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X)
+              for s in sets1]
+        sec, _ = time_graph_steps(torch, gs, host, args.steps, args.warmup, poll=True)
+        b = sets1[0].bytes
+        out.update(step_latency_us=round(sec * 1e6, 2), GBps=round(b / sec / 1e9, 1),
+                   alg_bytes=b)
+        for g in gs:
+            g.close()
     else:
         sets8 = [StepSet(torch, dev, 0, 5000 + 1000 * j, 8, False) for j in range(2)]
         host8 = torch.zeros(8, dtype=torch.int32).pin_memory()
@@ -229,10 +240,11 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--only", choices=["lm_head", "batched"], default=None,
+    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step"], default=None,
                     help="only time one other configuration (for profiling runs): "
-                         "the fused lm_head (1024 -> 151,936 + argmax, m = 1) or "
-                         "the m = 8 step; prints one JSON line")
+                         "the fused lm_head (1024 -> 151,936 + argmax, m = 1), "
+                         "the m = 8 step, or the int8-activation step; prints one "
+                         "JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
