@@ -354,6 +354,26 @@ def main() -> int:
         for g in chain:
             g.close()
 
+        log("levels graph (q|k|v, o, gate|up, down per layer: 113 nodes)")
+        lv = []
+        for l in range(28):
+            lv += [4 * l] * 3 + [4 * l + 1] + [4 * l + 2] * 2 + [4 * l + 3]
+        lv.append(4 * 28)
+        lvg = [q8.StepGraph(s.descs, 1, host_idx=host, levels=lv) for s in sets]
+        assert lvg[0].info() == (113, 0)
+        lsec, ltoks = time_graph_steps(torch, lvg, host, steps2, 3, poll=True)
+        lksec, _ = time_graph_steps(torch, [_KernelLaunch(g) for g in lvg], host,
+                                    steps2, 3, poll=True)
+        assert ltoks == toks[:len(ltoks)], "levels graph token differs"
+        extra["levels_graph_113_nodes"] = {
+            "step_latency_us": round(lsec * 1e6, 2),
+            "GBps": round(step_bytes / lsec / 1e9, 1),
+            "per_node_us": round(lsec * 1e6 / 113, 3),
+            "kernel_launches_step_latency_us": round(lksec * 1e6, 2),
+        }
+        for g in lvg:
+            g.close()
+
         log("lm_head fused (4 copies rotated)")
         lm_extra = [torch.from_numpy(gen.weights(151936, 1024, seed=0, index=2000 + c)
                                      .reshape(-1)).to(dev) for c in range(2)]

@@ -63,6 +63,7 @@ extern "C" {
 #define Q8_ERR_BAD_HANDLE 9  /* NULL, unknown or destroyed graph handle     */
 #define Q8_ERR_COUNT 10      /* descriptor count or argmax count out of range */
 #define Q8_ERR_MODE 11       /* unknown step-graph mode                     */
+#define Q8_ERR_LEVELS 12     /* step levels negative or decreasing          */
 
 /* ---- limits --------------------------------------------------------- */
 #define Q8_BLOCK 32                 /* quants per block                       */
@@ -168,6 +169,7 @@ typedef struct q8_step_graph q8_step_graph;
 #define Q8_GRAPH_CHAIN 0
 #define Q8_GRAPH_PERSISTENT 1
 #define Q8_GRAPH_PERSISTENT_I8X 2
+#define Q8_GRAPH_LEVELS 3  /* built by q8_step_graph_build_levels only */
 
 /* Records the descriptors (1 <= count <= Q8_MAX_DESCS, at most
  * Q8_MAX_ARGMAX_DESCS with idx) for m activation rows into an instantiated
@@ -186,13 +188,28 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                         int32_t *host_idx, int32_t mode, void *stream,
                         q8_step_graph **out);
 
+/* A step with dependencies between its matvecs (the in-order command buffer
+ * of inferno.rs "IV.4", "One command buffer", with the siblings that read the
+ * same input run together): levels[i] >= 0 is descriptor i's dependency
+ * level, non-decreasing over the descriptors.  Each run of equal levels
+ * becomes one persistent kernel node over those descriptors (no ordering
+ * among them), and the nodes run in level order, each after the previous
+ * one has finished.  For a decoder layer: q, k, v at one level, o at the
+ * next, gate and up at the next, down at the next.  Otherwise as
+ * q8_step_graph_build (host_idx, ownership, errors); the graph's mode is
+ * Q8_GRAPH_LEVELS.  Q8_ERR_NULL for levels == NULL, Q8_ERR_LEVELS for a
+ * negative or decreasing level. */
+int q8_step_graph_build_levels(const q8_matvec_desc *descs, const int32_t *levels,
+                               int32_t count, int32_t m, int32_t *host_idx,
+                               void *stream, q8_step_graph **out);
+
 /* Enqueues the whole step with one hipGraphLaunch on `stream`. */
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
-/* Persistent modes only: enqueues the same recorded step (its one
- * kernel, with the arguments fixed at build time) with a single kernel
- * launch instead of hipGraphLaunch: the same work, results and host_idx
- * writes.  Runs on the graph's device whatever device is current; `stream`
+/* All but Q8_GRAPH_CHAIN: enqueues the same recorded step (its kernel, or
+ * its kernels in level order, with the arguments fixed at build time) with
+ * kernel launches instead of hipGraphLaunch: the same work, results and
+ * host_idx writes.  Runs on the graph's device whatever device is current; `stream`
  * must belong to that device.  On MI355X with ROCm 7.2 a hipGraphLaunch
  * costs ~10 us more launch latency than a kernel launch (measured).
  * Q8_ERR_MODE for a chain graph. */

@@ -22,6 +22,7 @@ Q8_MAX_N = 65536
 Q8_GRAPH_CHAIN = 0
 Q8_GRAPH_PERSISTENT = 1
 Q8_GRAPH_PERSISTENT_I8X = 2
+Q8_GRAPH_LEVELS = 3
 BLOCK = 32
 BLOCK_BYTES = 34
 
@@ -70,6 +71,9 @@ def load(path: str = LIB_PATH):
         "q8_step_graph_build": (ctypes.c_int, [ctypes.POINTER(MatvecDesc), i32,
                                                i32, vp, i32, vp,
                                                ctypes.POINTER(vp)]),
+        "q8_step_graph_build_levels": (ctypes.c_int, [ctypes.POINTER(MatvecDesc), vp,
+                                                      i32, i32, vp, vp,
+                                                      ctypes.POINTER(vp)]),
         "q8_step_graph_launch": (ctypes.c_int, [vp, vp]),
         "q8_step_graph_launch_kernel": (ctypes.c_int, [vp, vp]),
         "q8_step_graph_info": (ctypes.c_int, [vp, pi32, pi32]),
@@ -252,7 +256,7 @@ class StepGraph:
     """
 
     def __init__(self, descs, m: int, host_idx=None,
-                 mode: int = Q8_GRAPH_CHAIN, device=None):
+                 mode: int = Q8_GRAPH_CHAIN, device=None, levels=None):
         torch = _torch()
         self._keep = []
         arr = (MatvecDesc * len(descs))()
@@ -287,11 +291,21 @@ class StepGraph:
         self.mode = mode
         dev = device if device is not None else descs[0]["x"].device
         handle = ctypes.c_void_p(None)
+        hptr = host_idx.data_ptr() if host_idx is not None else None
         with torch.cuda.device(dev):
-            _check(load().q8_step_graph_build(
-                arr, len(descs), m,
-                host_idx.data_ptr() if host_idx is not None else None,
-                mode, _stream(None, dev), ctypes.byref(handle)))
+            if levels is not None:  # one persistent node per run of a level
+                lv = (ctypes.c_int32 * len(descs))(*[int(v) for v in levels])
+                if len(levels) != len(descs):
+                    raise ValueError("one level per descriptor")
+                self._keep.append(lv)
+                _check(load().q8_step_graph_build_levels(
+                    arr, ctypes.addressof(lv), len(descs), m, hptr,
+                    _stream(None, dev), ctypes.byref(handle)))
+                self.mode = Q8_GRAPH_LEVELS
+            else:
+                _check(load().q8_step_graph_build(
+                    arr, len(descs), m, hptr, mode, _stream(None, dev),
+                    ctypes.byref(handle)))
         self._h = handle
         self.device = dev
 

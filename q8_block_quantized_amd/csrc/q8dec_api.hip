@@ -114,6 +114,16 @@ constexpr uint32_t kGraphMagic = 0x51384447u;  // "Q8DG"
 
 }  // namespace
 
+// One persistent kernel launch of a step: the descriptor table and
+// workgroup ranges of its descriptors (device memory) and its shape.
+struct SegmentLaunch {
+  const q8::StepDesc *table;
+  const q8::WgGroup *groups;
+  int32_t count, group_size, grid;
+  size_t lds;
+  bool all_staged;
+};
+
 struct q8_step_graph {
   uint32_t magic;
   int device;
@@ -122,14 +132,12 @@ struct q8_step_graph {
   int32_t memcpy_nodes;
   hipGraph_t graph;
   hipGraphExec_t exec;
-  void *workspace;  // argmax slots (+ descriptor table in persistent mode)
-  // persistent mode: the recorded kernel launch, for q8_step_graph_launch_kernel
-  const q8::StepDesc *table;
-  const q8::WgGroup *groups;
-  int32_t count, m, group_size, grid;
-  size_t lds;
-  bool all_staged;
+  void *workspace;  // argmax slots, then each segment's table and ranges
+  int32_t m;
   bool i8x;
+  // persistent modes: the recorded kernel launches in order, for
+  // q8_step_graph_launch_kernel
+  std::vector<SegmentLaunch> launches;
 };
 
 namespace {
@@ -286,6 +294,7 @@ const char *q8_status_name(int status) {
     case Q8_ERR_BAD_HANDLE: return "q8_err_bad_handle";
     case Q8_ERR_COUNT: return "q8_err_count";
     case Q8_ERR_MODE: return "q8_err_mode";
+    case Q8_ERR_LEVELS: return "q8_err_levels";
     default: return "q8_code_out_of_range";
   }
 }
@@ -376,17 +385,25 @@ int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
-int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
-                        int32_t *host_idx, int32_t mode, void *stream,
-                        q8_step_graph **out) {
-  (void)stream;
+namespace {
+
+// Builds every form of step graph.  levels (Q8_GRAPH_LEVELS only) gives each
+// descriptor's dependency level; each run of equal levels becomes one
+// persistent kernel node, the nodes in level order.
+int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t count,
+                int32_t m, int32_t *host_idx, int32_t mode, q8_step_graph **out) {
   if (!out || !descs) return Q8_ERR_NULL;
   *out = nullptr;
   if (count < 1 || count > Q8_MAX_DESCS) return Q8_ERR_COUNT;
   if (mode != Q8_GRAPH_CHAIN && mode != Q8_GRAPH_PERSISTENT &&
-      mode != Q8_GRAPH_PERSISTENT_I8X)
+      mode != Q8_GRAPH_PERSISTENT_I8X && mode != Q8_GRAPH_LEVELS)
     return Q8_ERR_MODE;
   if (m < 1 || m > Q8_MAX_M) return Q8_ERR_SHAPE;
+  if (mode == Q8_GRAPH_LEVELS) {
+    if (!levels) return Q8_ERR_NULL;
+    for (int32_t i = 0; i < count; i++)
+      if (levels[i] < 0 || (i && levels[i] < levels[i - 1])) return Q8_ERR_LEVELS;
+  }
   const bool i8x = mode == Q8_GRAPH_PERSISTENT_I8X;
   const bool persistent = mode != Q8_GRAPH_CHAIN;
   int nargmax = 0;
@@ -409,63 +426,93 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
     if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
   }
 
+  // persistent segments: all descriptors, or each run of one level
+  struct Segment {
+    int32_t begin, end;
+    q8::StepPlan plan;
+  };
+  std::vector<Segment> segs;
+  if (persistent) {
+    for (int32_t i = 0; i < count;) {
+      int32_t j = i + 1;
+      if (mode == Q8_GRAPH_LEVELS) {
+        while (j < count && levels[j] == levels[i]) j++;
+      } else {
+        j = count;
+      }
+      segs.push_back(Segment{i, j, q8::StepPlan()});
+      i = j;
+    }
+    for (auto &sg : segs) {
+      st = q8::plan_step(descs + sg.begin, sg.end - sg.begin, m, dev,
+                         m == 1 ? q8::kStepGroupSize : q8::kStepGroupSizeBatched,
+                         sg.plan, i8x);
+      if (st) return st;
+    }
+  }
+
   q8_step_graph *g = new (std::nothrow) q8_step_graph();
   if (!g) return Q8_ERR_GRAPH;
   g->magic = kGraphMagic;
   g->device = dev;
   g->mode = mode;
+  g->m = m;
+  g->i8x = i8x;
 
-  // workspace: one argmax slot per argmax descriptor, then (persistent mode)
-  // the device copies of the descriptor table and the workgroup ranges
+  // workspace: one argmax slot per argmax descriptor, then each segment's
+  // descriptor table and workgroup ranges (16-byte aligned pieces)
   const size_t slot_bytes = (size_t)(nargmax ? nargmax : 1) * sizeof(q8::ArgmaxSlot);
-  q8::StepPlan plan;
-  if (persistent) {
-    st = q8::plan_step(descs, count, m, dev,
-                       m == 1 ? q8::kStepGroupSize : q8::kStepGroupSizeBatched, plan, i8x);
-    if (st) {
-      release_graph(g);
-      return st;
-    }
+  size_t total = slot_bytes;
+  std::vector<size_t> table_off, group_off;
+  for (auto &sg : segs) {
+    table_off.push_back(total);
+    total += sg.plan.descs.size() * sizeof(q8::StepDesc);
+    group_off.push_back(total);
+    total += (sg.plan.groups.size() * sizeof(q8::WgGroup) + 15) & ~(size_t)15;
   }
-  const size_t table_bytes = plan.descs.size() * sizeof(q8::StepDesc);
-  const size_t group_bytes = plan.groups.size() * sizeof(q8::WgGroup);
-  const size_t total = slot_bytes + table_bytes + group_bytes;
   hipError_t e = hipMalloc(&g->workspace, total);
   if (e == hipSuccess) e = hipMemset(g->workspace, 0, total);
   if (e != hipSuccess) {
     release_graph(g);
     return hip_fail(e);
   }
-  q8::ArgmaxSlot *slots = (q8::ArgmaxSlot *)g->workspace;
-  q8::StepDesc *table = (q8::StepDesc *)((char *)g->workspace + slot_bytes);
-  q8::WgGroup *groups =
-      (q8::WgGroup *)((char *)g->workspace + slot_bytes + table_bytes);
+  char *ws = (char *)g->workspace;
+  q8::ArgmaxSlot *slots = (q8::ArgmaxSlot *)ws;
   {
-    // argmax slots: keys and counters zero, arrival counts from the plan
-    // (persistent mode; the chain's kernels count their own grids), host
-    // copy of argmax descriptor a at host_idx + a * m
+    // argmax slots: keys and counters zero, arrival counts from the plans
+    // (the chain's kernels count their own grids), host copy of argmax
+    // descriptor a (in descriptor order) at host_idx + a * m
     std::vector<q8::ArgmaxSlot> hs(nargmax ? nargmax : 1);
     std::memset(hs.data(), 0, hs.size() * sizeof(q8::ArgmaxSlot));
     for (int a = 0; a < nargmax; a++)
       hs[a].host = host_dev ? host_dev + (size_t)a * m : nullptr;
-    if (persistent) {
-      int a = 0;
-      for (auto &t : plan.descs) {
+    int a = 0;
+    for (auto &sg : segs) {
+      int k = 0;
+      for (auto &t : sg.plan.descs) {
         if (!t.idx) continue;
         uint32_t nteams = 0;
         for (int j = 0; j < q8::kArgmaxTeams; j++) {
-          hs[a].team[j].expected = plan.expected[a][j];
-          nteams += plan.expected[a][j] ? 1u : 0u;
+          hs[a].team[j].expected = sg.plan.expected[k][j];
+          nteams += sg.plan.expected[k][j] ? 1u : 0u;
         }
         hs[a].top.expected = nteams;
         t.slot = &slots[a++];
+        k++;
       }
     }
     e = hipMemcpy(slots, hs.data(), slot_bytes, hipMemcpyHostToDevice);
-    if (e == hipSuccess && table_bytes)
-      e = hipMemcpy(table, plan.descs.data(), table_bytes, hipMemcpyHostToDevice);
-    if (e == hipSuccess && group_bytes)
-      e = hipMemcpy(groups, plan.groups.data(), group_bytes, hipMemcpyHostToDevice);
+    for (size_t i = 0; i < segs.size() && e == hipSuccess; i++) {
+      const q8::StepPlan &pl = segs[i].plan;
+      e = hipMemcpy(ws + table_off[i], pl.descs.data(),
+                    pl.descs.size() * sizeof(q8::StepDesc), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(ws + group_off[i], pl.groups.data(),
+                      pl.groups.size() * sizeof(q8::WgGroup), hipMemcpyHostToDevice);
+      g->launches.push_back(SegmentLaunch{
+          (const q8::StepDesc *)(ws + table_off[i]), (const q8::WgGroup *)(ws + group_off[i]),
+          segs[i].end - segs[i].begin, pl.group_size, pl.grid, pl.lds, pl.all_staged});
+    }
     if (e != hipSuccess) {
       release_graph(g);
       return hip_fail(e);
@@ -490,17 +537,11 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                                slot, d.idx, cs);
       }
     } else {
-      le = q8::launch_step(table, count, groups, plan.group_size, m, plan.grid,
-                           plan.lds, plan.all_staged, cs, i8x);
-      g->i8x = i8x;
-      g->table = table;
-      g->groups = groups;
-      g->count = count;
-      g->m = m;
-      g->group_size = plan.group_size;
-      g->grid = plan.grid;
-      g->lds = plan.lds;
-      g->all_staged = plan.all_staged;
+      for (size_t i = 0; i < g->launches.size() && le == hipSuccess; i++) {
+        const SegmentLaunch &L = g->launches[i];
+        le = q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid,
+                             L.lds, L.all_staged, cs, i8x);
+      }
     }
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
@@ -531,6 +572,23 @@ int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
   return Q8_OK;
 }
 
+}  // namespace
+
+int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
+                        int32_t *host_idx, int32_t mode, void *stream,
+                        q8_step_graph **out) {
+  (void)stream;
+  if (mode == Q8_GRAPH_LEVELS) return Q8_ERR_MODE;  // needs the levels
+  return build_graph(descs, nullptr, count, m, host_idx, mode, out);
+}
+
+int q8_step_graph_build_levels(const q8_matvec_desc *descs, const int32_t *levels,
+                               int32_t count, int32_t m, int32_t *host_idx,
+                               void *stream, q8_step_graph **out) {
+  (void)stream;
+  return build_graph(descs, levels, count, m, host_idx, Q8_GRAPH_LEVELS, out);
+}
+
 int q8_step_graph_launch(q8_step_graph *g, void *stream) {
   if (!live_graph(g)) return Q8_ERR_BAD_HANDLE;
   hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
@@ -544,8 +602,11 @@ int q8_step_graph_launch_kernel(q8_step_graph *g, void *stream) {
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e);
   if (cur != g->device && (e = hipSetDevice(g->device)) != hipSuccess) return hip_fail(e);
-  e = q8::launch_step(g->table, g->count, g->groups, g->group_size, g->m, g->grid,
-                      g->lds, g->all_staged, (hipStream_t)stream, g->i8x);
+  for (size_t i = 0; i < g->launches.size() && e == hipSuccess; i++) {
+    const SegmentLaunch &L = g->launches[i];
+    e = q8::launch_step(L.table, L.count, L.groups, L.group_size, g->m, L.grid, L.lds,
+                        L.all_staged, (hipStream_t)stream, g->i8x);
+  }
   if (cur != g->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }

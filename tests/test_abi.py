@@ -49,10 +49,10 @@ def test_status_names(lib):
     want = {0: "q8_ok", 1: "q8_err_null", 2: "q8_err_shape", 3: "q8_err_align",
             4: "q8_err_no_device", 5: "q8_err_arch", 6: "q8_err_code_object",
             7: "q8_err_hip", 8: "q8_err_graph", 9: "q8_err_bad_handle",
-            10: "q8_err_count", 11: "q8_err_mode"}
+            10: "q8_err_count", 11: "q8_err_mode", 12: "q8_err_levels"}
     for code, name in want.items():
         assert q8.q8_status_name(code) == name
-    for code in (-1, 12, 99, 1 << 30):
+    for code in (-1, 13, 99, 1 << 30):
         assert q8.q8_status_name(code) == "q8_code_out_of_range"
 
 
@@ -108,6 +108,26 @@ def _descs(k, **over):
     return arr
 
 
+def test_step_graph_levels_refusals(lib):
+    """Levels are checked before any GPU work: NULL, negative or decreasing
+    levels are refused, and the plain builder refuses the levels mode."""
+    h = ctypes.c_void_p(None)
+    b = lib.q8_step_graph_build_levels
+    keep = []
+
+    def lv(*v):
+        a = (ctypes.c_int32 * len(v))(*v)
+        keep.append(a)
+        return ctypes.addressof(a)
+    assert b(_descs(2), None, 2, 1, None, None, ctypes.byref(h)) == NULL
+    assert b(_descs(2), lv(1, 0), 2, 1, None, None, ctypes.byref(h)) == 12
+    assert b(_descs(2), lv(-1, 0), 2, 1, None, None, ctypes.byref(h)) == 12
+    assert b(_descs(2), lv(0, 0), 2, 0, None, None, ctypes.byref(h)) == SHAPE
+    assert b(_descs(2, n=40), lv(0, 1), 2, 1, None, None, ctypes.byref(h)) == SHAPE
+    assert lib.q8_step_graph_build(_descs(1), 1, 1, None, 3, None, ctypes.byref(h)) == MODE
+    assert not h.value
+
+
 def test_step_graph_refusals(lib):
     h = ctypes.c_void_p(None)
     b = lib.q8_step_graph_build
@@ -130,6 +150,8 @@ def test_graph_handle_refusals(lib):
     fake = ctypes.c_void_p(0x12345678)
     k = ctypes.c_int32(0)
     assert lib.q8_step_graph_launch(None, None) == BAD_HANDLE
+    assert lib.q8_step_graph_launch_kernel(None, None) == BAD_HANDLE
+    assert lib.q8_step_graph_launch_kernel(fake, None) == BAD_HANDLE
     assert lib.q8_step_graph_launch(fake, None) == BAD_HANDLE
     assert lib.q8_step_graph_info(None, ctypes.byref(k), None) == BAD_HANDLE
     assert lib.q8_step_graph_info(fake, ctypes.byref(k), None) == BAD_HANDLE

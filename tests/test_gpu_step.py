@@ -188,6 +188,52 @@ def test_kernel_launch_equals_graph_launch(cuda, m):
     gc.close()
 
 
+def layer_levels(layers):
+    """Dependency levels of a decoder step in model order: q, k, v together,
+    then o, then gate and up together, then down, per layer; the lm_head
+    last."""
+    lv = []
+    for l in range(layers):
+        base = 4 * l
+        lv += [base, base, base, base + 1, base + 2, base + 2, base + 3]
+    return lv + [4 * layers]
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_levels_step_equals_standalone(cuda, m):
+    """q8_step_graph_build_levels: one persistent node per level (9 for two
+    layers and the lm_head); every output and token equals the standalone
+    calls' bit for bit, through the graph and through the kernel launches."""
+    import torch
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(2, 20000, m, seed=8)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, device=cuda, levels=layer_levels(2))
+    assert g.info() == (9, 0)
+    want = []
+    for d in descs[:-1]:
+        y = torch.empty_like(d["y"])
+        q8.q8_matvec_batched(d["w"], d["x"], y)
+        want.append(y)
+    lm = descs[-1]
+    ylm = torch.empty_like(lm["y"])
+    idx = torch.empty_like(lm["idx"])
+    q8.q8_matvec_argmax(lm["w"], lm["x"], idx, lm["p"], y=ylm)
+    want.append(ylm)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        host[:] = -9
+        (g.launch if k != 1 else g.launch_kernel)()
+        torch.cuda.synchronize()
+        for d, w_ in zip(descs, want):
+            assert torch.equal(d["y"], w_)
+        assert torch.equal(host, idx.cpu())
+    g.close()
+
+
 def test_destroyed_handle_is_refused(cuda):
     import q8_block_quantized_amd as q8
     shapes, ws, xs = step_inputs(0, 64, 1, seed=4)
