@@ -1025,8 +1025,15 @@ struct OneSrc {
 struct TableSrc {
   const StepDesc *tab;
   int32_t count;
-  // Last descriptor at or after `lo` with tile_begin <= t.
+  // Last descriptor at or after `lo` with tile_begin <= t.  A workgroup
+  // moves to the next matvec or the one after it almost always, so a short
+  // forward scan answers before the binary search (dependent loads delay
+  // the next tile's prefetch).
   __device__ __forceinline__ int32_t find(int32_t t, int32_t lo) const {
+#pragma unroll
+    for (int k = 0; k < 2; k++)
+      if (lo + 1 < count && tab[lo + 1].tile_begin <= t) lo++;
+    if (lo + 1 >= count || tab[lo + 1].tile_begin > t) return lo;
     int32_t hi = count - 1;
     while (lo < hi) {
       const int32_t mid = (lo + hi + 1) >> 1;

@@ -234,6 +234,31 @@ def test_levels_step_equals_standalone(cuda, m):
     g.close()
 
 
+@pytest.mark.parametrize("mode", [1, 2], ids=["persistent", "persistent-i8x"])
+def test_step_with_empty_descriptors(cuda, mode):
+    """Descriptors with p = 0 own no tiles; placed first, between others and
+    last-but-one, the tile lookup skips them and every other output equals
+    its standalone call bit for bit."""
+    import torch
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(1, 3000, 1, seed=9)
+    descs = device_step(shapes, ws, xs, 1, cuda)
+    empty = lambda: dict(n=1024, p=0, w=torch.empty(0, dtype=torch.uint8, device=cuda),  # noqa: E731
+                         x=to_dev(np.ones((1, 1024), np.float32), cuda), idx=None,
+                         y=torch.empty((1, 0), dtype=torch.float32, device=cuda))
+    mixed = [empty(), descs[0], descs[1], empty(), empty(), *descs[2:-1], empty(), descs[-1]]
+    g, host = run_graph(mixed, 1, mode, cuda)
+    g.launch()
+    torch.cuda.synchronize()
+    fn = q8.q8_matvec_i8x if mode == 2 else q8.q8_matvec_batched
+    for d in descs[:-1]:
+        y = torch.empty_like(d["y"])
+        fn(d["w"], d["x"], y)
+        torch.cuda.synchronize()
+        assert torch.equal(d["y"], y)
+    g.close()
+
+
 def test_destroyed_handle_is_refused(cuda):
     import q8_block_quantized_amd as q8
     shapes, ws, xs = step_inputs(0, 64, 1, seed=4)
