@@ -34,11 +34,19 @@
  *   y[r] = sum_b scale_b * d_b * sum_j qw_bj * qx_bj
  * with the integer sums exact and the rest in binary64, natural order.
  *
+ * The rest of the decode step (inferno.rs "IV.4": "Eight kernels" for
+ * rms_norm_row, rope_row, append_kv, attention_decode, add_inplace and
+ * silu_hadamard; "One command buffer" for their order in a layer) is
+ * evaluated in binary64 from the listings' definitions, except the RoPE
+ * angle, which the listing types in binary32 and which is reproduced in
+ * binary32 (q8o_rope_angle).
+ *
  * Build: plain C11, no -ffast-math, floating contraction off.
  */
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* IEEE-754 binary16 -> binary64, from the format's definition: 1 sign bit,
  * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 holds zero and the
@@ -210,4 +218,168 @@ void q8o_matvec_i8x(const uint8_t *w, const float *d, const int8_t *q,
     y[r] = acc;
     if (tol) tol[r] = 1e-4 * size + 1e-6;
   }
+}
+
+/* ---- the rest of the decode step ---------------------------------------------
+ * inferno.rs "IV.4", "Eight kernels": rms_norm_row, rope_row, append_kv,
+ * attention_decode, add_inplace and silu_hadamard; "One command buffer": the
+ * order in which a layer runs them.  Activations are binary64 throughout;
+ * the weights are the Q8_0 bytes and the binary32 norm weights, widened
+ * exactly.  The one step the pages type in binary32 on purpose, the RoPE
+ * angle, is reproduced in binary32 (q8o_rope_angle). */
+
+/* q8_matvec with binary64 activations: y[r] = sum_b scale_b sum_j q_bj x_j,
+ * natural order; mag[r] = sum of |scale*q*x| (if non-NULL). */
+void q8o_matvec_f64(const uint8_t *w, const double *x, int64_t n, int64_t p,
+                    double *y, double *mag) {
+  const int64_t blocks = n / 32;
+  for (int64_t r = 0; r < p; r++) {
+    const uint8_t *row = w + (size_t)r * (size_t)blocks * 34u;
+    double sum = 0.0, size = 0.0;
+    for (int64_t b = 0; b < blocks; b++) {
+      const uint8_t *blk = row + (size_t)b * 34u;
+      double scale = q8o_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+      for (int j = 0; j < 32; j++) {
+        double t = scale * (double)(int8_t)blk[2 + j] * x[32 * b + j];
+        sum += t;
+        size += fabs(t);
+      }
+    }
+    y[r] = sum;
+    if (mag) mag[r] = size;
+  }
+}
+
+/* rms_norm_row: every row of dim values is divided by the root of (its mean
+ * square + eps) and multiplied element-wise by the weight. */
+void q8o_rms_norm(const double *x, const double *w, double *out, int64_t rows,
+                  int64_t dim, double eps) {
+  for (int64_t r = 0; r < rows; r++) {
+    const double *xr = x + r * dim;
+    double ss = 0.0;
+    for (int64_t i = 0; i < dim; i++) ss += xr[i] * xr[i];
+    const double inv = 1.0 / sqrt(ss / (double)dim + eps);
+    for (int64_t i = 0; i < dim; i++) out[r * dim + i] = xr[i] * inv * w[i];
+  }
+}
+
+/* rope_row's angle for pair i of a head (half = head_dim / 2) at position
+ * pos.  The listing types it in binary32: the frequency is 1 over
+ * theta^(i/half), the power correctly rounded (its precise:: functions) and
+ * the quotient rounded to binary32, and the angle is pos times that
+ * frequency, rounded to binary32. */
+float q8o_rope_angle(int64_t pos, int64_t i, int64_t half, float theta) {
+  const float e = (float)i / (float)half;
+  const float pw = (float)pow((double)theta, (double)e);
+  const float freq = 1.0f / pw;
+  return (float)pos * freq;
+}
+
+/* rope_row: in each of `heads` heads, element i and element i + half turn
+ * together by the angle of pair i: (a, b) -> (a cos - b sin, a sin + b cos). */
+void q8o_rope(double *x, int64_t heads, int64_t head_dim, int64_t pos, float theta) {
+  const int64_t half = head_dim / 2;
+  for (int64_t h = 0; h < heads; h++) {
+    double *xh = x + h * head_dim;
+    for (int64_t i = 0; i < half; i++) {
+      const double ang = (double)q8o_rope_angle(pos, i, half, theta);
+      const double c = cos(ang), s = sin(ang);
+      const double a = xh[i], b = xh[i + half];
+      xh[i] = a * c - b * s;
+      xh[i + half] = a * s + b * c;
+    }
+  }
+}
+
+/* attention_decode: query head h reads key/value head h / kv_group of the
+ * seq cached rows (row t of head g starts at t * kv_width + g * head_dim);
+ * score_t = q . k_t / sqrt(head_dim); weights = softmax of the scores with
+ * their maximum subtracted; out = sum_t weight_t v_t.  probs, if non-NULL,
+ * receives the weights, [n_heads][seq]. */
+void q8o_attention(const double *q, const double *kc, const double *vc, double *out,
+                   double *probs, int64_t seq, int64_t kv_width, int64_t head_dim,
+                   int64_t kv_group, int64_t n_heads) {
+  const double scale = 1.0 / sqrt((double)head_dim);
+  for (int64_t h = 0; h < n_heads; h++) {
+    const int64_t off = (h / kv_group) * head_dim;
+    const double *qh = q + h * head_dim;
+    double *sc = probs ? probs + h * seq : (double *)malloc(sizeof(double) * (size_t)(seq > 0 ? seq : 1));
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < seq; t++) {
+      const double *kr = kc + t * kv_width + off;
+      double d = 0.0;
+      for (int64_t j = 0; j < head_dim; j++) d += qh[j] * kr[j];
+      sc[t] = d * scale;
+      if (sc[t] > mx) mx = sc[t];
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < seq; t++) {
+      sc[t] = exp(sc[t] - mx);
+      sum += sc[t];
+    }
+    for (int64_t t = 0; t < seq; t++) sc[t] /= sum;
+    for (int64_t j = 0; j < head_dim; j++) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < seq; t++) acc += sc[t] * vc[t * kv_width + off + j];
+      out[h * head_dim + j] = acc;
+    }
+    if (!probs) free(sc);
+  }
+}
+
+/* silu_hadamard: out = gate / (1 + e^-gate) * up, element-wise. */
+void q8o_silu_mul(const double *g, const double *u, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* Shapes of a decoder layer. */
+typedef struct {
+  int64_t hidden, n_heads, n_kv_heads, head_dim, inter;
+  double eps;
+  float theta;
+} q8o_dims;
+
+/* One layer's weights: Q8_0 bytes of the seven projections ([out][in/32]
+ * blocks) and the binary64 norm weights. */
+typedef struct {
+  const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+  const double *attn_norm, *q_norm, *k_norm, *ffn_norm;
+} q8o_layer;
+
+/* The layer's intermediate values, each sized for its role. */
+typedef struct {
+  double *xn, *q, *k, *v, *attn, *attn_out, *xn2, *gate, *up, *h, *ffn_out;
+} q8o_acts;
+
+/* One layer of the decode step at position pos, in the order the command
+ * buffer encodes it: norm -> q, k, v -> QK-norm -> RoPE on q and k -> append
+ * k, v as cache row pos -> attention over rows 0..pos -> o projection, added
+ * into x -> norm -> gate, up -> SwiGLU -> down projection, added into x.
+ * x [hidden] is updated in place; kc, vc are [>= pos + 1][kv_width]. */
+void q8o_decode_layer(const q8o_dims *dm, const q8o_layer *L, double *x, double *kc,
+                      double *vc, int64_t pos, const q8o_acts *a) {
+  const int64_t H = dm->hidden, hd = dm->head_dim;
+  const int64_t qw = dm->n_heads * hd, kvw = dm->n_kv_heads * hd;
+  q8o_rms_norm(x, L->attn_norm, a->xn, 1, H, dm->eps);
+  q8o_matvec_f64(L->wq, a->xn, H, qw, a->q, 0);
+  q8o_matvec_f64(L->wk, a->xn, H, kvw, a->k, 0);
+  q8o_matvec_f64(L->wv, a->xn, H, kvw, a->v, 0);
+  q8o_rms_norm(a->q, L->q_norm, a->q, dm->n_heads, hd, dm->eps);
+  q8o_rms_norm(a->k, L->k_norm, a->k, dm->n_kv_heads, hd, dm->eps);
+  q8o_rope(a->q, dm->n_heads, hd, pos, dm->theta);
+  q8o_rope(a->k, dm->n_kv_heads, hd, pos, dm->theta);
+  for (int64_t i = 0; i < kvw; i++) {
+    kc[pos * kvw + i] = a->k[i];
+    vc[pos * kvw + i] = a->v[i];
+  }
+  q8o_attention(a->q, kc, vc, a->attn, 0, pos + 1, kvw, hd,
+                dm->n_heads / dm->n_kv_heads, dm->n_heads);
+  q8o_matvec_f64(L->wo, a->attn, qw, H, a->attn_out, 0);
+  for (int64_t i = 0; i < H; i++) x[i] += a->attn_out[i];
+  q8o_rms_norm(x, L->ffn_norm, a->xn2, 1, H, dm->eps);
+  q8o_matvec_f64(L->wg, a->xn2, H, dm->inter, a->gate, 0);
+  q8o_matvec_f64(L->wu, a->xn2, H, dm->inter, a->up, 0);
+  q8o_silu_mul(a->gate, a->up, a->h, dm->inter);
+  q8o_matvec_f64(L->wd, a->h, dm->inter, H, a->ffn_out, 0);
+  for (int64_t i = 0; i < H; i++) x[i] += a->ffn_out[i];
 }

@@ -410,6 +410,289 @@ def pin_q8x_tolerance_hand_case(orc):
     assert abs(tol[0] - (1e-4 * d * 381 + 1e-6)) <= 1e-18
 
 
+# ---- the rest of the decode step ----------------------------------------------
+
+def selector(p: int, n: int, col) -> np.ndarray:
+    """Q8_0 rows that pick one input: row r has scale 1.0 and quant 1 at
+    column col(r), zero elsewhere (zero scales on the other blocks)."""
+    bpr = n // 32
+    bits = np.zeros((p, bpr), dtype=np.uint16)
+    q = np.zeros((p, bpr, 32), dtype=np.int8)
+    for r in range(p):
+        c = col(r)
+        bits[r, c // 32] = 0x3C00
+        q[r, c // 32, c % 32] = 1
+    return make_blocks(bits, q)
+
+
+def zero_q8(p: int, n: int) -> np.ndarray:
+    return np.zeros((p, n // 32 * 34), dtype=np.uint8)
+
+
+def np_rms(x, w, eps):
+    """rms_norm_row with numpy, rows of the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
+def np_silu_mul(g, u):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g)) * u
+
+
+TINY = dict(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, inter=96,
+            eps=1e-6, theta=10000.0)
+
+
+def tiny_layer(rng, **over):
+    """A layer of the tiny shapes: random weights unless replaced."""
+    H, hd, inter = TINY["hidden"], TINY["head_dim"], TINY["inter"]
+    qw, kvw = TINY["n_heads"] * hd, TINY["n_kv_heads"] * hd
+
+    def rnd(p, n):
+        bits = np.full((p, n // 32), 0x2000, dtype=np.uint16)  # 2^-7
+        q = rng.integers(-127, 128, size=(p, n // 32, 32)).astype(np.int8)
+        return make_blocks(bits, q)
+    layer = dict(wq=rnd(qw, H), wk=rnd(kvw, H), wv=rnd(kvw, H), wo=rnd(H, qw),
+                 wg=rnd(inter, H), wu=rnd(inter, H), wd=rnd(H, inter),
+                 attn_norm=rng.uniform(0.5, 1.5, H), q_norm=rng.uniform(0.5, 1.5, hd),
+                 k_norm=rng.uniform(0.5, 1.5, hd), ffn_norm=rng.uniform(0.5, 1.5, H))
+    layer.update(over)
+    return layer
+
+
+def pin_rms_norm_closed_forms(orc):
+    """rms_norm_row: (3, 4) with eps 0 is (3, 4)/sqrt(12.5); a constant row
+    c with eps e is c/sqrt(c^2 + e) times the weight; with eps 0 and unit
+    weight the mean square of the output is 1; scaling x by 8 changes
+    nothing (exact in binary64); rows are independent; the weight is applied
+    element-wise."""
+    out = orc.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(out, [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=1e-15, atol=0)
+    w = np.arange(1.0, 9.0)
+    out = orc.rms_norm(np.full(8, 2.0), w, 0.5)
+    assert np.allclose(out, 2.0 / math.sqrt(4.5) * w, rtol=1e-15, atol=0)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 128))
+    out = orc.rms_norm(x, np.ones(128), 0.0)
+    assert np.allclose(np.mean(out * out, axis=1), 1.0, rtol=1e-13, atol=0)
+    assert np.array_equal(orc.rms_norm(8.0 * x, np.ones(128), 0.0), out)
+    for r in range(3):
+        assert np.array_equal(orc.rms_norm(x[r], np.ones(128), 0.0), out[r])
+    e = np.zeros(128)
+    e[17] = 5.0
+    o2 = orc.rms_norm(x[0], e, 1e-6)
+    assert np.count_nonzero(o2) == 1 and o2[17] != 0.0
+    assert np.allclose(orc.rms_norm(x, np.ones(128), 1e-6), np_rms(x, 1.0, 1e-6),
+                       rtol=1e-13, atol=0)
+
+
+def pin_rope_closed_forms(orc):
+    """rope_row: pair 0 turns by exactly pos radians (its frequency is 1);
+    pair i's angle at position 1 is theta^(-i/half) to binary32 accuracy;
+    position 0 is the identity; a unit vector on element 0 goes to
+    (cos pos, sin pos) on elements 0 and half, one on element half to
+    (-sin pos, cos pos); every pair keeps its length; every head turns the
+    same way; pair 0's dot products depend only on the difference of the
+    positions."""
+    for pos in (0, 1, 7, 513, 4095):
+        assert orc.rope_angle(pos, 0, 64, 1e6) == np.float32(pos)
+    for i in range(64):
+        a = float(orc.rope_angle(1, i, 64, 1e6))
+        ref = 1e6 ** (-i / 64)
+        assert abs(a - ref) <= 2 * 2.0 ** -23 * ref
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(3 * 8)
+    assert np.array_equal(orc.rope(x, 8, 0, 1e4), x)
+    for pos in (1, 3, 100):
+        e0 = np.zeros(8)
+        e0[0] = 1.0
+        out = orc.rope(e0, 8, pos, 1e4)
+        ref = np.zeros(8)
+        ref[0], ref[4] = math.cos(pos), math.sin(pos)
+        assert np.allclose(out, ref, rtol=0, atol=1e-15)
+        e4 = np.zeros(8)
+        e4[4] = 1.0
+        out = orc.rope(e4, 8, pos, 1e4)
+        ref = np.zeros(8)
+        ref[0], ref[4] = -math.sin(pos), math.cos(pos)
+        assert np.allclose(out, ref, rtol=0, atol=1e-15)
+        e1 = np.zeros(8)
+        e1[1] = 1.0
+        out = orc.rope(e1, 8, pos, 1e4)
+        ang = float(np.float32(pos) * (np.float32(1.0) / np.float32(1e4 ** 0.25)))
+        ref = np.zeros(8)
+        ref[1], ref[5] = math.cos(ang), math.sin(ang)
+        assert np.allclose(out, ref, rtol=0, atol=1e-15)
+    out = orc.rope(x, 8, 37, 1e4).reshape(3, 8)
+    xr = x.reshape(3, 8)
+    assert np.allclose(np.hypot(out[:, :4], out[:, 4:]), np.hypot(xr[:, :4], xr[:, 4:]),
+                       rtol=1e-14, atol=0)
+    same = orc.rope(np.concatenate([xr[0], xr[0]]), 8, 37, 1e4).reshape(2, 8)
+    assert np.array_equal(same[0], same[1]) and np.array_equal(same[0], out[0])
+    q, k = rng.standard_normal(8), rng.standard_normal(8)
+
+    def dot0(a, b):
+        return a[0] * b[0] + a[4] * b[4]
+    d1 = dot0(orc.rope(q, 8, 5, 1e4), orc.rope(k, 8, 3, 1e4))
+    d2 = dot0(orc.rope(q, 8, 2, 1e4), orc.rope(k, 8, 0, 1e4))
+    assert abs(d1 - d2) <= 1e-13
+
+
+def pin_attention_closed_forms(orc):
+    """attention_decode (4 query heads, 2 key/value heads of width 4): one
+    cached row gives that row's values; equal keys give the mean of the
+    values; query head h reads key/value head h // 2; two rows with scores
+    s/2 and 0 (the 1/sqrt(4) scale) weigh the first by 1/(1 + e^(-s/2));
+    scores of +-1000 (beyond exp's binary64 range) stay finite and pick the top row; permuting the cached
+    rows changes nothing; the weights sum to one."""
+    rng = np.random.default_rng(11)
+    H, KV, hd = 4, 2, 4
+    kvw = KV * hd
+    q = rng.standard_normal(H * hd)
+    kc = rng.standard_normal((5, kvw))
+    vc = rng.standard_normal((5, kvw))
+    out, pr = orc.attention(q, kc, vc, 1, H, KV, hd)
+    for h in range(H):
+        assert np.array_equal(out[h * hd:(h + 1) * hd], vc[0, (h // 2) * hd:(h // 2 + 1) * hd])
+    kce = np.tile(kc[:1], (5, 1))
+    out, pr = orc.attention(q, kce, vc, 5, H, KV, hd)
+    for h in range(H):
+        g = h // 2
+        assert np.allclose(out[h * hd:(h + 1) * hd], vc[:, g * hd:(g + 1) * hd].mean(axis=0),
+                           rtol=1e-13, atol=1e-15)
+    vcg = np.empty_like(vc)
+    vcg[:, :hd], vcg[:, hd:] = 1.0, 2.0
+    out, pr = orc.attention(q, kc, vcg, 5, H, KV, hd)
+    assert np.allclose(out, np.repeat([1.0, 1.0, 2.0, 2.0], hd), rtol=1e-14, atol=0)
+    assert np.allclose(pr.sum(axis=1), 1.0, rtol=1e-14, atol=0)
+    s = 3.0
+    q2 = np.zeros(H * hd)
+    q2[0] = s
+    k2 = np.zeros((2, kvw))
+    k2[0, 0] = 1.0
+    v2 = np.zeros((2, kvw))
+    v2[0, :] = 1.0
+    out, pr = orc.attention(q2, k2, v2, 2, H, KV, hd)
+    p0 = 1.0 / (1.0 + math.exp(-s / 2))
+    assert abs(out[0] - p0) <= 1e-15 and abs(pr[0, 0] - p0) <= 1e-15
+    q3 = np.zeros(H * hd)
+    q3[0] = 2000.0
+    k3 = np.zeros((3, kvw))
+    k3[0, 0], k3[1, 0], k3[2, 0] = 1.0, -1.0, 0.5
+    v3 = np.arange(3 * kvw, dtype=np.float64).reshape(3, kvw)
+    out, pr = orc.attention(q3, k3, v3, 3, H, KV, hd)
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[:hd], v3[0, :hd], rtol=1e-15, atol=1e-100)
+    perm = [3, 0, 4, 1, 2]
+    o1, _ = orc.attention(q, kc, vc, 5, H, KV, hd)
+    o2, _ = orc.attention(q, kc[perm], vc[perm], 5, H, KV, hd)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-15)
+
+
+def pin_silu_closed_forms(orc):
+    """silu_hadamard: silu(0) = 0; silu(1) = 1/(1 + e^-1); silu(-1000) = -0;
+    silu(40) = 40 to binary64 rounding; the up factor multiplies."""
+    out = orc.silu_mul([0.0, 1.0, -1000.0, 40.0, 2.0, 1.0], [5.0, 1.0, 1.0, 1.0, 3.0, 2.0])
+    assert out[0] == 0.0
+    assert abs(out[1] - 0.7310585786300049) <= 1e-16
+    assert out[2] == 0.0 and math.copysign(1.0, out[2]) == -1.0
+    assert abs(out[3] - 40.0) <= 40.0 * 2.0 ** -52 * 4
+    assert abs(out[4] - 6.0 / (1.0 + math.exp(-2.0))) <= 1e-15
+    assert abs(out[5] - 2.0 * 0.7310585786300049) <= 2e-16
+
+
+def pin_matvec_f64_is_matvec(orc):
+    """With binary32-representable activations the binary64-activation matvec
+    gives the pinned matvec's values and magnitudes, bit for bit."""
+    w, x = rich_case(40, 256, seed=21)
+    y, tol = orc.matvec(w, x)
+    y2, mag = orc.matvec_f64(w, x.astype(np.float64))
+    assert np.array_equal(y, y2)
+    assert np.array_equal(tol, 1e-4 * mag + 1e-6)
+
+
+def _tiny_run(orc, layer, x, pos, kc, vc):
+    kc, vc = kc.copy(), vc.copy()
+    xo, acts = orc.decode_layer(TINY, layer, x, kc, vc, pos)
+    return xo, acts, kc, vc
+
+
+def pin_decode_layer_attention_branch(orc):
+    """A layer whose value and o projections pick inputs one to one and whose
+    MLP is zero: at position 0 attention returns the value row, so x gains
+    xn[kv slice of the head]; the cache receives v = xn[:32] and the QK-normed
+    key (RoPE is the identity at 0).  With a zero query projection at
+    position 3 every score is 0, so attention is the mean of the 3 cached
+    value rows and the appended one: the step attends over pos + 1 rows and
+    appends at row pos; the appended key is RoPE(QK-norm(k)) at 3."""
+    rng = np.random.default_rng(17)
+    H, hd = TINY["hidden"], TINY["head_dim"]
+    qw, kvw, inter = 4 * hd, 2 * hd, TINY["inter"]
+    eps = TINY["eps"]
+    layer = tiny_layer(rng, wv=selector(kvw, H, lambda r: r), wo=selector(H, qw, lambda r: r),
+                       wg=zero_q8(inter, H), wu=zero_q8(inter, H), wd=zero_q8(H, inter))
+    x = rng.standard_normal(H)
+    kc0 = rng.standard_normal((8, kvw))
+    vc0 = rng.standard_normal((8, kvw))
+    xo, acts, kc, vc = _tiny_run(orc, layer, x, 0, kc0, vc0)
+    xn = np_rms(x, layer["attn_norm"], eps)
+    gidx = np.array([((r // hd) // 2) * hd + r % hd for r in range(H)])
+    assert np.allclose(xo, x + xn[gidx], rtol=1e-14, atol=1e-15)
+    assert np.allclose(vc[0], xn[:kvw], rtol=1e-15, atol=0)
+    k = dense_dequant(layer["wk"], H) @ xn
+    kn = np_rms(k.reshape(2, hd), layer["k_norm"], eps).ravel()
+    assert np.allclose(kc[0], kn, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(kc[1:], kc0[1:]) and np.array_equal(vc[1:], vc0[1:])
+    layer["wq"] = zero_q8(qw, H)
+    xo, acts, kc, vc = _tiny_run(orc, layer, x, 3, kc0, vc0)
+    vmean = (vc0[:3].sum(axis=0) + xn[:kvw]) / 4.0
+    assert np.allclose(xo, x + vmean[gidx], rtol=1e-13, atol=1e-14)
+    assert np.allclose(kc[3], orc.rope(kn, hd, 3, TINY["theta"]), rtol=1e-12, atol=1e-14)
+    assert np.array_equal(kc[4:], kc0[4:]) and np.array_equal(kc[:3], kc0[:3])
+
+
+def pin_decode_layer_mlp_branch(orc):
+    """A layer whose o projection is zero and whose gate/up pick xn2[r % 64]
+    and down picks h[r]: x gains silu(xn2) * xn2, with xn2 the ffn-normed x."""
+    rng = np.random.default_rng(19)
+    H, hd = TINY["hidden"], TINY["head_dim"]
+    qw, inter = 4 * hd, TINY["inter"]
+    layer = tiny_layer(rng, wo=zero_q8(H, qw), wg=selector(inter, H, lambda r: r % H),
+                       wu=selector(inter, H, lambda r: r % H),
+                       wd=selector(H, inter, lambda r: r))
+    x = rng.standard_normal(H)
+    kc0 = rng.standard_normal((4, 2 * hd))
+    xo, acts, _, _ = _tiny_run(orc, layer, x, 1, kc0, kc0)
+    xn2 = np_rms(x, layer["ffn_norm"], TINY["eps"])
+    assert np.allclose(xo, x + np_silu_mul(xn2, xn2), rtol=1e-14, atol=1e-15)
+    assert np.allclose(acts["h"][:H], np_silu_mul(xn2, xn2), rtol=1e-14, atol=1e-15)
+
+
+def pin_decode_step_head(orc):
+    """Two layers with zero o and down projections leave x unchanged, so the
+    step's logits are the lm_head applied to out_norm(x) (dense numpy product)
+    and its token is their argmax."""
+    rng = np.random.default_rng(23)
+    H, hd, inter = TINY["hidden"], TINY["head_dim"], TINY["inter"]
+    layers = [tiny_layer(rng, wo=zero_q8(H, 4 * hd), wd=zero_q8(H, inter)) for _ in range(2)]
+    vocab = 50
+    lm = gen.weights(vocab, H, seed=5, index=1)
+    model = dict(dims=dict(TINY, vocab=vocab), layers=layers,
+                 out_norm=rng.uniform(0.5, 1.5, H), lm_head=lm)
+    x = rng.standard_normal(H)
+    kcs = [rng.standard_normal((4, 2 * hd)) for _ in range(2)]
+    vcs = [rng.standard_normal((4, 2 * hd)) for _ in range(2)]
+    r = orc.decode_step(model, x, 2, kcs, vcs)
+    assert np.array_equal(r["x"], x)
+    xf = np_rms(x, model["out_norm"], TINY["eps"])
+    assert np.allclose(r["xf"], xf, rtol=1e-14, atol=0)
+    ref = dense_dequant(lm, H) @ xf
+    assert np.allclose(r["logits"], ref, rtol=1e-12, atol=1e-14)
+    assert r["token"] == int(np.argmax(ref))
+
+
 ALL_PINS = [
     pin_f16_golden,
     pin_f16_exhaustive,
@@ -432,4 +715,12 @@ ALL_PINS = [
     pin_q8x_exact_on_grid,
     pin_q8x_quantization_bound,
     pin_q8x_tolerance_hand_case,
+    pin_rms_norm_closed_forms,
+    pin_rope_closed_forms,
+    pin_attention_closed_forms,
+    pin_silu_closed_forms,
+    pin_matvec_f64_is_matvec,
+    pin_decode_layer_attention_branch,
+    pin_decode_layer_mlp_branch,
+    pin_decode_step_head,
 ]

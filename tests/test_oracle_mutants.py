@@ -64,6 +64,53 @@ MUTANTS = [
      "(int64_t)q[32 * b + j]", "(int64_t)(uint8_t)q[32 * b + j]"),
     ("int8-activation tolerance uses signed products",
      "iabs += prod < 0 ? -prod : prod;", "iabs += prod;"),
+    ("rms eps outside the root",
+     "sqrt(ss / (double)dim + eps)", "(sqrt(ss / (double)dim) + eps)"),
+    ("rms mean over dim - 1",
+     "ss / (double)dim", "ss / (double)(dim - 1)"),
+    ("rms weight dropped",
+     "out[r * dim + i] = xr[i] * inv * w[i];", "out[r * dim + i] = xr[i] * inv;"),
+    ("rope rotates the wrong way",
+     "xh[i] = a * c - b * s;", "xh[i] = a * c + b * s;"),
+    ("rope second element sign",
+     "xh[i + half] = a * s + b * c;", "xh[i + half] = b * c - a * s;"),
+    ("rope frequency exponent over head_dim",
+     "(float)i / (float)half", "(float)i / (float)(2 * half)"),
+    ("rope pairs adjacent elements",
+     "const double a = xh[i], b = xh[i + half];", "const double a = xh[i], b = xh[(i + 1) % half];"),
+    ("attention without the scale",
+     "sc[t] = d * scale;", "sc[t] = d;"),
+    ("attention scaled by head_dim",
+     "1.0 / sqrt((double)head_dim)", "1.0 / (double)head_dim"),
+    ("attention kv head by modulo",
+     "(h / kv_group) * head_dim", "(h % kv_group) * head_dim"),
+    ("attention without the max",
+     "sc[t] = exp(sc[t] - mx);", "sc[t] = exp(sc[t]);"),
+    ("attention not normalised",
+     "for (int64_t t = 0; t < seq; t++) sc[t] /= sum;", ""),
+    ("attention over pos rows",
+     "a->attn, 0, pos + 1,", "a->attn, 0, pos,"),
+    ("silu of the negated gate",
+     "exp(-g[i])", "exp(g[i])"),
+    ("silu without the up factor",
+     "(1.0 + exp(-g[i])) * u[i];", "(1.0 + exp(-g[i]));"),
+    ("attention residual replaces x",
+     "x[i] += a->attn_out[i];", "x[i] = a->attn_out[i];"),
+    ("mlp residual dropped",
+     "x[i] += a->ffn_out[i];", "x[i] += 0.0 * a->ffn_out[i];"),
+    ("ffn norm with the attention weight",
+     "L->ffn_norm, a->xn2", "L->attn_norm, a->xn2"),
+    ("k norm with the q weight",
+     "L->k_norm, a->k", "L->q_norm, a->k"),
+    ("rope skipped on k",
+     "q8o_rope(a->k, dm->n_kv_heads, hd, pos, dm->theta);", ""),
+    ("value cache gets the key",
+     "vc[pos * kvw + i] = a->v[i];", "vc[pos * kvw + i] = a->k[i];"),
+    ("mlp reads the attention norm output",
+     "q8o_matvec_f64(L->wg, a->xn2,", "q8o_matvec_f64(L->wg, a->xn,"),
+    ("f64 matvec drops the scale",
+     "double t = scale * (double)(int8_t)blk[2 + j] * x[32 * b + j];",
+     "double t = (double)(int8_t)blk[2 + j] * x[32 * b + j];"),
 ]
 
 
