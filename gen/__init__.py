@@ -131,3 +131,56 @@ def activations(m: int, n: int, seed: int = 0, index: int = 0) -> np.ndarray:
     for r in range(m):
         out[r] = normals(stream_key(seed, ROLE_X, index, r), 0, n)
     return out
+
+
+# ---- a whole synthetic decoder ------------------------------------------------
+
+ROLE_MODEL = 3  # the decode model's weights, norms, caches and input row
+
+# Qwen3-0.6B's shapes (the model the inferno.rs page decodes; its eps and
+# RoPE base are the ones that model's configuration states).
+QWEN3_DIMS = dict(n_layers=N_LAYERS, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
+                  inter=3072, vocab=151936, eps=1e-6, theta=1e6)
+
+DECODE_WEIGHTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def decode_weight_shapes(dims: dict) -> dict:
+    """(n_in, p_out) of each projection of a layer."""
+    H, hd, inter = dims["hidden"], dims["head_dim"], dims["inter"]
+    qw, kvw = dims["n_heads"] * hd, dims["n_kv_heads"] * hd
+    return dict(wq=(H, qw), wk=(H, kvw), wv=(H, kvw), wo=(qw, H), w_gate=(H, inter),
+                w_up=(H, inter), w_down=(inter, H))
+
+
+def decode_model(dims: dict, cache_rows: int, seed: int = 0) -> dict:
+    """Seeded synthetic decoder of the given shapes: per layer the seven Q8_0
+    projections (generator weights), norm weights 1 + N(0, 0.1^2), a key
+    cache of N(0, 1) rows and a value cache of N(0, 0.4^2) rows
+    ([cache_rows, n_kv*head_dim], standing in for earlier tokens); the final
+    norm, the lm_head, and an N(0, 1) input row x_in."""
+    H, hd = dims["hidden"], dims["head_dim"]
+    kvw = dims["n_kv_heads"] * hd
+    shapes = decode_weight_shapes(dims)
+
+    def nrm(index, count, sd=1.0, mean=0.0):
+        v = normals(stream_key(seed, ROLE_MODEL, index), 0, count)
+        return (mean + np.float32(sd) * v).astype(np.float32)
+    layers = []
+    for l in range(dims["n_layers"]):
+        base = 64 * (l + 1)
+        L = {}
+        for j, name in enumerate(DECODE_WEIGHTS):
+            n, p = shapes[name]
+            L[name] = weights(p, n, seed=seed, index=base + j)
+        L["attn_norm"] = nrm(base + 10, H, 0.1, 1.0)
+        L["ffn_norm"] = nrm(base + 11, H, 0.1, 1.0)
+        L["q_norm"] = nrm(base + 12, hd, 0.1, 1.0)
+        L["k_norm"] = nrm(base + 13, hd, 0.1, 1.0)
+        L["k_cache"] = nrm(base + 14, cache_rows * kvw).reshape(cache_rows, kvw)
+        L["v_cache"] = nrm(base + 15, cache_rows * kvw, 0.4).reshape(cache_rows, kvw)
+        layers.append(L)
+    return dict(dims=dict(dims, cache_rows=cache_rows), layers=layers,
+                out_norm=nrm(1, H, 0.1, 1.0),
+                lm_head=weights(dims["vocab"], H, seed=seed, index=2),
+                x_in=nrm(3, H))

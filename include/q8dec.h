@@ -17,6 +17,8 @@
  *   of the largest logit, ties to the lowest index, so only four bytes per
  *   row leave the device.  NaN logits never win; -0 and +0 are equal; a row
  *   whose logits are all NaN yields -1.
+ * The whole decode step (q8_decode_graph_build, below) adds the layer's
+ *   other operations: norms, RoPE, the KV append, attention, SwiGLU.
  * The step (sections "One command buffer" and "The seam"): the 197 matvecs
  *   of one decode step (7 projections x 28 layers, then the lm_head and its
  *   argmax) are recorded once and submitted once, and one int32 comes back
@@ -223,6 +225,82 @@ int q8_step_graph_info(const q8_step_graph *g, int32_t *kernel_nodes,
 
 /* Destroys the graph and its workspace; the handle becomes invalid. */
 int q8_step_graph_destroy(q8_step_graph *g);
+
+/* ---- the whole decode step ------------------------------------------------
+ * inferno.rs "IV.4", "One command buffer": per layer, rms_norm_row ->
+ * q, k, v projections -> QK-norm (rms_norm_row per head) -> rope_row on q
+ * and k -> append_kv at row pos -> attention_decode over rows 0..pos ->
+ * o projection -> add_inplace into x -> rms_norm_row -> gate, up ->
+ * silu_hadamard -> down projection -> add_inplace; then the final norm, the
+ * lm_head and argmax_row ("Eight kernels" defines each operation).  The
+ * pages encode 18 dispatches per layer; here a layer is 5 kernel nodes (the
+ * q/k/v matvecs; the attention with the QK-norm, RoPE and append folded in;
+ * the o matvec whose last workgroup adds into x and norms; gate/up whose
+ * last workgroup applies SwiGLU; down, adding into x and norming for the
+ * next layer), plus one norm node before the first layer and the fused
+ * lm_head argmax: 5 * n_layers + 2 nodes.  Everything is binary32. */
+
+#define Q8_GRAPH_DECODE 4  /* mode of graphs from q8_decode_graph_build */
+
+/* One layer's resident weights (device pointers, caller-owned). */
+typedef struct {
+  const void *wq, *wk, *wv, *wo;        /* Q8_0 [out][in/32 blocks]: q [n_heads*128][hidden],
+                                           k, v [n_kv_heads*128][hidden], o [hidden][n_heads*128] */
+  const void *w_gate, *w_up, *w_down;   /* Q8_0: gate, up [inter][hidden], down [hidden][inter] */
+  const float *attn_norm, *ffn_norm;    /* float32 [hidden] */
+  const float *q_norm, *k_norm;         /* float32 [128], the per-head QK-norm weights */
+  float *k_cache, *v_cache;             /* float32 [cache_rows][n_kv_heads*128]: row t is token t's
+                                           key (after QK-norm and RoPE) and value */
+} q8_decode_layer;
+
+/* The model: shapes (head_dim must be 128; n_heads a multiple of n_kv_heads,
+ * at most 4 query heads per key/value head; hidden <= 4096; hidden, inter
+ * multiples of 32; 1 <= cache_rows <= 65536), eps and theta, a HOST array
+ * of n_layers layers, and the final norm and lm_head (device). */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, cache_rows;
+  float eps, theta;
+  const q8_decode_layer *layers;
+  const float *out_norm;                /* float32 [hidden] */
+  const void *lm_head;                  /* Q8_0 [vocab][hidden/32 blocks] */
+} q8_decode_model;
+
+/* The step's activations: device buffers owned by the caller, each sized
+ * for its role (float32).  The caller writes x_in (the token's embedding
+ * row, inferno.rs "The decoder: kernels and helpers", embed_row) and *pos
+ * (the token's position; cache rows 0..pos-1 hold the earlier tokens) before
+ * each launch.  After a launch every buffer holds the last layer's values;
+ * the step reads x_in and writes the rest, so a launch can be repeated. */
+typedef struct {
+  const float *x_in;                    /* [hidden] */
+  const int32_t *pos;                   /* int32 [1] */
+  float *x;                             /* [hidden] the residual stream */
+  float *xn;                            /* [hidden] attention-norm output (q/k/v input) */
+  float *q, *k, *v;                     /* [n_heads*128], [n_kv*128], [n_kv*128]: projections,
+                                           before QK-norm and RoPE */
+  float *attn;                          /* [n_heads*128] attention output */
+  float *attn_out;                      /* [hidden] o projection */
+  float *xn2;                           /* [hidden] ffn-norm output */
+  float *gate, *up, *h;                 /* [inter] projections and their SwiGLU */
+  float *ffn_out;                       /* [hidden] down projection */
+  float *xf;                            /* [hidden] final-norm output (lm_head input) */
+  float *logits;                        /* [vocab], or NULL: logits not stored */
+  int32_t *token;                       /* int32 [1]: the argmax of the logits */
+} q8_decode_buffers;
+
+/* Records the whole decode step as one hipGraph (mode Q8_GRAPH_DECODE) that
+ * q8_step_graph_launch / _launch_kernel / _info / _destroy take.  host_token
+ * (pinned host memory, or NULL) also receives the token, stored by the
+ * kernel.  A pos outside [0, cache_rows) writes no cache row and makes the
+ * attention output NaN, so the token is -1.  Buffers and weights are baked
+ * in (resident state: nothing is allocated or uploaded per step); the graph
+ * owns a workspace of (n_heads * ceil(cache_rows/64) * 528 + small) bytes.
+ * Two launches of one graph must not overlap.  Errors: Q8_ERR_NULL for a
+ * missing pointer, Q8_ERR_SHAPE for shapes outside the limits above,
+ * Q8_ERR_ALIGN for weights or activation buffers not 16-byte aligned,
+ * Q8_ERR_HIP for an unpinned host_token. */
+int q8_decode_graph_build(const q8_decode_model *model, const q8_decode_buffers *buf,
+                          int32_t *host_token, void *stream, q8_step_graph **out);
 
 #ifdef __cplusplus
 }

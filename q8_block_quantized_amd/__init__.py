@@ -23,6 +23,7 @@ Q8_GRAPH_CHAIN = 0
 Q8_GRAPH_PERSISTENT = 1
 Q8_GRAPH_PERSISTENT_I8X = 2
 Q8_GRAPH_LEVELS = 3
+Q8_GRAPH_DECODE = 4
 BLOCK = 32
 BLOCK_BYTES = 34
 
@@ -41,6 +42,32 @@ class MatvecDesc(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("n", ctypes.c_int32), ("p", ctypes.c_int32)]
+
+
+LAYER_FIELDS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "attn_norm",
+                "ffn_norm", "q_norm", "k_norm", "k_cache", "v_cache")
+BUFFER_FIELDS = ("x_in", "pos", "x", "xn", "q", "k", "v", "attn", "attn_out", "xn2",
+                 "gate", "up", "h", "ffn_out", "xf", "logits", "token")
+
+
+class DecodeLayer(ctypes.Structure):
+    """q8_decode_layer of include/q8dec.h."""
+    _fields_ = [(f, ctypes.c_void_p) for f in LAYER_FIELDS]
+
+
+class DecodeModel(ctypes.Structure):
+    """q8_decode_model of include/q8dec.h."""
+    _fields_ = [(f, ctypes.c_int32) for f in
+                ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter",
+                 "vocab", "cache_rows")] + [
+                ("eps", ctypes.c_float), ("theta", ctypes.c_float),
+                ("layers", ctypes.c_void_p), ("out_norm", ctypes.c_void_p),
+                ("lm_head", ctypes.c_void_p)]
+
+
+class DecodeBuffers(ctypes.Structure):
+    """q8_decode_buffers of include/q8dec.h."""
+    _fields_ = [(f, ctypes.c_void_p) for f in BUFFER_FIELDS]
 
 
 _lib = None
@@ -78,6 +105,9 @@ def load(path: str = LIB_PATH):
         "q8_step_graph_launch_kernel": (ctypes.c_int, [vp, vp]),
         "q8_step_graph_info": (ctypes.c_int, [vp, pi32, pi32]),
         "q8_step_graph_destroy": (ctypes.c_int, [vp]),
+        "q8_decode_graph_build": (ctypes.c_int, [ctypes.POINTER(DecodeModel),
+                                                 ctypes.POINTER(DecodeBuffers), vp, vp,
+                                                 ctypes.POINTER(vp)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -331,3 +361,101 @@ class StepGraph:
             self.close()
         except Exception:
             pass
+
+
+# ---- the whole decode step --------------------------------------------------
+
+def decode_buffer_sizes(dims: dict) -> dict:
+    """Element counts of every q8_decode_buffers entry for the given shapes."""
+    H, hd, inter = dims["hidden"], dims["head_dim"], dims["inter"]
+    qw, kvw = dims["n_heads"] * hd, dims["n_kv_heads"] * hd
+    return dict(x_in=H, pos=1, x=H, xn=H, q=qw, k=kvw, v=kvw, attn=qw, attn_out=H, xn2=H,
+                gate=inter, up=inter, h=inter, ffn_out=H, xf=H, logits=dims["vocab"],
+                token=1)
+
+
+def decode_buffers(dims: dict, device, logits: bool = True) -> dict:
+    """Allocates (with torch) the activation buffers of one decode step."""
+    torch = _torch()
+    out = {}
+    for k, n in decode_buffer_sizes(dims).items():
+        if k == "logits" and not logits:
+            out[k] = None
+            continue
+        dt = torch.int32 if k in ("pos", "token") else torch.float32
+        out[k] = torch.zeros(n, dtype=dt, device=device)
+    return out
+
+
+class DecodeGraph(StepGraph):
+    """The whole decode step (q8_decode_graph_build), launched like a StepGraph.
+
+    ``dims``: n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab,
+    cache_rows, eps, theta.  ``layers``: one dict per layer with the tensors
+    of LAYER_FIELDS (uint8 Q8_0 weights, float32 norms and caches).
+    ``bufs``: the tensors of BUFFER_FIELDS (decode_buffers makes them;
+    logits may be None).  Every tensor must stay alive while the graph
+    exists; this object keeps references to them.
+    """
+
+    def __init__(self, dims: dict, layers, out_norm, lm_head, bufs: dict,
+                 host_token=None, device=None):
+        torch = _torch()
+        dev = device if device is not None else bufs["x"].device
+        H, hd = int(dims["hidden"]), int(dims["head_dim"])
+        qw, kvw = int(dims["n_heads"]) * hd, int(dims["n_kv_heads"]) * hd
+        inter, rows = int(dims["inter"]), int(dims["cache_rows"])
+        if len(layers) != int(dims["n_layers"]):
+            raise ValueError("one layer dict per layer")
+        wshape = dict(wq=(H, qw), wk=(H, kvw), wv=(H, kvw), wo=(qw, H), w_gate=(H, inter),
+                      w_up=(H, inter), w_down=(inter, H))
+        fsize = dict(attn_norm=H, ffn_norm=H, q_norm=hd, k_norm=hd, k_cache=rows * kvw,
+                     v_cache=rows * kvw)
+        self._keep = [layers, out_norm, lm_head, bufs, host_token]
+        arr = (DecodeLayer * len(layers))()
+        for i, L in enumerate(layers):
+            vals = []
+            for f in LAYER_FIELDS:
+                t = L[f]
+                if f in wshape:
+                    _check_w(t, *wshape[f], dev)
+                else:
+                    _need(t, torch.float32, f"layers[{i}].{f}", dev)
+                    if t.numel() != fsize[f]:
+                        raise ValueError(f"layers[{i}].{f} must hold {fsize[f]} floats")
+                vals.append(t.data_ptr())
+            arr[i] = DecodeLayer(*vals)
+        _need(out_norm, torch.float32, "out_norm", dev)
+        _check_w(lm_head, H, int(dims["vocab"]), dev)
+        sizes = decode_buffer_sizes(dims)
+        bvals = []
+        for f in BUFFER_FIELDS:
+            t = bufs.get(f)
+            if t is None and f == "logits":
+                bvals.append(None)
+                continue
+            _need(t, torch.int32 if f in ("pos", "token") else torch.float32, f, dev)
+            if t.numel() != sizes[f]:
+                raise ValueError(f"bufs[{f}] must hold {sizes[f]} elements")
+            bvals.append(t.data_ptr())
+        if host_token is not None:
+            if host_token.dtype != torch.int32 or host_token.device.type != "cpu" \
+                    or not host_token.is_pinned() or host_token.numel() < 1:
+                raise ValueError("host_token must be a pinned int32 CPU tensor")
+        model = DecodeModel(int(dims["n_layers"]), H, int(dims["n_heads"]),
+                            int(dims["n_kv_heads"]), hd, inter, int(dims["vocab"]), rows,
+                            float(dims["eps"]), float(dims["theta"]),
+                            ctypes.addressof(arr), out_norm.data_ptr(), lm_head.data_ptr())
+        cb = DecodeBuffers(*bvals)
+        self._keep += [arr, model, cb]
+        self.host_idx = host_token
+        self.m = 1
+        self.mode = Q8_GRAPH_DECODE
+        self.dims = dict(dims)
+        handle = ctypes.c_void_p(None)
+        hptr = host_token.data_ptr() if host_token is not None else None
+        with torch.cuda.device(dev):
+            _check(load().q8_decode_graph_build(ctypes.byref(model), ctypes.byref(cb), hptr,
+                                                _stream(None, dev), ctypes.byref(handle)))
+        self._h = handle
+        self.device = dev

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "q8dec_api.hip"),
-           os.path.join(CSRC, "q8dec_kernels.hip")]
+           os.path.join(CSRC, "q8dec_kernels.hip"),
+           os.path.join(CSRC, "q8dec_decode.hip")]
 LIB = os.path.join(HERE, "libq8dec.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

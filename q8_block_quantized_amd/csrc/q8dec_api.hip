@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -116,13 +117,30 @@ constexpr uint32_t kGraphMagic = 0x51384447u;  // "Q8DG"
 
 // One persistent kernel launch of a step: the descriptor table and
 // workgroup ranges of its descriptors (device memory) and its shape.
+// Decode graphs add attention and norm nodes (kind).
+constexpr int kStepNode = 0, kAttnNode = 1, kNormNode = 2;
 struct SegmentLaunch {
   const q8::StepDesc *table;
   const q8::WgGroup *groups;
   int32_t count, group_size, grid;
   size_t lds;
   bool all_staged;
+  int kind = kStepNode;
+  const q8::Epilogue *epi = nullptr;
+  q8::AttnArgs attn{};
+  const float *nx = nullptr, *nw = nullptr;
+  float *nout = nullptr, *ncopy = nullptr;
+  int32_t ndim = 0;
+  float neps = 0.f;
 };
+
+hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
+  if (L.kind == kAttnNode) return q8::launch_attention(L.attn, s);
+  if (L.kind == kNormNode)
+    return q8::launch_rms_norm(L.nx, L.nw, L.nout, L.ncopy, 1, L.ndim, L.neps, s);
+  return q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
+                         L.all_staged, s, i8x, L.epi);
+}
 
 struct q8_step_graph {
   uint32_t magic;
@@ -387,6 +405,51 @@ int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
 
 namespace {
 
+// Records what `record` enqueues into g's graph on a capture stream,
+// instantiates it and registers the handle in *out; releases g on failure.
+extern "C++" {
+template <class F>
+int capture_graph(q8_step_graph *g, q8_step_graph **out, F record) {
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    release_graph(g);
+    return hip_fail(e);
+  }
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  hipError_t le = hipSuccess;
+  if (e == hipSuccess) {
+    le = record(cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    g->graph = graph;
+  }
+  (void)hipStreamDestroy(cs);
+  if (le != hipSuccess || e != hipSuccess || !g->graph) {
+    hip_fail(le != hipSuccess ? le : e);
+    release_graph(g);
+    return Q8_ERR_GRAPH;
+  }
+  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hip_fail(e);
+    release_graph(g);
+    return Q8_ERR_GRAPH;
+  }
+  int st = count_nodes(g);
+  if (st) {
+    release_graph(g);
+    return st;
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_graphs.insert(g);
+  }
+  *out = g;
+  return Q8_OK;
+}
+}  // extern "C++"
+
 // Builds every form of step graph.  levels (Q8_GRAPH_LEVELS only) gives each
 // descriptor's dependency level; each run of equal levels becomes one
 // persistent kernel node, the nodes in level order.
@@ -519,16 +582,9 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
     }
   }
 
-  hipStream_t cs = nullptr;
-  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-  if (e != hipSuccess) {
-    release_graph(g);
-    return hip_fail(e);
-  }
-  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-  hipError_t le = hipSuccess;
-  if (e == hipSuccess) {
-    if (mode == Q8_GRAPH_CHAIN) {
+  if (mode == Q8_GRAPH_CHAIN) {
+    return capture_graph(g, out, [&](hipStream_t cs) {
+      hipError_t le = hipSuccess;
       int a = 0;
       for (int32_t i = 0; i < count && le == hipSuccess; i++) {
         const q8_matvec_desc &d = descs[i];
@@ -536,43 +592,259 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
         le = q8::launch_matvec((const uint8_t *)d.w, d.x, d.y, m, d.n, d.p,
                                slot, d.idx, cs);
       }
-    } else {
-      for (size_t i = 0; i < g->launches.size() && le == hipSuccess; i++) {
-        const SegmentLaunch &L = g->launches[i];
-        le = q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid,
-                             L.lds, L.all_staged, cs, i8x);
-      }
+      return le;
+    });
+  }
+  return capture_graph(g, out, [&](hipStream_t cs) {
+    hipError_t le = hipSuccess;
+    for (size_t i = 0; i < g->launches.size() && le == hipSuccess; i++)
+      le = run_segment(g->launches[i], m, i8x, cs);
+    return le;
+  });
+}
+
+bool ok16(const void *p) { return p && aligned(p, 16); }
+
+// The whole decode step: argument checks, then the plans, the workspace and
+// the node list (norm; per layer q/k/v, attention, o + add + norm, gate/up +
+// SwiGLU, down + add + norm; lm_head argmax), then the capture.
+int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t *host_token,
+                 q8_step_graph **out) {
+  if (!out) return Q8_ERR_NULL;
+  *out = nullptr;
+  if (!md || !bf) return Q8_ERR_NULL;
+  const q8_decode_model &M = *md;
+  const q8_decode_buffers &B = *bf;
+  const int64_t qw = (int64_t)M.n_heads * M.head_dim, kvw = (int64_t)M.n_kv_heads * M.head_dim;
+  if (M.n_layers < 1 || M.n_layers > Q8_MAX_DESCS / 8) return Q8_ERR_SHAPE;
+  if (M.head_dim != q8::kAttnHeadDim) return Q8_ERR_SHAPE;
+  if (M.n_kv_heads < 1 || M.n_heads < M.n_kv_heads || M.n_heads % M.n_kv_heads ||
+      M.n_heads / M.n_kv_heads > q8::kAttnMaxGroup || qw > Q8_MAX_N || kvw > Q8_MAX_N)
+    return Q8_ERR_SHAPE;
+  if (M.hidden < Q8_BLOCK || M.hidden > q8::kNormMaxDim || M.hidden % Q8_BLOCK)
+    return Q8_ERR_SHAPE;
+  if (M.inter < Q8_BLOCK || M.inter > Q8_MAX_N || M.inter % Q8_BLOCK) return Q8_ERR_SHAPE;
+  if (M.vocab < 1 || M.cache_rows < 1 || M.cache_rows > 65536) return Q8_ERR_SHAPE;
+  if (!(M.eps >= 0.f) || !(M.eps < INFINITY) || !(M.theta > 0.f) || !(M.theta < INFINITY))
+    return Q8_ERR_SHAPE;
+  if (!M.layers || !M.out_norm || !M.lm_head) return Q8_ERR_NULL;
+  const void *need[] = {B.x_in, B.x, B.xn, B.q, B.k, B.v, B.attn, B.attn_out, B.xn2,
+                        B.gate, B.up, B.h, B.ffn_out, B.xf, M.out_norm, M.lm_head};
+  for (const void *p : need) {
+    if (!p) return Q8_ERR_NULL;
+    if (!aligned(p, 16)) return Q8_ERR_ALIGN;
+  }
+  if (!B.pos || !B.token) return Q8_ERR_NULL;
+  if (!aligned(B.pos, 4) || !aligned(B.token, 4)) return Q8_ERR_ALIGN;
+  if (B.logits && !aligned(B.logits, 16)) return Q8_ERR_ALIGN;
+  for (int32_t l = 0; l < M.n_layers; l++) {
+    const q8_decode_layer &L = M.layers[l];
+    const void *lp[] = {L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down, L.attn_norm,
+                        L.ffn_norm, L.q_norm, L.k_norm, L.k_cache, L.v_cache};
+    for (const void *p : lp) {
+      if (!p) return Q8_ERR_NULL;
+      if (!aligned(p, 16)) return Q8_ERR_ALIGN;
     }
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(cs, &graph);
-    g->graph = graph;
   }
-  (void)hipStreamDestroy(cs);
-  if (le != hipSuccess || e != hipSuccess || !g->graph) {
-    hip_fail(le != hipSuccess ? le : e);
-    release_graph(g);
-    return Q8_ERR_GRAPH;
+  if (host_token && !aligned(host_token, 4)) return Q8_ERR_ALIGN;
+  int dev = 0;
+  int st = ensure_device(&dev);
+  if (st) return st;
+  int32_t *host_dev = nullptr;
+  if (host_token) {
+    hipError_t he = hipHostGetDevicePointer((void **)&host_dev, host_token, 0);
+    if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
   }
-  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+
+  // the matvec levels: per layer q/k/v (0), o (1), gate/up (2), down (3); then the lm_head
+  const int H = M.hidden, QW = (int)qw, KVW = (int)kvw, I = M.inter;
+  auto mv = [](const void *w, const float *x, float *y, int32_t *idx, int n, int p) {
+    q8_matvec_desc d;
+    d.w = w;
+    d.x = x;
+    d.y = y;
+    d.idx = idx;
+    d.n = n;
+    d.p = p;
+    return d;
+  };
+  std::vector<std::vector<q8_matvec_desc>> lv;
+  for (int32_t l = 0; l < M.n_layers; l++) {
+    const q8_decode_layer &L = M.layers[l];
+    lv.push_back({mv(L.wq, B.xn, B.q, nullptr, H, QW), mv(L.wk, B.xn, B.k, nullptr, H, KVW),
+                  mv(L.wv, B.xn, B.v, nullptr, H, KVW)});
+    lv.push_back({mv(L.wo, B.attn, B.attn_out, nullptr, QW, H)});
+    lv.push_back({mv(L.w_gate, B.xn2, B.gate, nullptr, H, I), mv(L.w_up, B.xn2, B.up, nullptr, H, I)});
+    lv.push_back({mv(L.w_down, B.h, B.ffn_out, nullptr, I, H)});
+  }
+  lv.push_back({mv(M.lm_head, B.xf, B.logits, B.token, H, M.vocab)});
+  std::vector<q8::StepPlan> plans(lv.size());
+  for (size_t i = 0; i < lv.size(); i++) {
+    st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
+                       plans[i]);
+    if (st) return st;
+  }
+
+  q8_step_graph *g = new (std::nothrow) q8_step_graph();
+  if (!g) return Q8_ERR_GRAPH;
+  g->magic = kGraphMagic;
+  g->device = dev;
+  g->mode = Q8_GRAPH_DECODE;
+  g->m = 1;
+  g->i8x = false;
+
+  // workspace (16-byte aligned pieces): the lm_head argmax slot, the
+  // epilogues' arrival slot, the attention arrival slots, the epilogues,
+  // the RoPE frequencies, the attention partials, then each level's table
+  // and workgroup ranges
+  const int chunks = q8::attn_chunks(M.cache_rows);
+  size_t total = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = total;
+    total += (bytes + 255) & ~(size_t)255;
+    return off;
+  };
+  const size_t o_amax = take(sizeof(q8::ArgmaxSlot));
+  const size_t o_earr = take(sizeof(q8::ArgmaxSlot));
+  const size_t o_aarr = take(sizeof(q8::ArgmaxSlot) * (size_t)M.n_kv_heads);
+  const size_t o_epi = take(sizeof(q8::Epilogue) * 3 * (size_t)M.n_layers);
+  const size_t o_freq = take(sizeof(float) * q8::kAttnHeadDim / 2);
+  const size_t o_part = take(sizeof(float) * (size_t)M.n_heads * chunks * q8::kAttnPart);
+  std::vector<size_t> o_tab(plans.size()), o_grp(plans.size());
+  for (size_t i = 0; i < plans.size(); i++) {
+    o_tab[i] = take(plans[i].descs.size() * sizeof(q8::StepDesc));
+    o_grp[i] = take(plans[i].groups.size() * sizeof(q8::WgGroup));
+  }
+  hipError_t e = hipMalloc(&g->workspace, total);
+  if (e == hipSuccess) e = hipMemset(g->workspace, 0, total);
   if (e != hipSuccess) {
-    hip_fail(e);
     release_graph(g);
-    return Q8_ERR_GRAPH;
+    return hip_fail(e);
   }
-  st = count_nodes(g);
-  if (st) {
-    release_graph(g);
-    return st;
-  }
+  char *ws = (char *)g->workspace;
+  q8::ArgmaxSlot *amax = (q8::ArgmaxSlot *)(ws + o_amax);
+  q8::ArgmaxSlot *earr = (q8::ArgmaxSlot *)(ws + o_earr);
+  q8::Epilogue *epis = (q8::Epilogue *)(ws + o_epi);
   {
-    std::lock_guard<std::mutex> lock(g_mu);
-    g_graphs.insert(g);
+    q8::StepPlan &pl = plans.back();
+    q8::ArgmaxSlot hs;
+    std::memset(&hs, 0, sizeof(hs));
+    uint32_t nteams = 0;
+    for (int j = 0; j < q8::kArgmaxTeams; j++) {
+      hs.team[j].expected = pl.expected[0][j];
+      nteams += pl.expected[0][j] ? 1u : 0u;
+    }
+    hs.top.expected = nteams;
+    hs.host = host_dev;
+    pl.descs[0].slot = amax;
+    e = hipMemcpy(amax, &hs, sizeof(hs), hipMemcpyHostToDevice);
   }
-  *out = g;
-  return Q8_OK;
+  std::vector<q8::Epilogue> he(3 * (size_t)M.n_layers);
+  for (int32_t l = 0; l < M.n_layers && e == hipSuccess; l++) {
+    const q8_decode_layer &L = M.layers[l];
+    q8::Epilogue *E = &he[3 * (size_t)l];
+    std::memset(E, 0, 3 * sizeof(q8::Epilogue));
+    E[0].op = q8::kEpiAddNorm;  // after o: x += attn_out; xn2 = norm(x)
+    E[0].n = H;
+    E[0].eps = M.eps;
+    E[0].x = B.x;
+    E[0].r = B.attn_out;
+    E[0].g = L.ffn_norm;
+    E[0].out = B.xn2;
+    E[0].arrive = earr;
+    E[1].op = q8::kEpiSiluMul;  // after gate/up: h = silu(gate) * up
+    E[1].n = I;
+    E[1].r = B.up;
+    E[1].g = B.gate;
+    E[1].out = B.h;
+    E[1].arrive = earr;
+    const bool lastl = l + 1 == M.n_layers;
+    E[2].op = q8::kEpiAddNorm;  // after down: x += ffn_out; next layer's xn, or xf
+    E[2].n = H;
+    E[2].eps = M.eps;
+    E[2].x = B.x;
+    E[2].r = B.ffn_out;
+    E[2].g = lastl ? M.out_norm : M.layers[l + 1].attn_norm;
+    E[2].out = lastl ? B.xf : B.xn;
+    E[2].arrive = earr;
+  }
+  if (e == hipSuccess)
+    e = hipMemcpy(epis, he.data(), he.size() * sizeof(q8::Epilogue), hipMemcpyHostToDevice);
+  for (size_t i = 0; i < plans.size() && e == hipSuccess; i++) {
+    e = hipMemcpy(ws + o_tab[i], plans[i].descs.data(),
+                  plans[i].descs.size() * sizeof(q8::StepDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(ws + o_grp[i], plans[i].groups.data(),
+                    plans[i].groups.size() * sizeof(q8::WgGroup), hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = q8::launch_rope_freq(M.theta, (float *)(ws + o_freq), nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    release_graph(g);
+    return hip_fail(e);
+  }
+
+  auto step_node = [&](size_t i, const q8::Epilogue *epi) {
+    const q8::StepPlan &pl = plans[i];
+    SegmentLaunch L{(const q8::StepDesc *)(ws + o_tab[i]), (const q8::WgGroup *)(ws + o_grp[i]),
+                    (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged};
+    L.epi = epi;
+    g->launches.push_back(L);
+  };
+  {
+    SegmentLaunch L{nullptr, nullptr, 0, 0, 0, 0, true};
+    L.kind = kNormNode;
+    L.nx = B.x_in;
+    L.nw = M.layers[0].attn_norm;
+    L.nout = B.xn;
+    L.ncopy = B.x;
+    L.ndim = H;
+    L.neps = M.eps;
+    g->launches.push_back(L);
+  }
+  for (int32_t l = 0; l < M.n_layers; l++) {
+    const q8_decode_layer &Ly = M.layers[l];
+    step_node(4 * (size_t)l, nullptr);
+    SegmentLaunch A{nullptr, nullptr, 0, 0, 0, 0, true};
+    A.kind = kAttnNode;
+    A.attn.q = B.q;
+    A.attn.k = B.k;
+    A.attn.v = B.v;
+    A.attn.q_norm = Ly.q_norm;
+    A.attn.k_norm = Ly.k_norm;
+    A.attn.kc = Ly.k_cache;
+    A.attn.vc = Ly.v_cache;
+    A.attn.pos = B.pos;
+    A.attn.freq = (const float *)(ws + o_freq);
+    A.attn.out = B.attn;
+    A.attn.part = (float *)(ws + o_part);
+    A.attn.arrive = (q8::ArgmaxSlot *)(ws + o_aarr);
+    A.attn.n_heads = M.n_heads;
+    A.attn.n_kv = M.n_kv_heads;
+    A.attn.cache_rows = M.cache_rows;
+    A.attn.chunks = chunks;
+    A.attn.eps = M.eps;
+    g->launches.push_back(A);
+    step_node(4 * (size_t)l + 1, &epis[3 * (size_t)l]);
+    step_node(4 * (size_t)l + 2, &epis[3 * (size_t)l + 1]);
+    step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2]);
+  }
+  step_node(plans.size() - 1, nullptr);
+  return capture_graph(g, out, [&](hipStream_t cs) {
+    hipError_t le = hipSuccess;
+    for (size_t i = 0; i < g->launches.size() && le == hipSuccess; i++)
+      le = run_segment(g->launches[i], 1, false, cs);
+    return le;
+  });
 }
 
 }  // namespace
+
+int q8_decode_graph_build(const q8_decode_model *model, const q8_decode_buffers *buf,
+                          int32_t *host_token, void *stream, q8_step_graph **out) {
+  (void)stream;
+  return build_decode(model, buf, host_token, out);
+}
 
 int q8_step_graph_build(const q8_matvec_desc *descs, int32_t count, int32_t m,
                         int32_t *host_idx, int32_t mode, void *stream,
@@ -602,11 +874,8 @@ int q8_step_graph_launch_kernel(q8_step_graph *g, void *stream) {
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e);
   if (cur != g->device && (e = hipSetDevice(g->device)) != hipSuccess) return hip_fail(e);
-  for (size_t i = 0; i < g->launches.size() && e == hipSuccess; i++) {
-    const SegmentLaunch &L = g->launches[i];
-    e = q8::launch_step(L.table, L.count, L.groups, L.group_size, g->m, L.grid, L.lds,
-                        L.all_staged, (hipStream_t)stream, g->i8x);
-  }
+  for (size_t i = 0; i < g->launches.size() && e == hipSuccess; i++)
+    e = run_segment(g->launches[i], g->m, g->i8x, (hipStream_t)stream);
   if (cur != g->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }

@@ -84,9 +84,13 @@ hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
 // `descs` table (device memory, `count` entries in tile order); workgroup g
 // belongs to groups[g / group_size] (device memory).  `lds` bytes of dynamic
 // LDS: step_lds_bytes of the widest matvec.
+// `epi` (device memory, or NULL): work the last workgroup to finish runs
+// once every tile of the launch is written (see Epilogue).
+struct Epilogue;
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
-                       bool all_staged, hipStream_t s, bool i8x = false);
+                       bool all_staged, hipStream_t s, bool i8x = false,
+                       const Epilogue *epi = nullptr);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
@@ -123,6 +127,65 @@ constexpr int kStepGroupSizeBatched = 2;
 
 // Host stub of one kernel, used to check that the code object loads.
 const void *probe_kernel();
+
+// ---- the rest of the decode step (norms, attention, SwiGLU) -------------
+
+// Element-wise work a persistent step launch finishes with, run by the last
+// workgroup to arrive (every workgroup arrives once, after its tiles):
+//   kEpiAddNorm: x += r over n values (r may be NULL: no add), then
+//                out = x / sqrt(mean(x^2) + eps) * g   (rms_norm_row);
+//   kEpiSiluMul: out = g / (1 + e^-g) * r over n values (silu_hadamard,
+//                g the gate, r the up projection).
+// `arrive` is a zeroed ArgmaxSlot used only for its counters.
+enum EpiOp : int32_t { kEpiNone = 0, kEpiAddNorm = 1, kEpiSiluMul = 2 };
+struct Epilogue {
+  int32_t op, n;
+  float eps;
+  int32_t pad0;
+  float *x;
+  const float *r;
+  const float *g;
+  float *out;
+  ArgmaxSlot *arrive;
+  int64_t pad1;
+};
+static_assert(sizeof(Epilogue) == 64, "epilogue layout");
+
+constexpr int kNormMaxDim = 4096;   // widest row a norm workgroup takes
+constexpr int kSiluMaxN = 65536;    // widest SwiGLU epilogue
+constexpr int kAttnHeadDim = 128;   // the attention kernel's head width
+constexpr int kAttnChunk = 64;      // cached rows per attention workgroup
+constexpr int kAttnPart = 132;      // floats per (head, chunk) partial: m, l, pad, acc[128]
+constexpr int kAttnMaxGroup = 4;    // query heads per key/value head
+
+// attention_decode for one token (with the QK-norm, the RoPE of q and k and
+// the append of k, v at row *pos folded in).  Grid n_kv * chunks workgroups,
+// chunks = attn_chunks(cache_rows); workgroup (g, c) takes cached rows
+// [64c, 64c + 64) of key/value head g and writes a partial softmax; the last
+// workgroup of head g to finish merges them into out.
+struct AttnArgs {
+  const float *q, *k, *v;        // projections: [n_heads*128], [n_kv*128] x 2
+  const float *q_norm, *k_norm;  // [128]
+  float *kc, *vc;                // [cache_rows][n_kv*128]
+  const int32_t *pos;            // device int32
+  const float *freq;             // [64] RoPE frequencies (rope_freq)
+  float *out;                    // [n_heads*128]
+  float *part;                   // [n_heads][chunks][kAttnPart]
+  ArgmaxSlot *arrive;            // [n_kv], zeroed (counters only)
+  int32_t n_heads, n_kv, cache_rows, chunks;
+  float eps;
+};
+int attn_chunks(int cache_rows);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+
+// rms_norm_row over `rows` rows of dim <= kNormMaxDim values; copy (or NULL)
+// also receives x.
+hipError_t launch_rms_norm(const float *x, const float *w, float *out, float *copy,
+                           int rows, int dim, float eps, hipStream_t s);
+
+// freq[i] = 1 / theta^(i / 64) for i < 64, the power rounded to binary32
+// from binary64 and the quotient in binary32 (the RoPE frequencies).
+hipError_t launch_rope_freq(float theta, float *freq, hipStream_t s);
 
 }  // namespace q8
 

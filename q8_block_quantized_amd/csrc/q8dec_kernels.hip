@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "q8dec_decode_dev.h"
 #include "q8dec_internal.h"
 
 namespace q8 {
@@ -1240,15 +1241,22 @@ mv_kernel(StepDesc d, int32_t m) {
 // The decode step: every tile of every descriptor of a device-side table
 // (count entries in tile order), with no ordering between descriptors.
 // Workgroups form groups; a group interleaves its contiguous tile range.
+// epi (or NULL): element-wise work that the last workgroup to finish runs
+// once every tile is written.
 template <bool M1, bool ANY, bool I8X>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
-            const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
+            const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
+            const Epilogue *__restrict__ epi) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
   run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
+  if (epi) {
+    __syncthreads();  // every wave is done with the tile buffer
+    dec::run_epilogue(epi, blockIdx.x, gridDim.x, lds);
+  }
 }
 
 // ---- argmax over f32 logits ---------------------------------------------
@@ -1417,30 +1425,30 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
-                       bool all_staged, hipStream_t s, bool i8x) {
+                       bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi) {
   if (i8x) {
     if (m == 1)
       hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
     else
       hipLaunchKernelGGL((step_kernel<false, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
     return hipGetLastError();
   }
   if (m == 1) {
     if (all_staged)
       hipLaunchKernelGGL((step_kernel<true, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
     else
       hipLaunchKernelGGL((step_kernel<true, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
   } else {
     if (all_staged)
       hipLaunchKernelGGL((step_kernel<false, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
     else
       hipLaunchKernelGGL((step_kernel<false, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m);
+                         s, descs, count, groups, group_size, m, epi);
   }
   return hipGetLastError();
 }

@@ -190,3 +190,64 @@ def test_no_device_is_reported():
     if "SKIP" in out.stdout:
         pytest.skip("a device stayed visible")
     assert f"CODES {[NODEV] * 5}" in out.stdout, out.stdout
+
+
+def _decode_args(n_layers=1, layer_over=None, buf_over=None, **over):
+    """A decode model and buffers of fake aligned device addresses."""
+    keep = []
+    layers = (q8.DecodeLayer * n_layers)()
+    for i in range(n_layers):
+        vals = {f: 0x100000 * (j + 1) for j, f in enumerate(q8.LAYER_FIELDS)}
+        vals.update(layer_over or {})
+        layers[i] = q8.DecodeLayer(*[vals[f] for f in q8.LAYER_FIELDS])
+    keep.append(layers)
+    dims = dict(n_layers=n_layers, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
+                inter=3072, vocab=151936, cache_rows=1024, eps=1e-6, theta=1e6)
+    dims.update(over)
+    model = q8.DecodeModel(dims["n_layers"], dims["hidden"], dims["n_heads"],
+                           dims["n_kv_heads"], dims["head_dim"], dims["inter"], dims["vocab"],
+                           dims["cache_rows"], dims["eps"], dims["theta"],
+                           ctypes.addressof(layers), 0x7000000, 0x7100000)
+    bvals = {f: 0x8000000 + 0x100000 * j for j, f in enumerate(q8.BUFFER_FIELDS)}
+    bvals.update(buf_over or {})
+    bufs = q8.DecodeBuffers(*[bvals[f] for f in q8.BUFFER_FIELDS])
+    keep += [model, bufs]
+    return model, bufs, keep
+
+
+def test_decode_graph_refusals(lib):
+    """The whole-step builder checks shapes, pointers and alignment before any
+    GPU work."""
+    h = ctypes.c_void_p(None)
+    b = lib.q8_decode_graph_build
+
+    def call(**kw):
+        model, bufs, keep = _decode_args(**kw)
+        return b(ctypes.byref(model), ctypes.byref(bufs), None, None, ctypes.byref(h))
+    model, bufs, keep = _decode_args()
+    assert b(None, ctypes.byref(bufs), None, None, ctypes.byref(h)) == NULL
+    assert b(ctypes.byref(model), None, None, None, ctypes.byref(h)) == NULL
+    assert b(ctypes.byref(model), ctypes.byref(bufs), None, None, None) == NULL
+    assert call(head_dim=64) == SHAPE
+    assert call(n_kv_heads=3) == SHAPE          # 16 heads not a multiple of 3
+    assert call(n_heads=40, n_kv_heads=8) == SHAPE  # 5 query heads per kv head
+    assert call(n_kv_heads=0) == SHAPE
+    assert call(hidden=8192) == SHAPE
+    assert call(hidden=1000) == SHAPE
+    assert call(inter=100) == SHAPE
+    assert call(vocab=0) == SHAPE
+    assert call(cache_rows=0) == SHAPE
+    assert call(cache_rows=65537) == SHAPE
+    assert call(n_layers=0) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(theta=0.0) == SHAPE
+    assert call(layer_over=dict(wq=0)) == NULL
+    assert call(layer_over=dict(k_cache=0)) == NULL
+    assert call(layer_over=dict(wo=0x100004)) == ALIGN
+    assert call(buf_over=dict(xn=0)) == NULL
+    assert call(buf_over=dict(pos=0)) == NULL
+    assert call(buf_over=dict(token=0)) == NULL
+    assert call(buf_over=dict(q=0x8000008)) == ALIGN
+    assert call(buf_over=dict(logits=0x8000004)) == ALIGN
+    assert h.value is None
