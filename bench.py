@@ -39,7 +39,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ["q8dec_api.hip", "q8dec_internal.h", "q8dec_kernels.hip"]
+KERNEL_SOURCES = ["q8dec_api.hip", "q8dec_internal.h", "q8dec_kernels.hip",
+                  "q8dec_decode_dev.h"]
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_kernel_decode_step_hbm_bytes.md")
 
 
@@ -193,6 +194,50 @@ def cpu_baseline(sets, m_host, threads_req: int, budget_s: float):
     return statistics.median(times), used, worst, ok_idx
 
 
+def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
+                seed: int = 0) -> dict:
+    """The whole Qwen3-0.6B-shaped decode step (q8_decode_graph_build) at
+    position pos with a cache of `rows` rows: token latency of the graph
+    launch (and of its kernels launched directly), waiting on the token the
+    kernel stores into pinned memory.  Algorithmic bytes: the weights, the
+    norm weights, the pos + 1 key and value rows each layer reads, and the
+    activations (x, caches written: one row per layer)."""
+    model = gen.decode_model(gen.QWEN3_DIMS, cache_rows=rows, seed=seed)
+    dims = model["dims"]
+    layers = [{f: torch.from_numpy(L[f].reshape(-1)).to(dev) for f in q8.LAYER_FIELDS}
+              for L in model["layers"]]
+    out_norm = torch.from_numpy(model["out_norm"]).to(dev)
+    lm_head = torch.from_numpy(model["lm_head"].reshape(-1)).to(dev)
+    bufs = q8.decode_buffers(dims, dev, logits=False)
+    bufs["x_in"].copy_(torch.from_numpy(model["x_in"]))
+    bufs["pos"].fill_(pos)
+    host = torch.zeros(1, dtype=torch.int32).pin_memory()
+    g = q8.DecodeGraph(dims, layers, out_norm, lm_head, bufs, host_token=host)
+    nodes = g.info()
+    sec, toks = time_graph_steps(torch, [g], host, steps, warmup, poll=True)
+    ksec, ktoks = time_graph_steps(torch, [_KernelLaunch(g)], host, steps, warmup, poll=True)
+    assert ktoks == toks, "decode token differs between graph and kernel launches"
+    H, L = dims["hidden"], dims["n_layers"]
+    kvw = dims["n_kv_heads"] * dims["head_dim"]
+    wb = sum(model["layers"][0][k].size for k in gen.DECODE_WEIGHTS) * L \
+        + model["lm_head"].size
+    kvb = 2 * (pos + 1) * kvw * 4 * L
+    normb = (2 * H + 2 * dims["head_dim"]) * 4 * L + 4 * H
+    alg = wb + kvb + normb
+    g.close()
+    del layers, lm_head, bufs
+    torch.cuda.empty_cache()
+    return {
+        "pos": pos, "cache_rows": rows, "token": toks[-1],
+        "token_latency_us": round(sec * 1e6, 2),
+        "kernel_launches_token_latency_us": round(ksec * 1e6, 2),
+        "tokens_per_s": round(1.0 / sec, 1),
+        "GBps": round(alg / sec / 1e9, 1),
+        "alg_bytes": alg, "weight_bytes": wb, "kv_bytes": kvb,
+        "graph_nodes": {"kernel": nodes[0], "memcpy": nodes[1]},
+    }
+
+
 def only_workload(args, torch, q8, dev) -> int:
     """One configuration alone, for a kernel trace or counters of its kernel."""
     out = {"workload": args.only, "steps": args.steps}
@@ -206,6 +251,8 @@ def only_workload(args, torch, q8, dev) -> int:
                        args.steps, args.warmup)
         b = alg_bytes(1024, 151936, 1, False, True)
         out.update(avg_us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), alg_bytes=b)
+    elif args.only == "decode":
+        out.update(decode_step(torch, q8, dev, 1023, 4096, args.steps, args.warmup))
     elif args.only == "i8x_step":
         sets1 = [StepSet(torch, dev, 0, 1000 * j, 1, False) for j in range(2)]
         host = torch.zeros(1, dtype=torch.int32).pin_memory()
@@ -240,11 +287,12 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step"], default=None,
+    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode"],
+                    default=None,
                     help="only time one other configuration (for profiling runs): "
                          "the fused lm_head (1024 -> 151,936 + argmax, m = 1), "
-                         "the m = 8 step, or the int8-activation step; prints one "
-                         "JSON line")
+                         "the m = 8 step, the int8-activation step, or the whole "
+                         "decode step at position 1023; prints one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
@@ -462,6 +510,11 @@ def main() -> int:
         }
         for g in p8:
             g.close()
+
+        for dpos in (1023, 4095):
+            log(f"whole decode step (norms, attention, SwiGLU; 142 nodes), pos {dpos}")
+            extra[f"decode_step_pos{dpos}"] = decode_step(torch, q8, dev, dpos, 4096,
+                                                           steps2, 3)
     if extra:
         result["extra"] = extra
 

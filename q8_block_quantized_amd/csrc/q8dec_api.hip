@@ -132,12 +132,16 @@ struct SegmentLaunch {
   float *nout = nullptr, *ncopy = nullptr;
   int32_t ndim = 0;
   float neps = 0.f;
+  const int32_t *npos = nullptr;  // kNormNode: the position, the RoPE frequencies
+  const float *nfreq = nullptr;   // and the cos/sin table it writes
+  float *rope_out = nullptr;
 };
 
 hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
   if (L.kind == kAttnNode) return q8::launch_attention(L.attn, s);
   if (L.kind == kNormNode)
-    return q8::launch_rms_norm(L.nx, L.nw, L.nout, L.ncopy, 1, L.ndim, L.neps, s);
+    return q8::launch_step_start(L.nx, L.nw, L.nout, L.ncopy, L.ndim, L.neps, L.npos,
+                                 L.nfreq, L.rope_out, s);
   return q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
                          L.all_staged, s, i8x, L.epi);
 }
@@ -680,9 +684,12 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   lv.push_back({mv(M.lm_head, B.xf, B.logits, B.token, H, M.vocab)});
   std::vector<q8::StepPlan> plans(lv.size());
   for (size_t i = 0; i < lv.size(); i++) {
+    const bool epi = i + 1 < lv.size() && i % 4 != 0;  // o, gate/up, down
     st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
                        plans[i]);
     if (st) return st;
+    if (epi)  // their outputs are read by the epilogue
+      for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
   }
 
   q8_step_graph *g = new (std::nothrow) q8_step_graph();
@@ -693,10 +700,10 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   g->m = 1;
   g->i8x = false;
 
-  // workspace (16-byte aligned pieces): the lm_head argmax slot, the
+  // workspace (256-byte aligned pieces): the lm_head argmax slot, the
   // epilogues' arrival slot, the attention arrival slots, the epilogues,
-  // the RoPE frequencies, the attention partials, then each level's table
-  // and workgroup ranges
+  // the RoPE frequencies and the step's cos/sin table, the attention
+  // partials, then each level's table and workgroup ranges
   const int chunks = q8::attn_chunks(M.cache_rows);
   size_t total = 0;
   auto take = [&](size_t bytes) {
@@ -709,6 +716,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   const size_t o_aarr = take(sizeof(q8::ArgmaxSlot) * (size_t)M.n_kv_heads);
   const size_t o_epi = take(sizeof(q8::Epilogue) * 3 * (size_t)M.n_layers);
   const size_t o_freq = take(sizeof(float) * q8::kAttnHeadDim / 2);
+  const size_t o_rope = take(sizeof(float) * q8::kAttnHeadDim);
   const size_t o_part = take(sizeof(float) * (size_t)M.n_heads * chunks * q8::kAttnPart);
   std::vector<size_t> o_tab(plans.size()), o_grp(plans.size());
   for (size_t i = 0; i < plans.size(); i++) {
@@ -800,6 +808,9 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     L.ncopy = B.x;
     L.ndim = H;
     L.neps = M.eps;
+    L.npos = B.pos;
+    L.nfreq = (const float *)(ws + o_freq);
+    L.rope_out = (float *)(ws + o_rope);
     g->launches.push_back(L);
   }
   for (int32_t l = 0; l < M.n_layers; l++) {
@@ -815,7 +826,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     A.attn.kc = Ly.k_cache;
     A.attn.vc = Ly.v_cache;
     A.attn.pos = B.pos;
-    A.attn.freq = (const float *)(ws + o_freq);
+    A.attn.rope = (const float *)(ws + o_rope);
     A.attn.out = B.attn;
     A.attn.part = (float *)(ws + o_part);
     A.attn.arrive = (q8::ArgmaxSlot *)(ws + o_aarr);

@@ -39,7 +39,10 @@ __device__ __forceinline__ void load8(const float *p, float (&d)[8]) {
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
 
-// G query heads per key/value head.
+// G query heads per key/value head.  Every load the workgroup needs (its
+// vectors, the norm weights, the rotation table and its 64 cached key and
+// value rows) is issued as soon as pos is known, so the whole prologue costs
+// one memory round trip.
 template <int G>
 __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float qs[G][HD];  // normed, rotated queries
@@ -66,19 +69,49 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
   const bool owner = pos < t0 + CH;  // this chunk holds row pos
   const size_t kvw = (size_t)a.n_kv * HD;
 
-  // QK-norm and RoPE of the G queries and the key; lane l holds pair
-  // (l, l + 64) of a head.  The value is copied as it is.
-  for (int vec = wave; vec < G + 2; vec += 4) {
+  // Vectors: wave w takes vectors w and w + 4 of the G queries, the key (G)
+  // and the value (G + 1); lane l holds elements l and l + 64 (RoPE pair l).
+  constexpr int NV = (G + 2 + 3) / 4;
+  float x0[NV], x1[NV];
+#pragma unroll
+  for (int j = 0; j < NV; j++) {
+    const int vec = wave + 4 * j;
+    x0[j] = x1[j] = 0.f;
+    if (vec < G + 2) {
+      const float *src = vec < G ? a.q + (size_t)(g * G + vec) * HD
+                                 : (vec == G ? a.k : a.v) + (size_t)g * HD;
+      x0[j] = src[lane];
+      x1[j] = src[lane + 64];
+    }
+  }
+  const float wq0 = a.q_norm[lane], wq1 = a.q_norm[lane + 64];
+  const float wk0 = a.k_norm[lane], wk1 = a.k_norm[lane + 64];
+  const float cs = a.rope[2 * lane], sn = a.rope[2 * lane + 1];
+  // cached rows below pos: 16 lanes per row (8 dimensions each), 4 passes
+  const int slot = (int)threadIdx.x >> 4, sub = (int)threadIdx.x & 15;
+  float kr[4][8], vr[4][8];
+#pragma unroll
+  for (int ps = 0; ps < 4; ps++) {
+    const int tl = slot + 16 * ps, t = t0 + tl;
+#pragma unroll
+    for (int i = 0; i < 8; i++) kr[ps][i] = vr[ps][i] = 0.f;
+    if (tl < len && t != pos) {
+      const size_t off = (size_t)t * kvw + (size_t)g * HD + 8 * sub;
+      load8(a.kc + off, kr[ps]);
+      load8(a.vc + off, vr[ps]);
+    }
+  }
+
+  // QK-norm and RoPE of the queries and the key; the value as it is.  The
+  // chunk holding row pos appends this token's key and value to the cache.
+#pragma unroll
+  for (int j = 0; j < NV; j++) {
+    const int vec = wave + 4 * j;
     if (vec <= G) {
-      const float *src = vec < G ? a.q + (size_t)(g * G + vec) * HD : a.k + (size_t)g * HD;
-      const float *wn = vec < G ? a.q_norm : a.k_norm;
-      const float x0 = src[lane], x1 = src[lane + 64];
-      const float ss = dec::wave_sum(x0 * x0 + x1 * x1);
+      const float w0 = vec < G ? wq0 : wk0, w1 = vec < G ? wq1 : wk1;
+      const float ss = dec::wave_sum(x0[j] * x0[j] + x1[j] * x1[j]);
       const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
-      const float u0 = x0 * inv * wn[lane], u1 = x1 * inv * wn[lane + 64];
-      const float ang = (float)pos * a.freq[lane];
-      float sn, cs;
-      sincosf(ang, &sn, &cs);
+      const float u0 = x0[j] * inv * w0, u1 = x1[j] * inv * w1;
       const float r0 = u0 * cs - u1 * sn, r1 = u0 * sn + u1 * cs;
       float *dst = vec < G ? qs[vec] : kn;
       dst[lane] = r0;
@@ -88,32 +121,29 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
         row[lane] = r0;
         row[lane + 64] = r1;
       }
-    } else {
-      const float v0 = a.v[(size_t)g * HD + lane], v1 = a.v[(size_t)g * HD + lane + 64];
-      vn[lane] = v0;
-      vn[lane + 64] = v1;
+    } else if (vec == G + 1) {
+      vn[lane] = x0[j];
+      vn[lane + 64] = x1[j];
       if (owner) {
         float *row = a.vc + (size_t)pos * kvw + (size_t)g * HD;
-        row[lane] = v0;
-        row[lane + 64] = v1;
+        row[lane] = x0[j];
+        row[lane + 64] = x1[j];
       }
     }
   }
   __syncthreads();
-
-  // Scores: 16 lanes per cached row (8 dimensions each), 16 rows per pass.
-  const int slot = (int)threadIdx.x >> 4, sub = (int)threadIdx.x & 15;
-  float kr[4][8];
+  if (owner) {  // row pos comes from LDS
 #pragma unroll
-  for (int ps = 0; ps < 4; ps++) {
-    const int tl = slot + 16 * ps, t = t0 + tl;
-#pragma unroll
-    for (int i = 0; i < 8; i++) kr[ps][i] = 0.f;
-    if (tl < len) {
-      if (t != pos) load8(a.kc + (size_t)t * kvw + (size_t)g * HD + 8 * sub, kr[ps]);
-      else load8(kn + 8 * sub, kr[ps]);
+    for (int ps = 0; ps < 4; ps++) {
+      const int tl = slot + 16 * ps;
+      if (tl < len && t0 + tl == pos) {
+        load8(kn + 8 * sub, kr[ps]);
+        load8(vn + 8 * sub, vr[ps]);
+      }
     }
   }
+
+  // Scores q . k_t / sqrt(128).
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
   for (int h = 0; h < G; h++) {
@@ -145,18 +175,7 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Weighted value rows, same lane mapping as the scores.
-  float vr[4][8];
-#pragma unroll
-  for (int ps = 0; ps < 4; ps++) {
-    const int tl = slot + 16 * ps, t = t0 + tl;
-#pragma unroll
-    for (int i = 0; i < 8; i++) vr[ps][i] = 0.f;
-    if (tl < len) {
-      if (t != pos) load8(a.vc + (size_t)t * kvw + (size_t)g * HD + 8 * sub, vr[ps]);
-      else load8(vn + 8 * sub, vr[ps]);
-    }
-  }
+  // Weighted value rows.
 #pragma unroll
   for (int h = 0; h < G; h++) {
     float acc[8];
@@ -184,38 +203,69 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
     const int h = t / HD, d = t % HD;
     const float s = (red[0][h][d] + red[1][h][d]) + (red[2][h][d] + red[3][h][d]);
     float *p = a.part + ((size_t)(g * G + h) * a.chunks + c) * kAttnPart;
-    p[4 + d] = s;
+    dec::st_dev(p + 4 + d, s);
     if (d == 0) {
-      p[0] = ml[h][0];
-      p[1] = ml[h][1];
+      dec::st_dev(p, ml[h][0]);
+      dec::st_dev(p + 1, ml[h][1]);
     }
   }
 
-  // The last workgroup of this key/value head merges the nc partials, in
-  // chunk order: out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.
+  // The last workgroup of this key/value head merges the nc partials in
+  // chunk order, keeping a running maximum M: out = sum_c e^(m_c - M) acc_c /
+  // sum_c e^(m_c - M) l_c.  Partials are loaded 16 chunks at a time.
   if (!dec::arrive_last(a.arrive + g, (uint32_t)c, (uint32_t)nc, &flag)) return;
   for (int t = (int)threadIdx.x; t < G * HD; t += dec::kThreads) {
     const int h = t / HD, d = t % HD;
     const float *ph = a.part + (size_t)(g * G + h) * a.chunks * kAttnPart;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nc; cc++) M = fmaxf(M, ph[(size_t)cc * kAttnPart]);
-    float L = 0.f, A = 0.f;
-    for (int cc = 0; cc < nc; cc++) {
-      const float *p = ph + (size_t)cc * kAttnPart;
-      const float w = expf(p[0] - M);
-      L += p[1] * w;
-      A += p[4 + d] * w;
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 16) {
+      float pm[16], pl[16], pa[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        pm[i] = -INFINITY;
+        pl[i] = pa[i] = 0.f;
+        if (c0 + i < nc) {
+          const float *p = ph + (size_t)(c0 + i) * kAttnPart;
+          pm[i] = dec::ld_dev(p);
+          pl[i] = dec::ld_dev(p + 1);
+          pa[i] = dec::ld_dev(p + 4 + d);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        if (c0 + i < nc) {
+          if (pm[i] > M) {
+            const float r = expf(M - pm[i]);
+            L *= r;
+            A *= r;
+            M = pm[i];
+          }
+          const float w = expf(pm[i] - M);
+          L += pl[i] * w;
+          A += pa[i] * w;
+        }
+      }
     }
     a.out[(size_t)(g * G + h) * HD + d] = A / L;
   }
 }
 
+// The step's first node: x = x_in and xn = rms_norm_row(x_in) (first
+// layer's weight), and the RoPE cos/sin pairs of position *pos (the same for
+// every layer), rope[2i] = cos(pos * freq[i]), rope[2i + 1] = sin(...).
 __global__ void __launch_bounds__(dec::kThreads)
-rms_norm_kernel(const float *x, const float *w, float *out, float *copy, int dim,
-                float eps) {
+step_start_kernel(const float *x_in, const float *w, float *xn, float *x, int dim, float eps,
+                  const int32_t *pos, const float *freq, float *rope) {
   __shared__ float red[4];
-  const size_t off = (size_t)blockIdx.x * dim;
-  dec::norm_row(x + off, nullptr, copy ? copy + off : nullptr, w, out + off, dim, eps, red);
+  __shared__ float vs[kNormMaxDim];
+  if (threadIdx.x < HD / 2) {
+    const float ang = (float)*pos * freq[threadIdx.x];
+    float sn, cs;
+    sincosf(ang, &sn, &cs);
+    rope[2 * threadIdx.x] = cs;
+    rope[2 * threadIdx.x + 1] = sn;
+  }
+  dec::norm_row(x_in, nullptr, x, w, xn, dim, eps, vs, red);
 }
 
 __global__ void rope_freq_kernel(float theta, float *freq) {
@@ -243,11 +293,12 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rms_norm(const float *x, const float *w, float *out, float *copy,
-                           int rows, int dim, float eps, hipStream_t s) {
-  if (rows < 1 || dim < 1 || dim > kNormMaxDim) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)rows), dim3(dec::kThreads), 0, s, x, w,
-                     out, copy, dim, eps);
+hipError_t launch_step_start(const float *x_in, const float *w, float *xn, float *x,
+                             int dim, float eps, const int32_t *pos, const float *freq,
+                             float *rope, hipStream_t s) {
+  if (dim < 1 || dim > kNormMaxDim) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(step_start_kernel, dim3(1), dim3(dec::kThreads), 0, s, x_in, w, xn, x,
+                     dim, eps, pos, freq, rope);
   return hipGetLastError();
 }
 

@@ -54,8 +54,12 @@ struct StepDesc {
   int32_t n, p;
   int32_t tile_begin;     // first tile of this matvec in the launch
   int32_t rows_per_tile;
-  int32_t pad[2];
+  int32_t flags;          // kDescDeviceOut: outputs stored at device scope
+  int32_t pad;
 };
+// y is stored with device-scope stores, so that the launch's epilogue (m = 1)
+// can read it (see Epilogue); otherwise y takes plain stores.
+constexpr int32_t kDescDeviceOut = 1;
 static_assert(sizeof(StepDesc) == 64, "descriptor layout");
 
 // Workgroups g in [first, first + size) of a persistent step share the
@@ -168,7 +172,7 @@ struct AttnArgs {
   const float *q_norm, *k_norm;  // [128]
   float *kc, *vc;                // [cache_rows][n_kv*128]
   const int32_t *pos;            // device int32
-  const float *freq;             // [64] RoPE frequencies (rope_freq)
+  const float *rope;             // [64][2] cos, sin of pos * freq (step_start)
   float *out;                    // [n_heads*128]
   float *part;                   // [n_heads][chunks][kAttnPart]
   ArgmaxSlot *arrive;            // [n_kv], zeroed (counters only)
@@ -178,10 +182,12 @@ struct AttnArgs {
 int attn_chunks(int cache_rows);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
-// rms_norm_row over `rows` rows of dim <= kNormMaxDim values; copy (or NULL)
-// also receives x.
-hipError_t launch_rms_norm(const float *x, const float *w, float *out, float *copy,
-                           int rows, int dim, float eps, hipStream_t s);
+// The step's first node: x = x_in, xn = rms_norm_row(x_in) * w (dim <=
+// kNormMaxDim), and rope[2i], rope[2i + 1] = cos, sin of *pos * freq[i] for
+// i < 64.
+hipError_t launch_step_start(const float *x_in, const float *w, float *xn, float *x,
+                             int dim, float eps, const int32_t *pos, const float *freq,
+                             float *rope, hipStream_t s);
 
 // freq[i] = 1 / theta^(i / 64) for i < 64, the power rounded to binary32
 // from binary64 and the quotient in binary32 (the RoPE frequencies).

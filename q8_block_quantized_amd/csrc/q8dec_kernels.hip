@@ -59,6 +59,14 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gpw(T *p) {
   return (__attribute__((address_space(1))) T *)p;
 }
 
+// A matvec output.  dev: stored at device scope (written through to where
+// every XCD sees it), so that a workgroup of the same launch can read it with
+// device-scope loads and no L2 write-back (the epilogue, see arrive_last).
+__device__ __forceinline__ void store_y(float *p, float v, bool dev = false) {
+  if (dev) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else gpw(p)[0] = v;
+}
+
 constexpr int kWG = 256;           // threads per workgroup
 constexpr int kWaves = kWG / 64;   // wavefronts per workgroup
 constexpr int kRowsPerPass = 2 * kWaves;
@@ -385,6 +393,7 @@ struct Tile {
   float *y;         // [m][p] or nullptr
   int32_t n, bpr, p, m;
   int32_t r0, r1;   // rows [r0, r1) of this tile, r1 <= p
+  bool devy;        // y takes device-scope stores
 };
 
 // Direct path, m = 1, x in LDS.  NBL = blocks per lane per row (ceil(bpr / 32)); each
@@ -427,7 +436,7 @@ __device__ __forceinline__ void direct_m1(const Tile &c, unsigned long long &bes
       }
       acc = half_wave_sum(acc);
       if (k == 31 && r < c.r1) {
-        if (c.y) c.y[r] = acc;
+        if (c.y) store_y(&c.y[r], acc, c.devy);
         if (keys) best = umax64(best, argmax_key(acc, (uint32_t)r));
       }
     }
@@ -482,7 +491,7 @@ __device__ __forceinline__ void direct_mb(const Tile &c, unsigned long long *bes
         if (j < c.m) {
           const float v = half_wave_sum(acc[j]);
           if (k == 31 && r < c.r1) {
-            if (c.y) c.y[(int64_t)j * c.p + r] = v;
+            if (c.y) store_y(&c.y[(int64_t)j * c.p + r], v, c.devy);
             if (keys) best[j] = umax64(best[j], argmax_key(v, (uint32_t)r));
           }
         }
@@ -520,7 +529,7 @@ __device__ void rows_generic(const Tile &c, unsigned long long *best, bool keys)
       if (j < c.m) {
         const float v = half_wave_sum(acc[j]);
         if (k == 31 && r < c.r1) {
-          if (c.y) c.y[(int64_t)j * c.p + r] = v;
+          if (c.y) store_y(&c.y[(int64_t)j * c.p + r], v, c.devy);
           if (keys) best[j] = umax64(best[j], argmax_key(v, (uint32_t)r));
         }
       }
@@ -561,7 +570,7 @@ __device__ void run_direct(const Tile &c, int path, unsigned long long *best,
 // Rows [0, rows) of a staged tile (LDS `tl`, row pitch 34 * bpr bytes), m = 1.
 // Lane k of each half-wave reads the windows of blocks k, k+32, k+64 of its
 // row from LDS, and the block's 32 x values from LDS.
-template <int NBL>
+template <int NBL, bool DEVY>
 __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
                                           int32_t rows, const float *xs,
                                           float *y, int32_t r0, bool keys,
@@ -601,7 +610,7 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
     }
     acc = half_wave_sum(acc);
     if (k == 31 && rr < rows) {
-      if (y) gpw(y)[r0 + rr] = acc;
+      if (y) store_y(&y[r0 + rr], acc, DEVY);
       if (keys) best = umax64(best, argmax_key(acc, (uint32_t)(r0 + rr)));
     }
   }
@@ -702,7 +711,7 @@ __device__ __forceinline__ void staged_m1_i8(const uint32_t *tl, int32_t bpr,
     }
     acc = half_wave_sum(acc);
     if (k == 31 && rr < rows) {
-      if (y) gpw(y)[r0 + rr] = acc;
+      if (y) store_y(&y[r0 + rr], acc);
       if (keys) best = umax64(best, argmax_key(acc, (uint32_t)(r0 + rr)));
     }
   }
@@ -755,7 +764,7 @@ __device__ __forceinline__ void staged_mb_i8(const uint32_t *tl, int32_t bpr,
       if (j < m) {
         const float v = half_wave_sum(acc[j]);
         if (k == 31 && rr < rows) {
-          if (y) gpw(y)[(int64_t)j * p + r0 + rr] = v;
+          if (y) store_y(&y[(int64_t)j * p + r0 + rr], v);
           if (keys) best[j] = umax64(best[j], argmax_key(v, (uint32_t)(r0 + rr)));
         }
       }
@@ -913,7 +922,7 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
         v += rb[w * 4 * kRedStride + hi] + rb[w * 4 * kRedStride + lo];
       const int32_t rr = rg + jj;
       if (xr < m && rr < rows) {
-        if (y) gpw(y)[(int64_t)xr * p + r0 + rr] = v;
+        if (y) store_y(&y[(int64_t)xr * p + r0 + rr], v);
         if (keys) kb = umax64(kb, argmax_key(v, (uint32_t)(r0 + rr)));
       }
     }
@@ -1150,6 +1159,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         pf.load_x(nxt.d.x, m * nxt.d.n);
     }
     const bool keys = cur.d.idx != nullptr;
+    const bool devy = M1 && !I8X && (cur.d.flags & kDescDeviceOut);
     if (I8X) {
       const int nbl = nbl_of(cur.d.n);
       if (M1) {
@@ -1163,9 +1173,15 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       }
     } else if (staged(cur)) {
       const int nbl = nbl_of(cur.d.n);
-      if (nbl == 1) staged_m1<1>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-      else if (nbl == 2) staged_m1<2>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-      else staged_m1<3>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+      if (devy) {  // outputs read by the launch's epilogue (decode step levels)
+        if (nbl == 1) staged_m1<1, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        else if (nbl == 2) staged_m1<2, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        else staged_m1<3, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+      } else {
+        if (nbl == 1) staged_m1<1, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        else if (nbl == 2) staged_m1<2, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        else staged_m1<3, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+      }
     } else if (mfma(cur)) {
       if (bpr == 32)
         mfma_tile<8>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
@@ -1186,6 +1202,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       c.m = m;
       c.r0 = cur.r0;
       c.r1 = cur.r0 + cur.rows;
+      c.devy = devy;
       run_direct<M1>(c, cur.path, best, keys);
     }
     if (keys && (!more || nxt.desc != cur.desc)) {
@@ -1241,8 +1258,8 @@ mv_kernel(StepDesc d, int32_t m) {
 // The decode step: every tile of every descriptor of a device-side table
 // (count entries in tile order), with no ordering between descriptors.
 // Workgroups form groups; a group interleaves its contiguous tile range.
-// epi (or NULL): element-wise work that the last workgroup to finish runs
-// once every tile is written.
+// epi (or NULL; m = 1 with binary32 activations only): element-wise work
+// that the last workgroup to finish runs once every tile is written.
 template <bool M1, bool ANY, bool I8X>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
@@ -1253,9 +1270,11 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
   run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
-  if (epi) {
-    __syncthreads();  // every wave is done with the tile buffer
-    dec::run_epilogue(epi, blockIdx.x, gridDim.x, lds);
+  if constexpr (M1 && !I8X) {
+    if (epi) {
+      __syncthreads();  // every wave is done with the tile buffer
+      dec::run_epilogue(epi, blockIdx.x, gridDim.x, lds);
+    }
   }
 }
 
@@ -1426,6 +1445,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi) {
+  if (epi && (m != 1 || i8x)) return hipErrorInvalidValue;  // m = 1 binary32 only
   if (i8x) {
     if (m == 1)
       hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,
