@@ -251,6 +251,18 @@ def only_workload(args, torch, q8, dev) -> int:
                        args.steps, args.warmup)
         b = alg_bytes(1024, 151936, 1, False, True)
         out.update(avg_us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), alg_bytes=b)
+    elif args.only == "wide":
+        m = 32
+        sets32 = [StepSet(torch, dev, 0, 7000 + 1000 * j, m, False) for j in range(2)]
+        host32 = torch.zeros(m, dtype=torch.int32).pin_memory()
+        gw = [q8.StepGraph(s.descs, m, host_idx=host32, mode=q8.Q8_GRAPH_PERSISTENT)
+              for s in sets32]
+        sw, _ = time_graph_steps(torch, gw, host32, args.steps, args.warmup, poll=True)
+        bw = sets32[0].bytes
+        out.update(step_latency_us=round(sw * 1e6, 2), GBps=round(bw / sw / 1e9, 1),
+                   per_row_us=round(sw * 1e6 / m, 2), alg_bytes=bw)
+        for g in gw:
+            g.close()
     elif args.only == "decode":
         out.update(decode_step(torch, q8, dev, 1023, 4096, args.steps, args.warmup))
     elif args.only == "i8x_step":
@@ -287,12 +299,13 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode"],
+    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode", "wide"],
                     default=None,
                     help="only time one other configuration (for profiling runs): "
                          "the fused lm_head (1024 -> 151,936 + argmax, m = 1), "
-                         "the m = 8 step, the int8-activation step, or the whole "
-                         "decode step at position 1023; prints one JSON line")
+                         "the m = 8 step, the int8-activation step, the whole "
+                         "decode step at position 1023, or the m = 32 step; prints "
+                         "one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
@@ -510,6 +523,25 @@ def main() -> int:
         }
         for g in p8:
             g.close()
+        del sets8, p8
+
+        log("batched m=32 step (wide batch, persistent graph)")
+        sets32 = [StepSet(torch, dev, 0, 7000 + 1000 * j, 32, False, weights=s.w)
+                  for j, s in enumerate(sets)]
+        host32 = torch.zeros(32, dtype=torch.int32).pin_memory()
+        p32 = [q8.StepGraph(s.descs, 32, host_idx=host32, mode=q8.Q8_GRAPH_PERSISTENT)
+               for s in sets32]
+        s32, _ = time_graph_steps(torch, p32, host32, steps2, 3, poll=True)
+        b32 = sets32[0].bytes
+        extra["batched_m32_step"] = {
+            "step_latency_us": round(s32 * 1e6, 2),
+            "GBps": round(b32 / s32 / 1e9, 1),
+            "per_row_us": round(s32 * 1e6 / 32, 2),
+            "per_row_vs_m1": round((s32 / 32) / sec, 3),
+        }
+        for g in p32:
+            g.close()
+        del sets32, p32
 
         for dpos in (1023, 4095):
             log(f"whole decode step (norms, attention, SwiGLU; 142 nodes), pos {dpos}")

@@ -70,7 +70,9 @@ extern "C" {
 /* ---- limits --------------------------------------------------------- */
 #define Q8_BLOCK 32                 /* quants per block                       */
 #define Q8_BLOCK_BYTES 34           /* bytes per block                        */
-#define Q8_MAX_M 8                  /* activation rows per batched call       */
+#define Q8_MAX_M 32                 /* activation rows per batched call       */
+#define Q8_MAX_M_NARROW 8           /* m above this: n a positive multiple of 256,
+                                       binary32 activations only              */
 #define Q8_MAX_N 65536              /* 0 <= n <= Q8_MAX_N, n % 32 == 0        */
 #define Q8_MAX_P 0x7FFFFFFF         /* 0 <= p; p >= 1 where an argmax is taken */
 #define Q8_MAX_DESCS 4096           /* descriptors per step graph             */
@@ -102,12 +104,18 @@ int q8_init(void);
 int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
               void *stream);
 
-/* Batched decode: y[m][p] = x[m][n] W^T with 1 <= m <= 8; the weight blocks
- * are streamed once for all m rows. */
+/* Batched decode: y[m][p] = x[m][n] W^T with 1 <= m <= Q8_MAX_M (32); the
+ * weight blocks are streamed once for all m rows (the Algenta page's batched
+ * decode, where the rows of a batch share one weight sweep; rvllm's
+ * linear_small loops rows inside its weight loop).  m <= 8: any width
+ * (n == 0 writes zeros).  8 < m <= 32: n a positive multiple of 256, else
+ * Q8_ERR_SHAPE; each output is computed from x split into two bf16 parts and
+ * exact quants on the matrix cores, accumulated in binary32 (the same bound
+ * as every other entry point). */
 int q8_matvec_batched(const void *w, const float *x, float *y, int32_t m,
                       int32_t n, int32_t p, void *stream);
 
-/* idx[i] = argmax over logits[i][0..p-1] for i < m; 1 <= m <= 8, p >= 1. */
+/* idx[i] = argmax over logits[i][0..p-1] for i < m; 1 <= m <= Q8_MAX_M, p >= 1. */
 int q8_argmax(const float *logits, int32_t m, int32_t p, int32_t *idx,
               void *stream);
 
@@ -132,8 +140,8 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
  * sum_b |scale| * d/2 * sum_j |q| per output; it is a separate operation
  * with its own bound, never a replacement for q8_matvec.
  * Widths: n a multiple of 256 with n <= 3072 (n == 0 writes zeros); other
- * widths give Q8_ERR_SHAPE.  1 <= m <= Q8_MAX_M; layouts, alignment,
- * ownership and errors as q8_matvec_batched. */
+ * widths give Q8_ERR_SHAPE.  1 <= m <= Q8_MAX_M_NARROW (8); layouts,
+ * alignment, ownership and errors as q8_matvec_batched. */
 int q8_matvec_i8x(const void *w, const float *x, float *y, int32_t m, int32_t n,
                   int32_t p, void *stream);
 

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libq8dec.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "q8dec.h")
 
 Q8_OK = 0
-Q8_MAX_M = 8
+Q8_MAX_M = 32
+Q8_MAX_M_NARROW = 8
 Q8_MAX_N = 65536
 Q8_GRAPH_CHAIN = 0
 Q8_GRAPH_PERSISTENT = 1
@@ -196,7 +197,7 @@ def q8_matvec(w, x, y, stream=None) -> None:
 
 
 def q8_matvec_batched(w, x, y, stream=None) -> None:
-    """y[m, p] = x[m, n] W^T, 1 <= m <= 8."""
+    """y[m, p] = x[m, n] W^T, 1 <= m <= 32 (m > 8: n a multiple of 256)."""
     torch = _torch()
     _need(x, torch.float32, "x")
     _need(y, torch.float32, "y", x.device)

@@ -99,6 +99,7 @@ int check_matvec(const void *w, const float *x, const float *y,
                  bool need_y) {
   if (m < 1 || m > Q8_MAX_M) return Q8_ERR_SHAPE;
   if (n < 0 || n > Q8_MAX_N || (n % Q8_BLOCK) != 0) return Q8_ERR_SHAPE;
+  if (m > Q8_MAX_M_NARROW && !q8::wide_shape_ok(n)) return Q8_ERR_SHAPE;
   if (p < 0) return Q8_ERR_SHAPE;
   if (idx && p < 1) return Q8_ERR_SHAPE;
   const bool wbytes = n > 0 && p > 0;
@@ -386,7 +387,7 @@ int q8_matvec_i8x(const void *w, const float *x, float *y, int32_t m, int32_t n,
                   int32_t p, void *stream) {
   int st = check_matvec(w, x, y, nullptr, m, n, p, true);
   if (st) return st;
-  if (n > 0 && !q8::i8x_shape_ok(n)) return Q8_ERR_SHAPE;
+  if (m > Q8_MAX_M_NARROW || (n > 0 && !q8::i8x_shape_ok(n))) return Q8_ERR_SHAPE;
   if ((st = ensure_device(nullptr))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, m, n, p, nullptr,
                                    nullptr, (hipStream_t)stream, n > 0);
@@ -399,7 +400,7 @@ int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
   if (!idx) return Q8_ERR_NULL;
   int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
   if (st) return st;
-  if (n > 0 && !q8::i8x_shape_ok(n)) return Q8_ERR_SHAPE;
+  if (m > Q8_MAX_M_NARROW || (n > 0 && !q8::i8x_shape_ok(n))) return Q8_ERR_SHAPE;
   int dev = 0;
   if ((st = ensure_device(&dev))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
@@ -478,7 +479,7 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
     const q8_matvec_desc &d = descs[i];
     int st = check_matvec(d.w, d.x, d.y, d.idx, m, d.n, d.p, d.idx == nullptr);
     if (st) return st;
-    if (i8x && !q8::i8x_shape_ok(d.n)) return Q8_ERR_SHAPE;
+    if (i8x && (m > Q8_MAX_M_NARROW || !q8::i8x_shape_ok(d.n))) return Q8_ERR_SHAPE;
     if (d.idx) nargmax++;
   }
   if (nargmax > Q8_MAX_ARGMAX_DESCS) return Q8_ERR_COUNT;

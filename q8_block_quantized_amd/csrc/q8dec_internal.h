@@ -16,14 +16,13 @@ namespace q8 {
 // count out itself).  The keys and the counter sit in different 128-byte
 // lines, so atomics on one do not queue behind atomics on the other.
 struct ArgmaxGroup {
-  unsigned long long keys[8];
-  unsigned int pad0[16];
+  unsigned long long keys[32];
   unsigned int counter;
   unsigned int expected;
   unsigned int pad1[30];
 };
-static_assert(sizeof(ArgmaxGroup) == 256, "group layout");
-static_assert(offsetof(ArgmaxGroup, counter) == 128, "counter line");
+static_assert(sizeof(ArgmaxGroup) == 384, "group layout");
+static_assert(offsetof(ArgmaxGroup, counter) == 256, "counter line");
 
 #ifndef Q8_ARGMAX_TEAMS
 #define Q8_ARGMAX_TEAMS 32
@@ -79,6 +78,9 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 // Widths the int8-activation variant takes: the staged ones (n/32 a
 // multiple of 8, n <= 3072).
 bool i8x_shape_ok(int n);
+
+// Widths a wide batch (8 < m <= 32) takes: n a positive multiple of 256.
+bool wide_shape_ok(int n);
 
 // Launches idx[i] = argmax(logits[i][:p]) for i < m.
 hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,

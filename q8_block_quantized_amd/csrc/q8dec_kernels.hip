@@ -252,7 +252,8 @@ __device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
 // updates before it have returned (performed at the memory side), which
 // orders them without L2 write-back or invalidation.  Four dependent round
 // trips separate the last arrival from the result.
-__device__ void argmax_arrive(const unsigned long long (*lk)[8], int m,
+template <int MR>
+__device__ void argmax_arrive(const unsigned long long (*lk)[MR], int m,
                               ArgmaxSlot *__restrict__ slot,
                               int32_t *__restrict__ idx, uint32_t wg,
                               uint32_t nwg) {
@@ -290,16 +291,16 @@ __device__ void argmax_arrive(const unsigned long long (*lk)[8], int m,
   }
   if (!__builtin_amdgcn_readfirstlane(last)) return;
   // Every team is complete: lane j takes team j's keys in one round trip.
-  unsigned long long v[8];
+  unsigned long long v[MR];
 #pragma unroll
-  for (int r = 0; r < 8; r++) {
+  for (int r = 0; r < MR; r++) {
     v[r] = 0ull;
     if (r < m && lane < (int)T)
       v[r] = __hip_atomic_exchange(&slot->team[lane].keys[r], 0ull, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
-  for (int r = 0; r < 8; r++) {
+  for (int r = 0; r < MR; r++) {
     if (r < m) {
       const unsigned long long k = wave_max64(v[r]);
       if (lane == 0) {
@@ -328,7 +329,8 @@ __device__ void argmax_arrive(const unsigned long long (*lk)[8], int m,
 //  kDirect : each lane loads its blocks' windows straight from global
 //            memory (dword aligned, 34-byte lane stride); any row pitch.
 //  kGeneric: as kDirect, but x is read from global memory (large m * n).
-enum Path : int { kStaged = 0, kDirect = 1, kGeneric = 2, kMfma = 3 };
+//  kWide   : 8 < m <= 32, n a multiple of 256 (see wide_tiles).
+enum Path : int { kStaged = 0, kDirect = 1, kGeneric = 2, kMfma = 3, kWide = 4 };
 
 #ifndef Q8_TILE_BYTES
 #define Q8_TILE_BYTES 26112  // 8 rows of 3072 columns
@@ -347,13 +349,14 @@ constexpr int kMfmaRowPad = 16;
 constexpr int kMfmaTileBytes = 53248;  // LDS of a batched tile, pads included
 constexpr int kMfmaChunks = (kMfmaTileBytes + 16 * kWG - 1) / (16 * kWG);
 constexpr int kMfmaMaxBlocks = kMaxLdsBlocks / kWaves;  // x blocks per wave
-constexpr int kMaxM = 8;  // activation rows per launch (the ABI's limit)
+constexpr int kMaxM = 8;  // activation rows of the m <= 8 paths (wider: kWide)
 constexpr int kI8xMaxBlocks = kMaxM * kMaxLdsBlocks;  // int8-activation steps
 constexpr int kRedStride = 80;  // floats between a wave's partial-sum entries
 constexpr int kRedFloats = 2 * kWaves * 4 * kRedStride;  // two sets per wave
 
 __host__ __device__ inline int path_of(int m, int n) {
   const int bpr = n >> 5;
+  if (m > kMaxM) return kWide;  // callers ensure n % 256 == 0 (wide_shape_ok)
   if (bpr == 0 || bpr > kMaxLdsBlocks) return kGeneric;
   if (m == 1) return bpr % 8 == 0 ? kStaged : kDirect;
   if (bpr == 32 || bpr == 64 || bpr == 96) return kMfma;
@@ -367,6 +370,7 @@ __host__ __device__ inline int nbl_of(int n) { return ((n >> 5) + 31) >> 5; }
 // generic tiles are two or four passes.
 __host__ __device__ inline int tile_rows_of(int m, int n) {
   const int path = path_of(m, n);
+  if (path == kWide) return 128;  // kWideRows
   if (path == kStaged) {
     const int r = kTileMaxBytes / ((n >> 5) * 34);
     return r >= 64 ? 64 : (r < 1 ? 1 : r);
@@ -1242,6 +1246,241 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
 }
 
 
+// ---- wide batches: 8 < m <= 32 -------------------------------------------------
+//
+// Up to 32 activation rows share one sweep of the weights (the Algenta page's
+// batched decode arm, where the rows of a batch share one weight sweep;
+// rvllm's linear_small loops the rows inside its weight loop).  At this width
+// the products are a dense contraction, so they run on the matrix cores, but
+// x (32 rows x n, hi and lo bf16) no longer fits in registers, so it is
+// staged in LDS a K-chunk at a time beside the weights:
+//  * a tile is 128 weight rows (each wave two 16-row groups) over the whole
+//    row, walked in chunks of 8 blocks (256 columns);
+//  * per chunk the tile's 128 x 272 weight bytes go to LDS (coalesced
+//    16-byte loads, rows padded to 288 bytes) and the m x 256 floats of x
+//    become operand columns: column group c holds x rows 8c .. 8c + 7 as bf16
+//    "hi" (columns 0..7) and the bf16 of the rounding rest "lo" (8..15), the
+//    split of the m <= 8 path;
+//  * per block, each wave builds the quant operand of its two row groups
+//    once, reads each column group's operand once and issues up to eight
+//    v_mfma_f32_16x16x32_bf16, each scaled once by the block's scale;
+//  * the next chunk's bytes are loaded into registers while this one is
+//    computed.
+// At the end y[xr][row] = hi column + lo column (a lane and the lane 32
+// above it).  Requires n a multiple of 256.
+
+constexpr int kWideRows = 128;
+constexpr int kWideKB = 8;                                // blocks per chunk
+constexpr int kWideWPitch = kWideKB * 34 + 16;            // staged weight row, bytes
+constexpr int kWideXPitch = kWideKB * 32 * 2 + 16;        // operand column, bytes
+constexpr int kWideWBytes = kWideRows * kWideWPitch;      // 36,864
+constexpr int kWideXBytes = 4 * 16 * kWideXPitch;         // 33,792
+constexpr int kWideKeys = kWaves * 32 * 8;                // argmax keys, bytes
+constexpr int kWideLds = kWideWBytes + kWideXBytes + kWideKeys;
+constexpr int kWideWChunks = (kWideRows * 17 + kWG - 1) / kWG;  // 16-byte loads / thread
+constexpr int kWideXChunks = 32 * 64 / kWG;                      // float4 loads / thread
+
+struct WideItem {
+  int32_t desc;  // descriptor index, -1: none
+  int32_t r0, rows, kc;
+  StepDesc d;
+};
+
+// Registers carrying one chunk from memory to LDS.
+struct WidePrefetch {
+  u32x4 w[kWideWChunks];
+  f32x4 x[kWideXChunks];
+
+  __device__ __forceinline__ void load(const WideItem &it, int32_t m) {
+    const int32_t pitch = (it.d.n >> 5) * 34;
+    const uint8_t *wb = it.d.w + (int64_t)it.r0 * pitch + 272 * it.kc;
+#pragma unroll
+    for (int i = 0; i < kWideWChunks; i++) {
+      const int idx = (int)threadIdx.x + kWG * i;
+      const int row = idx / 17, q = idx % 17;
+      w[i] = u32x4{0u, 0u, 0u, 0u};
+      if (row < it.rows)
+        w[i] = __builtin_nontemporal_load(
+            (const u32x4 *)(wb + (int64_t)row * pitch + 16 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < kWideXChunks; i++) {
+      const int idx = (int)threadIdx.x + kWG * i;
+      const int xr = idx >> 6, q = idx & 63;
+      x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (xr < m)
+        x[i] = *(const f32x4 *)(it.d.x + (int64_t)xr * it.d.n + 256 * it.kc + 4 * q);
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t *wl, uint8_t *xl) const {
+#pragma unroll
+    for (int i = 0; i < kWideWChunks; i++) {
+      const int idx = (int)threadIdx.x + kWG * i;
+      const int row = idx / 17, q = idx % 17;
+      if (row < kWideRows) *(u32x4 *)(wl + row * kWideWPitch + 16 * q) = w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kWideXChunks; i++) {
+      const int idx = (int)threadIdx.x + kWG * i;
+      const int xr = idx >> 6, q = idx & 63;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const float hi = (float)(__bf16)x[i][c];
+        h[c] = bf16_bits(x[i][c]);
+        l[c] = bf16_bits(x[i][c] - hi);
+      }
+      uint8_t *col = xl + (xr >> 3) * 16 * kWideXPitch + (xr & 7) * kWideXPitch + 8 * q;
+      *(uint2 *)col = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *(uint2 *)(col + 8 * kWideXPitch) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    }
+  }
+};
+
+// The work items of one workgroup: tiles first, first + stride, ... (< end),
+// each in bpr / 8 chunks.
+template <class Src>
+__device__ __forceinline__ WideItem wide_item(const Src &src, int32_t t, int32_t end,
+                                              int32_t kc, int32_t hint) {
+  WideItem it;
+  it.desc = -1;
+  if (t >= end) return it;
+  it.desc = src.find(t, hint);
+  it.d = src.get(it.desc);
+  it.r0 = (t - it.d.tile_begin) * kWideRows;
+  it.rows = min(kWideRows, it.d.p - it.r0);
+  it.kc = kc;
+  return it;
+}
+
+template <class Src>
+__device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t stride,
+                           int32_t m, float *lds) {
+  uint8_t *wl = (uint8_t *)lds;
+  uint8_t *xl = wl + kWideWBytes;
+  unsigned long long(*lk)[32] = (unsigned long long(*)[32])(xl + kWideXBytes);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int ncg = (m + 7) >> 3;  // live column groups
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  int32_t t = first;
+  WideItem cur = wide_item(src, t, end, 0, 0);
+  if (cur.desc < 0) return;
+  WidePrefetch pf;
+  pf.load(cur, m);
+  f32x4 acc[2][4];
+  unsigned long long best[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) best[c][r] = 0ull;
+  for (;;) {
+    if (cur.kc == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 2; rg++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) acc[rg][c] = zero;
+    }
+    // the next chunk: this tile's, or the next tile's first
+    const int32_t nchunks = (cur.d.n >> 5) / kWideKB;
+    WideItem nxt = cur;
+    if (cur.kc + 1 < nchunks) {
+      nxt.kc = cur.kc + 1;
+    } else {
+      const int32_t tn = t + stride;
+      nxt = wide_item(src, tn, end, 0, cur.desc);
+    }
+    __syncthreads();  // the previous chunk's readers are done
+    pf.store(wl, xl);
+    __syncthreads();
+    if (nxt.desc >= 0) pf.load(nxt, m);
+
+#pragma unroll
+    for (int b = 0; b < kWideKB; b++) {
+      // quant operands and scales of the wave's two row groups (row j)
+      bf16x8 qb[2];
+      float sc[2];
+#pragma unroll
+      for (int rg = 0; rg < 2; rg++) {
+        // row pitch and 34 * (even b) are multiples of 4: an even block's
+        // scale opens a dword and its quants start 2 bytes in; an odd
+        // block's scale closes a dword and its quants are dword-aligned
+        const uint8_t *rp = wl + (32 * wave + 16 * rg + j) * kWideWPitch + 34 * b;
+        uint32_t qa, qc;
+        if ((b & 1) == 0) {
+          const uint32_t *wq = (const uint32_t *)(rp + 8 * g);
+          const uint32_t e0 = wq[0], e1 = wq[1], e2 = wq[2];
+          qa = __builtin_amdgcn_perm(e1, e0, 0x05040302u);
+          qc = __builtin_amdgcn_perm(e2, e1, 0x05040302u);
+          sc[rg] = (float)__builtin_bit_cast(
+              _Float16, (uint16_t)(((const uint32_t *)rp)[0] & 0xFFFFu));
+        } else {
+          const uint32_t *wq = (const uint32_t *)(rp + 2 + 8 * g);
+          qa = wq[0];
+          qc = wq[1];
+          sc[rg] = (float)__builtin_bit_cast(
+              _Float16, (uint16_t)(((const uint32_t *)(rp - 2))[0] >> 16));
+        }
+        qb[rg] = quants_bf16(qa, qc);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        if (c < ncg) {
+          const u32x4 xa = *(const u32x4 *)(xl + c * 16 * kWideXPitch + j * kWideXPitch +
+                                            2 * (32 * b + 8 * g));
+#pragma unroll
+          for (int rg = 0; rg < 2; rg++) {
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, xa), qb[rg], zero, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[rg][c][r] = fmaf(sc[rg], d[r], acc[rg][c][r]);
+          }
+        }
+      }
+    }
+
+    if (cur.kc + 1 == nchunks) {  // the tile is complete: outputs and keys
+      const bool keys = cur.d.idx != nullptr;
+#pragma unroll
+      for (int rg = 0; rg < 2; rg++) {
+        const int32_t row = 32 * wave + 16 * rg + j;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const float v = acc[rg][c][r] + __shfl_xor(acc[rg][c][r], 32, 64);
+            const int xr = 8 * c + 4 * (g & 1) + r;
+            if (g < 2 && c < ncg && xr < m && row < cur.rows) {
+              if (cur.d.y) store_y(&cur.d.y[(int64_t)xr * cur.d.p + cur.r0 + row], v);
+              if (keys) best[c][r] = umax64(best[c][r], argmax_key(v, (uint32_t)(cur.r0 + row)));
+            }
+          }
+        }
+      }
+      if (keys && (nxt.desc < 0 || nxt.desc != cur.desc)) {
+        // per x row: the maximum over the 16 lanes of each row, then over waves
+        __syncthreads();  // lk (after the x chunk) is free
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const unsigned long long k = row16_max(best[c][r]);
+            const int xr = 8 * c + 4 * (g & 1) + r;
+            if ((lane & 15) == 15 && g < 2 && xr < 32) lk[wave][xr] = xr < m ? k : 0ull;
+            best[c][r] = 0ull;
+          }
+        }
+        argmax_arrive(lk, m, cur.d.slot, cur.d.idx, blockIdx.x, gridDim.x);
+      }
+      t += stride;
+    }
+    if (nxt.desc < 0) break;
+    cur = nxt;
+  }
+}
+
+
 // ---- kernels -----------------------------------------------------------------
 
 // One matvec (descriptor passed by value), its tiles round-robin over the
@@ -1278,6 +1517,25 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   }
 }
 
+// Wide batches (8 < m <= 32): one matvec (tiles round-robin over the grid),
+// or every tile of a descriptor table in workgroup groups, as the kernels
+// above.
+__global__ void __launch_bounds__(kWG, 2) wide_mv_kernel(StepDesc d, int32_t m) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  OneSrc src{d};
+  wide_tiles(src, blockIdx.x, tiles_of(d), gridDim.x, m, lds);
+}
+
+__global__ void __launch_bounds__(kWG, 2)
+wide_step_kernel(const StepDesc *__restrict__ table, int32_t count,
+                 const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  TableSrc src{table, count};
+  const WgGroup g = groups[blockIdx.x / group_size];
+  const int32_t j = (int32_t)blockIdx.x - g.first;
+  wide_tiles(src, g.t0 + j, g.t1, g.size, m, lds);
+}
+
 // ---- argmax over f32 logits ---------------------------------------------
 // grid.y = activation row; every workgroup of the grid arrives once.
 __global__ void __launch_bounds__(kWG)
@@ -1287,7 +1545,7 @@ argmax_rows(const float *__restrict__ logits, int32_t m, int32_t p,
   unsigned long long key = 0ull;
   for (int32_t e = blockIdx.x * kWG + threadIdx.x; e < p; e += gridDim.x * kWG)
     key = umax64(key, argmax_key(row[e], (uint32_t)e));
-  __shared__ unsigned long long lk[kWaves][8];
+  __shared__ unsigned long long lk[kWaves][32];
   key = wave_max64(key);
   if ((threadIdx.x & 63) == 0)
     for (int r = 0; r < m; r++) lk[threadIdx.x >> 6][r] = r == (int)blockIdx.y ? key : 0ull;
@@ -1305,6 +1563,7 @@ size_t lds_bytes_i8x(int m, int n) {
 
 size_t lds_bytes_for(int m, int n) {
   const int path = path_of(m, n);
+  if (path == kWide) return kWideLds;
   if (m == 1) {  // the x region starts after the tile region
     const size_t x = path == kGeneric ? 0 : (size_t)x_lds_floats(m, n);
     return kTileMaxBytes + x * sizeof(float);
@@ -1352,6 +1611,13 @@ int mv_grid_cap(int dev) {
   return c;
 }
 
+int wide_grid_cap(int dev) {
+  static int cache[64] = {0};
+  int &c = cache[dev & 63];
+  if (!c) c = resident_wgs(wide_mv_kernel, kWideLds, dev);
+  return c;
+}
+
 template <bool M1, bool ANY, bool I8X>
 hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   int dev = 0;
@@ -1391,12 +1657,16 @@ size_t step_lds_bytes(int m, int n, bool i8x) {
 
 bool step_all_staged(int m, int n, bool i8x) {
   if (i8x) return i8x_shape_ok(n);
+  if (m > kMaxM) return true;  // one kernel for every wide matvec
   return path_of(m, n) == (m == 1 ? kStaged : kMfma);
 }
+
+bool wide_shape_ok(int n) { return n > 0 && n % 256 == 0; }
 
 bool i8x_shape_ok(int n) { return path_of(1, n) == kStaged; }
 
 int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x) {
+  if (m > kMaxM) return resident_wgs(wide_step_kernel, lds, device);
   if (i8x)
     return m == 1 ? resident_wgs(step_kernel<true, false, true>, lds, device)
                   : resident_wgs(step_kernel<false, false, true>, lds, device);
@@ -1421,6 +1691,15 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
   d.p = p;
   d.tile_begin = 0;
   d.rows_per_tile = tile_rows_of(i8x ? 1 : m, n);
+  if (m > kMaxM) {  // wide batch: 128-row tiles round-robin over the grid
+    const int32_t ntiles = tiles_of(d);
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const int cap = wide_grid_cap(dev);
+    const int grid = ntiles < cap ? ntiles : cap;
+    hipLaunchKernelGGL(wide_mv_kernel, dim3(grid), dim3(kWG), kWideLds, s, d, m);
+    return hipGetLastError();
+  }
   const int path = i8x ? (int)kStaged : path_of(m, n);
   // small matvecs: shorter tiles spread them over more workgroups (batched
   // tiles stay whole 16-row groups)
@@ -1446,6 +1725,12 @@ hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi) {
   if (epi && (m != 1 || i8x)) return hipErrorInvalidValue;  // m = 1 binary32 only
+  if (m > kMaxM) {
+    if (i8x) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(wide_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,
+                       group_size, m);
+    return hipGetLastError();
+  }
   if (i8x) {
     if (m == 1)
       hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,

@@ -74,8 +74,10 @@ def test_matvec_refusals(lib, args, want):
 
 
 @pytest.mark.parametrize("m,n,p,want", [
-    (0, 32, 1, SHAPE), (9, 32, 1, SHAPE), (-1, 32, 1, SHAPE),
+    (0, 32, 1, SHAPE), (33, 256, 1, SHAPE), (-1, 32, 1, SHAPE),
     (2, 31, 1, SHAPE), (2, 32, -5, SHAPE),
+    # more than 8 rows: n a positive multiple of 256
+    (9, 32, 1, SHAPE), (9, 0, 1, SHAPE), (32, 1000, 1, SHAPE), (16, 288, 4, SHAPE),
 ])
 def test_batched_refusals(lib, m, n, p, want):
     assert lib.q8_matvec_batched(W, X, Y, m, n, p, None) == want
@@ -84,7 +86,7 @@ def test_batched_refusals(lib, m, n, p, want):
 def test_argmax_refusals(lib):
     assert lib.q8_argmax(X, 1, 0, I, None) == SHAPE
     assert lib.q8_argmax(X, 0, 5, I, None) == SHAPE
-    assert lib.q8_argmax(X, 9, 5, I, None) == SHAPE
+    assert lib.q8_argmax(X, 33, 5, I, None) == SHAPE
     assert lib.q8_argmax(None, 1, 5, I, None) == NULL
     assert lib.q8_argmax(X, 1, 5, None, None) == NULL
     assert lib.q8_argmax(X + 2, 1, 5, I, None) == ALIGN
@@ -94,6 +96,7 @@ def test_argmax_refusals(lib):
 def test_matvec_argmax_refusals(lib):
     assert lib.q8_matvec_argmax(W, X, None, None, 1, 32, 4, None) == NULL
     assert lib.q8_matvec_argmax(W, X, None, I, 1, 32, 0, None) == SHAPE
+    assert lib.q8_matvec_argmax(W, X, None, I, 33, 256, 4, None) == SHAPE
     assert lib.q8_matvec_argmax(W, X, None, I, 9, 32, 4, None) == SHAPE
     assert lib.q8_matvec_argmax(None, X, None, I, 1, 32, 4, None) == NULL
     assert lib.q8_matvec_argmax(W, X, Y + 1, I, 1, 32, 4, None) == ALIGN
@@ -251,3 +254,9 @@ def test_decode_graph_refusals(lib):
     assert call(buf_over=dict(q=0x8000008)) == ALIGN
     assert call(buf_over=dict(logits=0x8000004)) == ALIGN
     assert h.value is None
+
+
+def test_wide_batch_int8_refusals(lib):
+    """The int8-activation entry points take at most 8 rows."""
+    assert lib.q8_matvec_i8x(W, X, Y, 9, 256, 4, None) == SHAPE
+    assert lib.q8_matvec_argmax_i8x(W, X, None, I, 9, 256, 4, None) == SHAPE
