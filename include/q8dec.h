@@ -217,8 +217,9 @@ int q8_step_graph_build_levels(const q8_matvec_desc *descs, const int32_t *level
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
 /* All but Q8_GRAPH_CHAIN: enqueues the same recorded step (its kernel, or
- * its kernels in level order, with the arguments fixed at build time) with
- * kernel launches instead of hipGraphLaunch: the same work, results and
+ * its kernels in level or node order, with the arguments fixed at build
+ * time; for Q8_GRAPH_DECODE the 5 * n_layers + 2 kernels of the decode step)
+ * with kernel launches instead of hipGraphLaunch: the same work, results and
  * host_idx writes.  Runs on the graph's device whatever device is current; `stream`
  * must belong to that device.  On MI355X with ROCm 7.2 a hipGraphLaunch
  * costs ~10 us more launch latency than a kernel launch (measured).
@@ -261,10 +262,11 @@ typedef struct {
                                            key (after QK-norm and RoPE) and value */
 } q8_decode_layer;
 
-/* The model: shapes (head_dim must be 128; n_heads a multiple of n_kv_heads,
- * at most 4 query heads per key/value head; hidden <= 4096; hidden, inter
- * multiples of 32; 1 <= cache_rows <= 65536), eps and theta, a HOST array
- * of n_layers layers, and the final norm and lm_head (device). */
+/* The model: shapes (1 <= n_layers <= 512; head_dim must be 128; n_heads a
+ * multiple of n_kv_heads, at most 4 query heads per key/value head;
+ * hidden <= 4096; hidden, inter multiples of 32; 1 <= cache_rows <= 65536;
+ * eps >= 0 and theta > 0, finite), a HOST array of n_layers layers, and the
+ * final norm and lm_head (device). */
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, cache_rows;
   float eps, theta;
