@@ -231,6 +231,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     t.tile_begin = (int32_t)tiles;
     tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
     if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
+    t.tile_end = (int32_t)tiles;
     const size_t l = step_lds_bytes(m, d.n, i8x);
     if (l > widest) widest = l;
     plan.all_staged = plan.all_staged && step_all_staged(m, d.n, i8x);
@@ -273,6 +274,10 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     if (e < gr.t0) e = gr.t0;
     gr.t1 = e;
     prev_end = e;
+    // the last descriptor starting at or before t0 (empty ones skipped)
+    gr.d0 = 0;
+    for (int32_t i = 0; i < count; i++)
+      if (plan.descs[i].tile_begin <= gr.t0) gr.d0 = i;
   }
   // arrivals of each argmax descriptor, by team
   plan.expected.clear();

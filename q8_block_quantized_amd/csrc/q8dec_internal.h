@@ -54,7 +54,7 @@ struct StepDesc {
   int32_t tile_begin;     // first tile of this matvec in the launch
   int32_t rows_per_tile;
   int32_t flags;          // kDescDeviceOut: outputs stored at device scope
-  int32_t pad;
+  int32_t tile_end;       // one past its last tile: tile_begin + ceil(p / rows_per_tile)
 };
 // y is stored with device-scope stores, so that the launch's epilogue (m = 1)
 // can read it (see Epilogue); otherwise y takes plain stores.
@@ -63,10 +63,13 @@ static_assert(sizeof(StepDesc) == 64, "descriptor layout");
 
 // Workgroups g in [first, first + size) of a persistent step share the
 // contiguous tile range [t0, t1), interleaved: workgroup first + j takes
-// tiles t0 + j, t0 + j + size, ...
+// tiles t0 + j, t0 + j + size, ...  d0: the descriptor holding tile t0 (a
+// start for the workgroups' descriptor search).
 struct WgGroup {
   int32_t t0, t1, first, size;
+  int32_t d0, pad[3];
 };
+static_assert(sizeof(WgGroup) == 32, "group layout");
 
 // Launches y = W x (m rows) with an optional fused argmax.  slot/idx are
 // both NULL for a plain matvec.  y may be NULL only when idx is set.  i8x:

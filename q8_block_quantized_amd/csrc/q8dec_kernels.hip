@@ -582,13 +582,25 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
   const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
   const int wave = threadIdx.x >> 6;
   const int32_t pitch = bpr * 34;
+  // A staged row pitch is a multiple of 16, so a block's byte offset mod 4
+  // follows from its index alone: 2 for odd blocks, 0 for even ones (and
+  // k + 32 i has the parity of k).
+  const uint32_t amod = (uint32_t)(k & 1) << 1;
+  const uint32_t sel = quant_sel(amod);
   // With one block per lane (n <= 1024) the lane's 32 x values are the same
   // for every row: they are read from LDS once per tile.
   float xk[32];
   if (NBL == 1) load_x32(xs + 36 * min(k, bpr - 1), xk);
+  // The row-owning lane's best row of the tile for the argmax: the first
+  // value that is not NaN, then only strictly larger ones.  Its rows ascend,
+  // so among equal values (-0 and +0 included) the lowest row stays, as the
+  // keys order them; the key is formed once per tile.
+  float bv = __builtin_nanf("");
+  int32_t br = 0;
   for (int32_t rr0 = 2 * wave; rr0 < rows; rr0 += kRowsPerPass) {
+    // rr may be `rows` (odd row count): that window lies in the x region of
+    // LDS, and its sum is dropped
     const int32_t rr = rr0 + half;
-    const int32_t rc = rr < rows ? rr : rows - 1;
     float acc = 0.f;
     // keeps the x reads inside the loop (hoisted, they would pin 32 * NBL
     // registers for the whole tile)
@@ -596,12 +608,10 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
 #pragma unroll
     for (int i = 0; i < NBL; i++) {
       const int32_t b = min(k + 32 * i, bpr - 1);
-      const int32_t o = rc * pitch + 34 * b;
-      const uint32_t *wp = tl + (o >> 2);
+      const uint32_t *wp = tl + ((rr * pitch + 34 * b) >> 2);
       uint32_t d[9];
 #pragma unroll
       for (int q = 0; q < 9; q++) d[q] = wp[q];
-      const uint32_t amod = (uint32_t)o & 2u;
       float xb[32];
       if (NBL == 1) {
 #pragma unroll
@@ -609,15 +619,17 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
       } else {
         load_x32(xs + 36 * b, xb);
       }
-      const float v = scale_of(d, amod) * block_dot(d, quant_sel(amod), xb);
+      const float v = scale_of(d, amod) * block_dot(d, sel, xb);
       acc += (k + 32 * i < bpr) ? v : 0.f;
     }
     acc = half_wave_sum(acc);
-    if (k == 31 && rr < rows) {
-      if (y) store_y(&y[r0 + rr], acc, DEVY);
-      if (keys) best = umax64(best, argmax_key(acc, (uint32_t)(r0 + rr)));
-    }
+    const bool mine = k == 31 && rr < rows;
+    if (mine && y) store_y(&y[r0 + rr], acc, DEVY);
+    const bool better = mine & ((acc > bv) | ((bv != bv) & (acc == acc)));  // no branches
+    bv = better ? acc : bv;
+    br = better ? rr : br;
   }
+  if (keys && bv == bv) best = umax64(best, argmax_key(bv, (uint32_t)(r0 + br)));
 }
 
 // ---- int8-activation variant -----------------------------------------------
@@ -1020,7 +1032,8 @@ struct Prefetch {
     for (int j = 0; j < XC; j++) {
       const int32_t c = j * kWG + (int32_t)threadIdx.x;
       if (c < chunks) {
-        const int32_t i = c / row_chunks, e = (c - i * row_chunks) * 4;
+        // one row (m = 1) needs no division
+        const int32_t i = m == 1 ? 0 : c / row_chunks, e = (c - i * row_chunks) * 4;
         *(f32x4 *)&xs[i * 36 * bpr + 36 * (e >> 5) + (e & 31)] = x[j];
       }
     }
@@ -1110,30 +1123,33 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   int32_t t = first;
   if (t >= end) return;
   Prefetch<XC, CH> pf;
+  // The job of tile tn, a later tile than `from`'s: the same matvec, or one
+  // found in the table.
+  auto job_after = [&](const Job &from, int32_t tn) {
+    if (tn < from.d.tile_end) return job_at(from.desc, from.d, tn, m);
+    const int32_t dn = src.find(tn, from.desc + 1);
+    return job_at(dn, src.get(dn), tn, m);
+  };
   int32_t di = src.find(t, d_hint);
   Job cur = job_at(di, src.get(di), t, m);
+  bool more = t + stride < end;
+  Job nxt = more ? job_after(cur, t + stride) : cur;
   if (staged(cur) || mfma(cur))
     pf.load_w(cur.d.w + (uint64_t)cur.r0 * (cur.d.n >> 5) * 34u,
               cur.rows * (cur.d.n >> 5) * 34);
   if (x_in_lds(cur)) pf.load_x(cur.d.x, m * cur.d.n);
-  int32_t xdesc = -1, xadesc = -1;
+  // the x staged in LDS (and the batched path's operand A): matvecs that
+  // share x (the same pointer and width) are staged once
+  const float *xptr = nullptr, *xaptr = nullptr;
+  int32_t xn = 0, xan = 0;
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
   u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
   for (;;) {
     const int32_t tn = t + stride;
-    const bool more = tn < end;
-    Job nxt = cur;
-    if (more) {
-      if (tn < cur.d.tile_begin + tiles_of(cur.d)) {
-        nxt = job_at(cur.desc, cur.d, tn, m);
-      } else {
-        const int32_t dn = src.find(tn, cur.desc + 1);
-        nxt = job_at(dn, src.get(dn), tn, m);
-      }
-    }
     const int32_t bpr = cur.d.n >> 5;
-    const bool new_x = x_in_lds(cur) && cur.desc != xdesc;
+    const bool x_changed = cur.d.x != xptr || cur.d.n != xn;
+    const bool new_x = x_in_lds(cur) && x_changed;
     __syncthreads();  // the previous tile's readers of LDS are done
     if (staged(cur)) pf.store_w(tl, cur.rows * bpr * 34);
     else if (mfma(cur)) pf.store_w_rows(tl, cur.rows * bpr * 34, bpr * 34);
@@ -1141,27 +1157,39 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       if (I8X) pf.store_xq(xq, xd, m, cur.d.n);
       else pf.store_x(xs, m, cur.d.n);
     }
-    if (I8X && !M1 && cur.desc != xdesc) {  // batched: quantised straight from memory
-      quantize_x_lds<kWG>(cur.d.x, m, cur.d.n, xq, xd);
-      xdesc = cur.desc;
-    }
+    const bool quant_x = I8X && !M1 && x_changed;  // batched: straight from memory
+    if (quant_x) quantize_x_lds<kWG>(cur.d.x, m, cur.d.n, xq, xd);
     __syncthreads();
-    if (new_x) xdesc = cur.desc;
+    if (new_x || quant_x) {
+      xptr = cur.d.x;
+      xn = cur.d.n;
+    }
     // a new matvec's operand A is loaded before the next tile's bytes are
     // requested, so waiting for it does not wait for them
-    if (mfma(cur) && cur.desc != xadesc) {
+    if (mfma(cur) && (cur.d.x != xaptr || cur.d.n != xan)) {
       if (bpr == 32) load_xa<8>(xa, cur.d.x, m, cur.d.n);
       else if (bpr == 64) load_xa<16>(xa, cur.d.x, m, cur.d.n);
       else load_xa<24>(xa, cur.d.x, m, cur.d.n);
-      xadesc = cur.desc;
+      xaptr = cur.d.x;
+      xan = cur.d.n;
     }
     if (more) {  // next tile's bytes go out before this tile is computed
+      // x first: a few scattered lines, slower to arrive than the tile's
+      // streamed bytes, so its latency overlaps theirs rather than following
+      if (x_in_lds(nxt) && (nxt.d.x != xptr || nxt.d.n != xn))
+        pf.load_x(nxt.d.x, m * nxt.d.n);
       if (staged(nxt) || mfma(nxt))
         pf.load_w(nxt.d.w + (uint64_t)nxt.r0 * (nxt.d.n >> 5) * 34u,
                   nxt.rows * (nxt.d.n >> 5) * 34);
-      if (x_in_lds(nxt) && nxt.desc != cur.desc)
-        pf.load_x(nxt.d.x, m * nxt.d.n);
     }
+    // The job two tiles ahead.  A new matvec's descriptor is read from the
+    // table here, so its scalar loads complete while this tile is computed:
+    // read at the top of the next round, they would hold its first barrier
+    // (which waits for every outstanding scalar load) and with it the next
+    // tile's loads.
+    const int32_t tn2 = tn + stride;
+    const bool more2 = more && tn2 < end;
+    const Job nxt2 = more2 ? job_after(nxt, tn2) : nxt;
     const bool keys = cur.d.idx != nullptr;
     const bool devy = M1 && !I8X && (cur.d.flags & kDescDeviceOut);
     if (I8X) {
@@ -1242,6 +1270,8 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     if (!more) break;
     t = tn;
     cur = nxt;
+    nxt = nxt2;
+    more = more2;
   }
 }
 
@@ -1491,7 +1521,7 @@ __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
-  run_tiles<M1, ANY, I8X>(src, blockIdx.x, tiles_of(d), gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X>(src, blockIdx.x, d.tile_end, gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
@@ -1508,7 +1538,7 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, 0, m, lds);
+  run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, g.d0, m, lds);
   if constexpr (M1 && !I8X) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
@@ -1639,6 +1669,7 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
     d.rows_per_tile = best_rows;
   }
   const int32_t ntiles = tiles_of(d);
+  d.tile_end = ntiles;
   const int grid = ntiles < cap ? ntiles : cap;
   hipLaunchKernelGGL((mv_kernel<M1, ANY, I8X>), dim3(grid), dim3(kWG),
                      I8X ? lds_bytes_i8x(m, d.n) : lds_bytes_for(m, d.n), s, d, m);
@@ -1691,6 +1722,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
   d.p = p;
   d.tile_begin = 0;
   d.rows_per_tile = tile_rows_of(i8x ? 1 : m, n);
+  d.tile_end = tiles_of(d);
   if (m > kMaxM) {  // wide batch: 128-row tiles round-robin over the grid
     const int32_t ntiles = tiles_of(d);
     int dev = 0;
