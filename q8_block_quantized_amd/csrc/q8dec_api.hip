@@ -290,7 +290,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
       const int32_t u = gr.t0 > tb ? gr.t0 : tb, v = gr.t1 < te ? gr.t1 : te;
       if (u >= v) continue;
       for (int32_t j = 0; j < gr.size; j++) {
-        int32_t t = gr.t0 + j;
+        int32_t t = gr.t0 + group_slot(j, gr.first, gr.size);
         if (t < u) t += (u - t + gr.size - 1) / gr.size * gr.size;
         if (t < v) team[(gr.first + j) % kArgmaxTeams]++;
       }

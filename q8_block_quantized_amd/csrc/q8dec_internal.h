@@ -44,6 +44,10 @@ struct ArgmaxSlot {
 };
 
 // One matvec of a launch, as the kernels see it.
+#ifndef Q8_XCD_SLOTS
+#define Q8_XCD_SLOTS 1
+#endif
+
 struct StepDesc {
   const uint8_t *w;
   const float *x;
@@ -70,6 +74,16 @@ struct WgGroup {
   int32_t d0, pad[3];
 };
 static_assert(sizeof(WgGroup) == 32, "group layout");
+
+// The first tile offset (within its group's range) of the group's j-th
+// workgroup.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b
+// runs on XCD b % 8), so when the group is a whole number of XCD rounds the
+// offsets are dealt so that consecutive tiles run on one XCD: their outputs
+// share 128-byte lines, which one L2 then writes back whole.
+__host__ __device__ inline int32_t group_slot(int32_t j, int32_t first, int32_t size) {
+  if (!Q8_XCD_SLOTS || (first & 7) || (size & 7)) return j;
+  return (j & 7) * (size >> 3) + (j >> 3);
+}
 
 // Launches y = W x (m rows) with an optional fused argmax.  slot/idx are
 // both NULL for a plain matvec.  y may be NULL only when idx is set.  i8x:

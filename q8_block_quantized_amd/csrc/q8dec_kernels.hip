@@ -1538,7 +1538,8 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY, I8X>(src, g.t0 + j, g.t1, g.size, g.d0, m, lds);
+  run_tiles<M1, ANY, I8X>(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, g.d0, m,
+                          lds);
   if constexpr (M1 && !I8X) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
@@ -1563,7 +1564,7 @@ wide_step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  wide_tiles(src, g.t0 + j, g.t1, g.size, m, lds);
+  wide_tiles(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, m, lds);
 }
 
 // ---- argmax over f32 logits ---------------------------------------------
