@@ -1521,7 +1521,11 @@ __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
-  run_tiles<M1, ANY, I8X>(src, blockIdx.x, d.tile_end, gridDim.x, 0, m, lds);
+  // tiles round-robin over the grid; within each 32 workgroups, runs of
+  // four consecutive tiles on one XCD (as the step's groups)
+  const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
+  const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
+  run_tiles<M1, ANY, I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
@@ -1658,7 +1662,10 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   // part-empty.  Among tile heights from the largest down to three quarters
   // of it, take the one whose busiest workgroup costs least, counting a
   // tile as its rows plus four rows' worth of fixed work (barriers, LDS
-  // staging).  Batched tiles stay whole 16-row groups.
+  // staging).  Batched tiles stay whole 16-row groups.  (Whole rounds of
+  // two tile heights, 21 and 22 rows for the lm_head, measured 1.5 us
+  // slower: more tiles, and a part-empty last round also frees bandwidth
+  // for the workgroups still running.)
   if ((I8X || path_of(m, d.n) != kMfma) && tiles_of(d) > cap) {
     int32_t best_rows = d.rows_per_tile;
     int64_t best_cost = INT64_MAX;
@@ -1713,7 +1720,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
                          int n, int p, ArgmaxSlot *slot, int32_t *idx,
                          hipStream_t s, bool i8x) {
   if (p <= 0) return hipSuccess;
-  StepDesc d;
+  StepDesc d{};  // flags 0: plain stores, tiles of equal height
   d.w = w;
   d.x = x;
   d.y = y;
