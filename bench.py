@@ -134,7 +134,7 @@ def settle(torch, fn, seconds: float = SETTLE_S) -> None:
 
 
 def time_graph_steps(torch, graphs, host, steps: int, warmup: int,
-                     poll: bool = False):
+                     poll: bool = False, spread: dict = None):
     """Wall seconds per step of: launch the step graph, wait, read the token.
     The wait is a stream synchronisation (every output complete), or with
     poll=True a spin on the pinned token slot, which the kernel writes last
@@ -164,9 +164,19 @@ def time_graph_steps(torch, graphs, host, steps: int, warmup: int,
         one(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    toks = [one(k) for k in range(steps)]
+    toks = []
+    stamps = [t0]
+    for k in range(steps):
+        toks.append(one(k))
+        stamps.append(time.perf_counter())
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps, toks
+    sec = (time.perf_counter() - t0) / steps
+    if spread is not None:  # per-step wall times: p10, median, p90 (us)
+        per = sorted(b - a for a, b in zip(stamps, stamps[1:]))
+        spread.update(p10=round(per[len(per) // 10] * 1e6, 2),
+                      median=round(statistics.median(per) * 1e6, 2),
+                      p90=round(per[(9 * len(per)) // 10] * 1e6, 2))
+    return sec, toks
 
 
 def event_time(torch, fn, count: int, warmup: int = 3) -> float:
@@ -372,8 +382,9 @@ def main() -> int:
     # the headline waits for the token the way a decode loop does: spinning
     # on the pinned slot the kernel writes last; the fully synchronised
     # figure (every output of the step complete) is reported beside it
+    spread = {}
     sec, toks = time_graph_steps(torch, pers, host, args.steps, args.warmup,
-                                 poll=True)
+                                 poll=True, spread=spread)
     ssec, stoks = time_graph_steps(torch, pers, host, args.steps, args.warmup)
     assert stoks == toks, "token differs between the two waits"
     # the same recorded step submitted as one kernel launch instead of a
@@ -416,6 +427,7 @@ def main() -> int:
             "graph_nodes": {"kernel": 1, "memcpy": 0},
         },
         "step_latency_us": round(sec * 1e6, 2),
+        "step_latency_spread_us": spread,
         "step_latency_synchronized_us": round(ssec * 1e6, 2),
         "step_latency_kernel_launch_us": round(ksec * 1e6, 2),
         "pct_of_hbm_peak": round(100 * step_bytes / sec / 1e9 / HBM_PEAK_GBS, 2),
@@ -494,17 +506,24 @@ def main() -> int:
             "GBps": round(lb0 / lt0 / 1e9, 1),
         }
 
-        log("single matvec 1024->2048 (rotating 56 layer copies)")
-        qs = [d for s in sets for d in s.descs if d["p"] == 2048 and d["n"] == 1024]
+        log("single matvec 1024->2048 (rotating 240 copies, 535 MB)")
+        qs = [d["w"] for s in sets for d in s.descs if d["p"] == 2048 and d["n"] == 1024]
+        qs += [torch.from_numpy(gen.weights(2048, 1024, seed=0, index=4000 + c)
+                                .reshape(-1)).to(dev) for c in range(240 - len(qs))]
+        qx = sets[0].descs[0]["x"].view(-1)
         qy = torch.empty(2048, dtype=torch.float32, device=dev)
-        st = event_time(torch, lambda k: q8.q8_matvec(
-            qs[k % len(qs)]["w"], qs[k % len(qs)]["x"].view(-1), qy), 112)
+        st = event_time(torch, lambda k: q8.q8_matvec(qs[k % len(qs)], qx, qy), 240)
+        hot = event_time(torch, lambda k: q8.q8_matvec(qs[0], qx, qy), 240)
         sb = alg_bytes(1024, 2048, 1, True, False)
         extra["single_matvec_1024x2048"] = {
             "avg_us": round(st * 1e6, 2),
             "GBps": round(sb / st / 1e9, 1),
-            "note": "back-to-back launches, 56 distinct copies (125 MB) rotated",
+            "matvecs_per_s": round(1.0 / st, 1),
+            "hot_avg_us": round(hot * 1e6, 2),
+            "note": ("back-to-back launches over 240 distinct weight copies (535 MB, "
+                     "beyond the 256 MB Infinity Cache); hot: one copy, cached"),
         }
+        del qs
 
         log("one layer: 7 matvecs back to back (56 layers rotated)")
         layers = [s.descs[7 * l:7 * l + 7] for s in sets for l in range(28)]
