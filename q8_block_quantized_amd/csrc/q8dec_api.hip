@@ -128,6 +128,7 @@ struct SegmentLaunch {
   bool all_staged;
   int kind = kStepNode;
   const q8::Epilogue *epi = nullptr;
+  const q8::Epilogue *pro = nullptr;
   q8::AttnArgs attn{};
   const float *nx = nullptr, *nw = nullptr;
   float *nout = nullptr, *ncopy = nullptr;
@@ -144,7 +145,7 @@ hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
     return q8::launch_step_start(L.nx, L.nw, L.nout, L.ncopy, L.ndim, L.neps, L.npos,
                                  L.nfreq, L.rope_out, s);
   return q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
-                         L.all_staged, s, i8x, L.epi);
+                         L.all_staged, s, i8x, L.epi, L.pro);
 }
 
 struct q8_step_graph {
@@ -690,10 +691,16 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   lv.push_back({mv(M.lm_head, B.xf, B.logits, B.token, H, M.vocab)});
   std::vector<q8::StepPlan> plans(lv.size());
   for (size_t i = 0; i < lv.size(); i++) {
-    const bool epi = i + 1 < lv.size() && i % 4 != 0;  // o, gate/up, down
     st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
                        plans[i]);
     if (st) return st;
+  }
+  // SwiGLU: computed by every workgroup of the down launch into its staged x
+  // (a prologue) when that launch is all staged, else by the last workgroup
+  // of the gate/up launch (an epilogue)
+  const bool silu_pro = plans[3].all_staged && I <= 3072;
+  for (size_t i = 0; i + 1 < lv.size(); i++) {
+    const bool epi = i % 4 == 1 || i % 4 == 3 || (i % 4 == 2 && !silu_pro);
     if (epi)  // their outputs are read by the epilogue
       for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
   }
@@ -766,7 +773,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     E[0].g = L.ffn_norm;
     E[0].out = B.xn2;
     E[0].arrive = earr;
-    E[1].op = q8::kEpiSiluMul;  // after gate/up: h = silu(gate) * up
+    E[1].op = q8::kEpiSiluMul;  // h = silu(gate) * up (down's prologue, or gate/up's epilogue)
     E[1].n = I;
     E[1].r = B.up;
     E[1].g = B.gate;
@@ -798,11 +805,12 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     return hip_fail(e);
   }
 
-  auto step_node = [&](size_t i, const q8::Epilogue *epi) {
+  auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Epilogue *pro = nullptr) {
     const q8::StepPlan &pl = plans[i];
     SegmentLaunch L{(const q8::StepDesc *)(ws + o_tab[i]), (const q8::WgGroup *)(ws + o_grp[i]),
                     (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged};
     L.epi = epi;
+    L.pro = pro;
     g->launches.push_back(L);
   };
   {
@@ -843,8 +851,13 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     A.attn.eps = M.eps;
     g->launches.push_back(A);
     step_node(4 * (size_t)l + 1, &epis[3 * (size_t)l]);
-    step_node(4 * (size_t)l + 2, &epis[3 * (size_t)l + 1]);
-    step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2]);
+    if (silu_pro) {
+      step_node(4 * (size_t)l + 2, nullptr);
+      step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2], &epis[3 * (size_t)l + 1]);
+    } else {
+      step_node(4 * (size_t)l + 2, &epis[3 * (size_t)l + 1]);
+      step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2]);
+    }
   }
   step_node(plans.size() - 1, nullptr);
   return capture_graph(g, out, [&](hipStream_t cs) {

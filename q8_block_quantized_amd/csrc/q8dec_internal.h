@@ -113,7 +113,7 @@ struct Epilogue;
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x = false,
-                       const Epilogue *epi = nullptr);
+                       const Epilogue *epi = nullptr, const Epilogue *pro = nullptr);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
@@ -160,6 +160,10 @@ const void *probe_kernel();
 //   kEpiSiluMul: out = g / (1 + e^-g) * r over n values (silu_hadamard,
 //                g the gate, r the up projection).
 // `arrive` is a zeroed ArgmaxSlot used only for its counters.
+// The same record with kEpiSiluMul can also serve as a launch's prologue
+// (m = 1, every tile staged, n <= 3072): every workgroup computes out into
+// its staged x before its tiles, the launch's matvecs read x = out, and
+// workgroup 0 stores out as well (`arrive` unused).
 enum EpiOp : int32_t { kEpiNone = 0, kEpiAddNorm = 1, kEpiSiluMul = 2 };
 struct Epilogue {
   int32_t op, n;

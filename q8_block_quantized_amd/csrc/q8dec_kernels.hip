@@ -1093,6 +1093,39 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
   return j;
 }
 
+// The staged x of a launch whose x is silu_hadamard's output (the decode
+// step's down projection): out = gate / (1 + e^-gate) * up over n values
+// (n a multiple of 32, at most 3072), written into the padded LDS layout of
+// the x region by every workgroup, and to `out` in memory by one (`keep`).
+// It replaces a last-workgroup epilogue on the gate/up launch.
+__device__ __forceinline__ void silu_mul_x(const float *gate, const float *up, float *out,
+                                           int32_t n, float *xs, bool keep) {
+  constexpr int K = 3;  // float4 chunks per thread: 3 * 256 * 4 >= 3072
+  f32x4 gv[K], uv[K];
+  const int32_t chunks = n >> 2;
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    const int32_t c = (int32_t)threadIdx.x + k * kWG;
+    gv[k] = uv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < chunks) {
+      gv[k] = gp((const f32x4 *)gate)[c];
+      uv[k] = gp((const f32x4 *)up)[c];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    const int32_t c = (int32_t)threadIdx.x + k * kWG;
+    if (c < chunks) {
+      f32x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; e++) h[e] = gv[k][e] / (1.0f + expf(-gv[k][e])) * uv[k][e];
+      const int32_t i = 4 * c;
+      *(f32x4 *)&xs[36 * (i >> 5) + (i & 31)] = h;
+      if (keep) gpw((f32x4 *)out)[c] = h;
+    }
+  }
+}
+
 // Tiles first, first + stride, ... (< end) of the launch, in order.  Each
 // tile's weights (and x, when the tile opens another matvec) are loaded into
 // registers while the previous tile is computed.  Tiles of one matvec are
@@ -1103,7 +1136,7 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
 template <bool M1, bool ANY, bool I8X, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
-                          float *lds) {
+                          float *lds, const Epilogue *pro = nullptr) {
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
   constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
@@ -1137,11 +1170,18 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   if (staged(cur) || mfma(cur))
     pf.load_w(cur.d.w + (uint64_t)cur.r0 * (cur.d.n >> 5) * 34u,
               cur.rows * (cur.d.n >> 5) * 34);
-  if (x_in_lds(cur)) pf.load_x(cur.d.x, m * cur.d.n);
   // the x staged in LDS (and the batched path's operand A): matvecs that
   // share x (the same pointer and width) are staged once
   const float *xptr = nullptr, *xaptr = nullptr;
   int32_t xn = 0, xan = 0;
+  if constexpr (M1 && !I8X) {
+    if (pro) {  // the launch's x is pro->out, computed here while the first tile loads
+      silu_mul_x(pro->g, pro->r, pro->out, pro->n, xs, blockIdx.x == 0);
+      xptr = pro->out;
+      xn = pro->n;
+    }
+  }
+  if (x_in_lds(cur) && (cur.d.x != xptr || cur.d.n != xn)) pf.load_x(cur.d.x, m * cur.d.n);
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
   u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
@@ -1537,13 +1577,13 @@ template <bool M1, bool ANY, bool I8X>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
-            const Epilogue *__restrict__ epi) {
+            const Epilogue *__restrict__ epi, const Epilogue *__restrict__ pro) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
   run_tiles<M1, ANY, I8X>(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, g.d0, m,
-                          lds);
+                          lds, pro);
   if constexpr (M1 && !I8X) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
@@ -1763,8 +1803,11 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
-                       bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi) {
-  if (epi && (m != 1 || i8x)) return hipErrorInvalidValue;  // m = 1 binary32 only
+                       bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi,
+                       const Epilogue *pro) {
+  // m = 1 binary32 only, and a prologue only where every tile is staged
+  if ((epi || pro) && (m != 1 || i8x)) return hipErrorInvalidValue;
+  if (pro && !all_staged) return hipErrorInvalidValue;
   if (m > kMaxM) {
     if (i8x) return hipErrorInvalidValue;
     hipLaunchKernelGGL(wide_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,
@@ -1774,26 +1817,26 @@ hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
   if (i8x) {
     if (m == 1)
       hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
     else
       hipLaunchKernelGGL((step_kernel<false, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
     return hipGetLastError();
   }
   if (m == 1) {
     if (all_staged)
       hipLaunchKernelGGL((step_kernel<true, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
     else
       hipLaunchKernelGGL((step_kernel<true, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
   } else {
     if (all_staged)
       hipLaunchKernelGGL((step_kernel<false, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
     else
       hipLaunchKernelGGL((step_kernel<false, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi);
+                         s, descs, count, groups, group_size, m, epi, pro);
   }
   return hipGetLastError();
 }
