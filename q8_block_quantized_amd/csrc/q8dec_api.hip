@@ -128,7 +128,7 @@ struct SegmentLaunch {
   bool all_staged;
   int kind = kStepNode;
   const q8::Epilogue *epi = nullptr;
-  const q8::Epilogue *pro = nullptr;
+  const q8::Prologue *pro = nullptr;
   q8::AttnArgs attn{};
   const float *nx = nullptr, *nw = nullptr;
   float *nout = nullptr, *ncopy = nullptr;
@@ -695,15 +695,18 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
                        plans[i]);
     if (st) return st;
   }
-  // SwiGLU: computed by every workgroup of the down launch into its staged x
-  // (a prologue) when that launch is all staged, else by the last workgroup
-  // of the gate/up launch (an epilogue)
-  const bool silu_pro = plans[3].all_staged && I <= 3072;
-  for (size_t i = 0; i + 1 < lv.size(); i++) {
-    const bool epi = i % 4 == 1 || i % 4 == 3 || (i % 4 == 2 && !silu_pro);
-    if (epi)  // their outputs are read by the epilogue
-      for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
-  }
+  // The element-wise steps between matvecs run as prologues when every
+  // launch is all staged and the vectors fit the staged x: each workgroup of
+  // the consuming launch computes its x (the residual adds and norms, the
+  // SwiGLU) while its first tile loads.  Otherwise they run as epilogues, by
+  // the last workgroup of the producing launch, whose outputs then take
+  // device-scope stores.
+  bool pro_path = H <= q8::kProMaxN && I <= q8::kProMaxN;
+  for (const auto &pl : plans) pro_path = pro_path && pl.all_staged;
+  if (!pro_path)
+    for (size_t i = 0; i + 1 < lv.size(); i++)
+      if (i % 4 != 0)  // o, gate/up, down: their outputs are read by the epilogue
+        for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
 
   q8_step_graph *g = new (std::nothrow) q8_step_graph();
   if (!g) return Q8_ERR_GRAPH;
@@ -728,6 +731,8 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   const size_t o_earr = take(sizeof(q8::ArgmaxSlot));
   const size_t o_aarr = take(sizeof(q8::ArgmaxSlot) * (size_t)M.n_kv_heads);
   const size_t o_epi = take(sizeof(q8::Epilogue) * 3 * (size_t)M.n_layers);
+  const size_t o_pro = take(sizeof(q8::Prologue) * 3 * (size_t)M.n_layers);
+  const size_t o_res = take(sizeof(float) * (size_t)H);  // the second residual buffer
   const size_t o_freq = take(sizeof(float) * q8::kAttnHeadDim / 2);
   const size_t o_rope = take(sizeof(float) * q8::kAttnHeadDim);
   const size_t o_part = take(sizeof(float) * (size_t)M.n_heads * chunks * q8::kAttnPart);
@@ -746,6 +751,14 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   q8::ArgmaxSlot *amax = (q8::ArgmaxSlot *)(ws + o_amax);
   q8::ArgmaxSlot *earr = (q8::ArgmaxSlot *)(ws + o_earr);
   q8::Epilogue *epis = (q8::Epilogue *)(ws + o_epi);
+  q8::Prologue *pros = (q8::Prologue *)(ws + o_pro);
+  // Prologue path: the residual stream after layer l, R_l, is written by
+  // the launch after that layer and read by the launches of the next, so it
+  // alternates between B.x and the workspace buffer, and the last one is
+  // in B.x: R_l lives in B.x when L - 1 - l is even (l = -1: the step's
+  // input, copied there by the first node).
+  float *const rbuf[2] = {B.x, (float *)(ws + o_res)};
+  auto resid = [&](int32_t l) { return rbuf[((M.n_layers - 1 - l) % 2 + 2) % 2]; };
   {
     q8::StepPlan &pl = plans.back();
     q8::ArgmaxSlot hs;
@@ -773,7 +786,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     E[0].g = L.ffn_norm;
     E[0].out = B.xn2;
     E[0].arrive = earr;
-    E[1].op = q8::kEpiSiluMul;  // h = silu(gate) * up (down's prologue, or gate/up's epilogue)
+    E[1].op = q8::kEpiSiluMul;  // after gate/up: h = silu(gate) * up
     E[1].n = I;
     E[1].r = B.up;
     E[1].g = B.gate;
@@ -791,6 +804,39 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   }
   if (e == hipSuccess)
     e = hipMemcpy(epis, he.data(), he.size() * sizeof(q8::Epilogue), hipMemcpyHostToDevice);
+  // prologues of layer l: 3l the gate/up launch's norm, 3l + 1 the down
+  // launch's SwiGLU, 3l + 2 the next layer's q/k/v launch's (or the
+  // lm_head's) residual add and norm
+  std::vector<q8::Prologue> hp(3 * (size_t)M.n_layers);
+  std::memset(hp.data(), 0, hp.size() * sizeof(q8::Prologue));
+  for (int32_t l = 0; l < M.n_layers; l++) {
+    const q8_decode_layer &L = M.layers[l];
+    q8::Prologue *P = &hp[3 * (size_t)l];
+    P[0].op = q8::kProAddNorm;  // xn2 = norm(R_{l-1} + attn_out)
+    P[0].n = H;
+    P[0].eps = M.eps;
+    P[0].a = resid(l - 1);
+    P[0].b = B.attn_out;
+    P[0].w = L.ffn_norm;
+    P[0].out = B.xn2;
+    P[1].op = q8::kProSiluMul;  // h = silu(gate) * up
+    P[1].n = I;
+    P[1].a = B.gate;
+    P[1].b = B.up;
+    P[1].out = B.h;
+    const bool lastl = l + 1 == M.n_layers;
+    P[2].op = q8::kProAddNorm;  // R_l = (R_{l-1} + attn_out) + ffn_out; the next xn, or xf
+    P[2].n = H;
+    P[2].eps = M.eps;
+    P[2].a = resid(l - 1);
+    P[2].b = B.attn_out;
+    P[2].c = B.ffn_out;
+    P[2].w = lastl ? M.out_norm : M.layers[l + 1].attn_norm;
+    P[2].out = lastl ? B.xf : B.xn;
+    P[2].resid = resid(l);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpy(pros, hp.data(), hp.size() * sizeof(q8::Prologue), hipMemcpyHostToDevice);
   for (size_t i = 0; i < plans.size() && e == hipSuccess; i++) {
     e = hipMemcpy(ws + o_tab[i], plans[i].descs.data(),
                   plans[i].descs.size() * sizeof(q8::StepDesc), hipMemcpyHostToDevice);
@@ -805,7 +851,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     return hip_fail(e);
   }
 
-  auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Epilogue *pro = nullptr) {
+  auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Prologue *pro = nullptr) {
     const q8::StepPlan &pl = plans[i];
     SegmentLaunch L{(const q8::StepDesc *)(ws + o_tab[i]), (const q8::WgGroup *)(ws + o_grp[i]),
                     (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged};
@@ -819,7 +865,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     L.nx = B.x_in;
     L.nw = M.layers[0].attn_norm;
     L.nout = B.xn;
-    L.ncopy = B.x;
+    L.ncopy = pro_path ? resid(-1) : B.x;
     L.ndim = H;
     L.neps = M.eps;
     L.npos = B.pos;
@@ -829,7 +875,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   }
   for (int32_t l = 0; l < M.n_layers; l++) {
     const q8_decode_layer &Ly = M.layers[l];
-    step_node(4 * (size_t)l, nullptr);
+    step_node(4 * (size_t)l, nullptr, pro_path && l ? &pros[3 * (size_t)l - 1] : nullptr);
     SegmentLaunch A{nullptr, nullptr, 0, 0, 0, 0, true};
     A.kind = kAttnNode;
     A.attn.q = B.q;
@@ -850,16 +896,18 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     A.attn.chunks = chunks;
     A.attn.eps = M.eps;
     g->launches.push_back(A);
-    step_node(4 * (size_t)l + 1, &epis[3 * (size_t)l]);
-    if (silu_pro) {
-      step_node(4 * (size_t)l + 2, nullptr);
-      step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2], &epis[3 * (size_t)l + 1]);
+    if (pro_path) {
+      step_node(4 * (size_t)l + 1, nullptr);
+      step_node(4 * (size_t)l + 2, nullptr, &pros[3 * (size_t)l]);
+      step_node(4 * (size_t)l + 3, nullptr, &pros[3 * (size_t)l + 1]);
     } else {
+      step_node(4 * (size_t)l + 1, &epis[3 * (size_t)l]);
       step_node(4 * (size_t)l + 2, &epis[3 * (size_t)l + 1]);
       step_node(4 * (size_t)l + 3, &epis[3 * (size_t)l + 2]);
     }
   }
-  step_node(plans.size() - 1, nullptr);
+  step_node(plans.size() - 1, nullptr,
+            pro_path ? &pros[3 * (size_t)M.n_layers - 1] : nullptr);
   return capture_graph(g, out, [&](hipStream_t cs) {
     hipError_t le = hipSuccess;
     for (size_t i = 0; i < g->launches.size() && le == hipSuccess; i++)

@@ -110,10 +110,11 @@ hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
 // `epi` (device memory, or NULL): work the last workgroup to finish runs
 // once every tile of the launch is written (see Epilogue).
 struct Epilogue;
+struct Prologue;
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x = false,
-                       const Epilogue *epi = nullptr, const Epilogue *pro = nullptr);
+                       const Epilogue *epi = nullptr, const Prologue *pro = nullptr);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
@@ -160,10 +161,6 @@ const void *probe_kernel();
 //   kEpiSiluMul: out = g / (1 + e^-g) * r over n values (silu_hadamard,
 //                g the gate, r the up projection).
 // `arrive` is a zeroed ArgmaxSlot used only for its counters.
-// The same record with kEpiSiluMul can also serve as a launch's prologue
-// (m = 1, every tile staged, n <= 3072): every workgroup computes out into
-// its staged x before its tiles, the launch's matvecs read x = out, and
-// workgroup 0 stores out as well (`arrive` unused).
 enum EpiOp : int32_t { kEpiNone = 0, kEpiAddNorm = 1, kEpiSiluMul = 2 };
 struct Epilogue {
   int32_t op, n;
@@ -177,6 +174,26 @@ struct Epilogue {
   int64_t pad1;
 };
 static_assert(sizeof(Epilogue) == 64, "epilogue layout");
+
+// Element-wise work a persistent step launch starts with (m = 1, every tile
+// staged, n <= kProMaxN): every workgroup computes the launch's x into its
+// staged x while its first tile loads, and the launch's matvecs read
+// x = out; workgroup 0 also stores out (and resid) in memory.
+//   kProSiluMul: out = a / (1 + e^-a) * b           (silu_hadamard: a the
+//                gate, b the up projection);
+//   kProAddNorm: s = (a + b) + c (c may be NULL), out = s / sqrt(mean(s^2)
+//                + eps) * w (rms_norm_row of the residual stream), resid
+//                (or NULL) receives s.
+enum ProOp : int32_t { kProNone = 0, kProSiluMul = 1, kProAddNorm = 2 };
+struct Prologue {
+  int32_t op, n;
+  float eps;
+  int32_t pad;
+  const float *a, *b, *c, *w;
+  float *out, *resid;
+};
+static_assert(sizeof(Prologue) == 64, "prologue layout");
+constexpr int kProMaxN = 3072;
 
 constexpr int kNormMaxDim = 4096;   // widest row a norm workgroup takes
 constexpr int kSiluMaxN = 65536;    // widest SwiGLU epilogue

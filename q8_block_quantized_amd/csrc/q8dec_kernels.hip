@@ -1093,35 +1093,58 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
   return j;
 }
 
-// The staged x of a launch whose x is silu_hadamard's output (the decode
-// step's down projection): out = gate / (1 + e^-gate) * up over n values
-// (n a multiple of 32, at most 3072), written into the padded LDS layout of
-// the x region by every workgroup, and to `out` in memory by one (`keep`).
-// It replaces a last-workgroup epilogue on the gate/up launch.
-__device__ __forceinline__ void silu_mul_x(const float *gate, const float *up, float *out,
-                                           int32_t n, float *xs, bool keep) {
-  constexpr int K = 3;  // float4 chunks per thread: 3 * 256 * 4 >= 3072
-  f32x4 gv[K], uv[K];
-  const int32_t chunks = n >> 2;
+// A launch's prologue (see Prologue): the launch's x, computed by every
+// workgroup into the padded LDS layout of its x region while its first tile
+// loads, and stored to memory by one workgroup (`keep`).  It replaces a
+// last-workgroup epilogue on the launch before, whose chain (completion
+// wait, arrival counters, device-scope loads) followed the last tile.
+// red: 4 floats of LDS not otherwise in use.
+__device__ __forceinline__ void run_prologue(const Prologue *p, float *xs, float *red,
+                                             bool keep) {
+  constexpr int K = kProMaxN / (4 * kWG);  // float4 chunks per thread
+  const int32_t chunks = p->n >> 2;
+  const bool norm = p->op == kProAddNorm;
+  f32x4 va[K], vb[K], vc[K];
 #pragma unroll
   for (int k = 0; k < K; k++) {
     const int32_t c = (int32_t)threadIdx.x + k * kWG;
-    gv[k] = uv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    va[k] = vb[k] = vc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < chunks) {
-      gv[k] = gp((const f32x4 *)gate)[c];
-      uv[k] = gp((const f32x4 *)up)[c];
+      va[k] = gp((const f32x4 *)p->a)[c];
+      vb[k] = gp((const f32x4 *)p->b)[c];
+      if (norm && p->c) vc[k] = gp((const f32x4 *)p->c)[c];
     }
+  }
+  float inv = 0.f;
+  if (norm) {  // the residual sum in the order the adds run: (a + b) + c
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      va[k] = va[k] + vb[k];
+      if (p->c) va[k] = va[k] + vc[k];
+#pragma unroll
+      for (int e = 0; e < 4; e++) ss += va[k][e] * va[k][e];
+    }
+    ss = dec::block_sum(ss, red);
+    inv = 1.0f / sqrtf(ss / (float)p->n + p->eps);
   }
 #pragma unroll
   for (int k = 0; k < K; k++) {
     const int32_t c = (int32_t)threadIdx.x + k * kWG;
     if (c < chunks) {
-      f32x4 h;
+      f32x4 o;
+      if (norm) {
+        const f32x4 w = gp((const f32x4 *)p->w)[c];
 #pragma unroll
-      for (int e = 0; e < 4; e++) h[e] = gv[k][e] / (1.0f + expf(-gv[k][e])) * uv[k][e];
+        for (int e = 0; e < 4; e++) o[e] = va[k][e] * inv * w[e];
+        if (keep && p->resid) gpw((f32x4 *)p->resid)[c] = va[k];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = va[k][e] / (1.0f + expf(-va[k][e])) * vb[k][e];
+      }
       const int32_t i = 4 * c;
-      *(f32x4 *)&xs[36 * (i >> 5) + (i & 31)] = h;
-      if (keep) gpw((f32x4 *)out)[c] = h;
+      *(f32x4 *)&xs[36 * (i >> 5) + (i & 31)] = o;
+      if (keep) gpw((f32x4 *)p->out)[c] = o;
     }
   }
 }
@@ -1136,7 +1159,7 @@ __device__ __forceinline__ void silu_mul_x(const float *gate, const float *up, f
 template <bool M1, bool ANY, bool I8X, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
-                          float *lds, const Epilogue *pro = nullptr) {
+                          float *lds, const Prologue *pro = nullptr) {
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
   constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
@@ -1176,7 +1199,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   int32_t xn = 0, xan = 0;
   if constexpr (M1 && !I8X) {
     if (pro) {  // the launch's x is pro->out, computed here while the first tile loads
-      silu_mul_x(pro->g, pro->r, pro->out, pro->n, xs, blockIdx.x == 0);
+      run_prologue(pro, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
       xptr = pro->out;
       xn = pro->n;
     }
@@ -1577,7 +1600,7 @@ template <bool M1, bool ANY, bool I8X>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
-            const Epilogue *__restrict__ epi, const Epilogue *__restrict__ pro) {
+            const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
@@ -1804,7 +1827,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi,
-                       const Epilogue *pro) {
+                       const Prologue *pro) {
   // m = 1 binary32 only, and a prologue only where every tile is staged
   if ((epi || pro) && (m != 1 || i8x)) return hipErrorInvalidValue;
   if (pro && !all_staged) return hipErrorInvalidValue;
