@@ -238,6 +238,26 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     plan.all_staged = plan.all_staged && step_all_staged(m, d.n, i8x);
   }
   if (tiles < 1) return Q8_ERR_SHAPE;  // nothing to run
+  // A launch of few tiles (the decode step's levels) spreads them over more
+  // workgroups: staged m = 1 tile heights above one pass (8 rows) halve
+  // until there are at least kStepMinTiles (as standalone matvecs do).
+  if (m == 1 && !i8x && plan.all_staged) {
+    while (tiles < kStepMinTiles) {
+      bool changed = false;
+      tiles = 0;
+      for (int32_t i = 0; i < count; i++) {
+        StepDesc &t = plan.descs[i];
+        if (t.rows_per_tile > kStepMinRows) {
+          t.rows_per_tile >>= 1;
+          changed = true;
+        }
+        t.tile_begin = (int32_t)tiles;
+        tiles += (t.p + t.rows_per_tile - 1) / t.rows_per_tile;
+        t.tile_end = (int32_t)tiles;
+      }
+      if (!changed) break;
+    }
+  }
   const int32_t ntiles = (int32_t)tiles;
   plan.lds = widest;
   if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;

@@ -147,6 +147,11 @@ struct StepPlan {
 // keeps a contiguous range of its own (groups of 2: 165 us per m = 8 step
 // against 206 us with 32).
 constexpr int kStepGroupSize = 32;
+#ifndef Q8_STEP_MIN_TILES
+#define Q8_STEP_MIN_TILES 512
+#endif
+constexpr int kStepMinTiles = Q8_STEP_MIN_TILES;  // fewer: staged m = 1 tiles get shorter
+constexpr int kStepMinRows = 8;                   // only heights above one pass halve
 constexpr int kStepGroupSizeBatched = 2;
 
 // Host stub of one kernel, used to check that the code object loads.
