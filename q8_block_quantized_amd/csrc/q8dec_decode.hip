@@ -39,6 +39,87 @@ __device__ __forceinline__ void load8(const float *p, float (&d)[8]) {
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
 
+// Merge of key/value head g's nc chunk partials by one workgroup: out =
+// sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c, M the maximum of the m_c.
+// Chunks go in rounds of R, each issuing all of its loads at once: thread
+// (h, i) loads chunk c0 + i's maximum and sum of head h, and every (h, d)
+// thread its R sums of dimension d.  Wave h then takes the round's maximum,
+// the running maximum M, the factor that rescales the earlier rounds and
+// the chunk weights e^(m_c - M) into LDS; each (h, d) thread rescales its
+// running sum and adds the weighted chunk sums in chunk order.  lds: 3 G R +
+// 4 G floats, not in use.
+template <int G, int R>
+__device__ __forceinline__ void merge_partials(const AttnArgs &a, int g, int nc, float *lds) {
+  constexpr int IT = (G * HD + dec::kThreads - 1) / dec::kThreads;  // (h, d) items per thread
+  static_assert(G <= 4 && R <= 64, "one wave per head, one lane per chunk");
+  const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float *mw = lds;         // [G][R]: the round's chunk maxima, then weights
+  float *ls = mw + G * R;  // [G][R]: the round's chunk sums
+  float *hs = ls + G * R;  // [G][4]: running maximum, running sum, rescale
+  if (tid < G) {
+    hs[4 * tid] = -INFINITY;
+    hs[4 * tid + 1] = 0.f;
+  }
+  float A[IT];
+#pragma unroll
+  for (int e = 0; e < IT; e++) A[e] = 0.f;
+  const float *ph = a.part + (size_t)(g * G) * a.chunks * kAttnPart;
+  for (int c0 = 0; c0 < nc; c0 += R) {
+    const int k = nc - c0 < R ? nc - c0 : R;
+    float pm = -INFINITY, pl = 0.f;
+    if (tid < G * R && tid % R < k) {
+      const float *p = ph + ((size_t)(tid / R) * a.chunks + c0 + tid % R) * kAttnPart;
+      pm = dec::ld_dev(p);
+      pl = dec::ld_dev(p + 1);
+    }
+    float pa[IT][R];
+#pragma unroll
+    for (int e = 0; e < IT; e++) {
+      const int it = tid + e * dec::kThreads, h = it / HD, d = it % HD;
+#pragma unroll
+      for (int i = 0; i < R; i++) {
+        pa[e][i] = 0.f;
+        if (it < G * HD && i < k)
+          pa[e][i] = dec::ld_dev(ph + ((size_t)h * a.chunks + c0 + i) * kAttnPart + 4 + d);
+      }
+    }
+    if (tid < G * R) {
+      mw[tid] = pm;
+      ls[tid] = pl;
+    }
+    __syncthreads();
+    if (wave < G) {
+      const float m = lane < R ? mw[wave * R + lane] : -INFINITY;
+      const float l = lane < R ? ls[wave * R + lane] : 0.f;
+      const float mo = hs[4 * wave], mn = fmaxf(mo, dec::wave_maxf(m));
+      const float r = mo == mn ? 1.f : expf(mo - mn);
+      const float w = lane < k ? expf(m - mn) : 0.f;
+      const float sl = dec::wave_sum(w * l);
+      if (lane < R) mw[wave * R + lane] = w;
+      if (lane == 0) {
+        hs[4 * wave] = mn;
+        hs[4 * wave + 1] = hs[4 * wave + 1] * r + sl;
+        hs[4 * wave + 2] = r;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < IT; e++) {
+      const int it = tid + e * dec::kThreads, h = it < G * HD ? it / HD : 0;
+      float v = A[e] * hs[4 * h + 2];
+#pragma unroll
+      for (int i = 0; i < R; i++) v += mw[h * R + i] * pa[e][i];
+      A[e] = v;
+    }
+    __syncthreads();  // before the next round rewrites mw, ls and hs
+  }
+#pragma unroll
+  for (int e = 0; e < IT; e++) {
+    const int it = tid + e * dec::kThreads;
+    if (it < G * HD) a.out[(size_t)(g * G) * HD + it] = A[e] / hs[4 * (it / HD) + 1];
+  }
+}
+
 // G query heads per key/value head.  Every load the workgroup needs (its
 // vectors, the norm weights, the rotation table and its 64 cached key and
 // value rows) is issued as soon as pos is known, so the whole prologue costs
@@ -210,44 +291,14 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
     }
   }
 
-  // The last workgroup of this key/value head merges the nc partials in
-  // chunk order, keeping a running maximum M: out = sum_c e^(m_c - M) acc_c /
-  // sum_c e^(m_c - M) l_c.  Partials are loaded 16 chunks at a time.
+  // The last workgroup of this key/value head merges the nc partials.
   if (!dec::arrive_last(a.arrive + g, (uint32_t)c, (uint32_t)nc, &flag)) return;
-  for (int t = (int)threadIdx.x; t < G * HD; t += dec::kThreads) {
-    const int h = t / HD, d = t % HD;
-    const float *ph = a.part + (size_t)(g * G + h) * a.chunks * kAttnPart;
-    float M = -INFINITY, L = 0.f, A = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 16) {
-      float pm[16], pl[16], pa[16];
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        pm[i] = -INFINITY;
-        pl[i] = pa[i] = 0.f;
-        if (c0 + i < nc) {
-          const float *p = ph + (size_t)(c0 + i) * kAttnPart;
-          pm[i] = dec::ld_dev(p);
-          pl[i] = dec::ld_dev(p + 1);
-          pa[i] = dec::ld_dev(p + 4 + d);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        if (c0 + i < nc) {
-          if (pm[i] > M) {
-            const float r = expf(M - pm[i]);
-            L *= r;
-            A *= r;
-            M = pm[i];
-          }
-          const float w = expf(pm[i] - M);
-          L += pl[i] * w;
-          A += pa[i] * w;
-        }
-      }
-    }
-    a.out[(size_t)(g * G + h) * HD + d] = A / L;
-  }
+  constexpr int IT = (G * HD + dec::kThreads - 1) / dec::kThreads;  // (h, d) items per thread
+  static_assert(3 * G * 64 + 4 * G <= 4 * G * HD, "the merge's state fits in red");
+  if (nc <= 16)
+    merge_partials<G, 16>(a, g, nc, &red[0][0][0]);
+  else
+    merge_partials<G, 64 / IT>(a, g, nc, &red[0][0][0]);
 }
 
 // The step's first node: x = x_in and xn = rms_norm_row(x_in) (first

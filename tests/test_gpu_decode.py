@@ -227,6 +227,14 @@ SMALL = [
                     vocab=77, eps=1e-6, theta=5e5), 64, 63),
     ("wide", dict(n_layers=1, hidden=4096, n_heads=4, n_kv_heads=2, head_dim=128, inter=128,
                   vocab=500, eps=1e-6, theta=1e6), 130, 129),
+    # long caches: the merge of the chunk partials takes two rounds (64
+    # chunks per round for G <= 2, 32 for G = 3, 4), the second ragged
+    ("g2-long", dict(n_layers=1, hidden=256, n_heads=2, n_kv_heads=1, head_dim=128,
+                     inter=256, vocab=300, eps=1e-6, theta=1e6), 5000, 4700),
+    ("g3-long", dict(n_layers=1, hidden=384, n_heads=3, n_kv_heads=1, head_dim=128,
+                     inter=160, vocab=77, eps=1e-6, theta=5e5), 2200, 2100),
+    ("g4-long", dict(n_layers=1, hidden=512, n_heads=4, n_kv_heads=2, head_dim=128,
+                     inter=96, vocab=1000, eps=1e-6, theta=1e6), 2600, 2500),
 ]
 
 
