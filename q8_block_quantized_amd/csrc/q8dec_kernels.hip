@@ -1149,14 +1149,35 @@ __device__ __forceinline__ void run_prologue(const Prologue *p, float *xs, float
   }
 }
 
+// Wave priority from the share of a workgroup's tiles still to come (left
+// of total): 3 while more than three quarters remain, down to 0 for the
+// last quarter.  The SIMD's arbiter prefers older waves, so of the
+// workgroups sharing a CU the first dispatched streams its tiles fastest
+// and the last finishes well after it (measured on MI355X with equal tile
+// counts: 76 µs against 104 µs in one 197-matvec launch); priority to the
+// workgroups with more tiles left evens out their progress and shortens
+// the tail of launches with a few tiles per workgroup.  s_setprio takes an
+// immediate, hence the branches (uniform: scalar).
+__device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
+  const int32_t b = left * 4 / (total + 1);
+  if (b >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (b == 2) __builtin_amdgcn_s_setprio(2);
+  else if (b == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Tiles first, first + stride, ... (< end) of the launch, in order.  Each
 // tile's weights (and x, when the tile opens another matvec) are loaded into
 // registers while the previous tile is computed.  Tiles of one matvec are
 // contiguous, so a workgroup meets each matvec in one run of tiles; the run
 // adds its argmax keys, if any, as one arrival.  M1: the launch has m = 1;
-// ANY: some matvec of the launch takes the direct or generic path.
+// ANY: some matvec of the launch takes the direct or generic path; PRIO:
+// wave priority by progress (set_progress_prio), for the launches where it
+// was measured faster on MI355X — standalone matvecs (fused lm_head 31.6 →
+// 30.4 µs) and the batched matrix-core step (m = 8: 170 → 154 µs); the
+// m = 1 and int8-activation steps run slower with it (+1–3 %).
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
-template <bool M1, bool ANY, bool I8X, class Src>
+template <bool M1, bool ANY, bool I8X, bool PRIO, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr) {
@@ -1208,9 +1229,12 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
   u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
+  const int32_t total = (end - 1 - first) / stride + 1;  // this workgroup's tiles
+  (void)total;
   for (;;) {
     const int32_t tn = t + stride;
     const int32_t bpr = cur.d.n >> 5;
+    if constexpr (PRIO) set_progress_prio((end - 1 - t) / stride, total);
     const bool x_changed = cur.d.x != xptr || cur.d.n != xn;
     const bool new_x = x_in_lds(cur) && x_changed;
     __syncthreads();  // the previous tile's readers of LDS are done
@@ -1588,7 +1612,7 @@ mv_kernel(StepDesc d, int32_t m) {
   // four consecutive tiles on one XCD (as the step's groups)
   const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
   const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
-  run_tiles<M1, ANY, I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X, !I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
@@ -1605,8 +1629,8 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY, I8X>(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, g.d0, m,
-                          lds, pro);
+  run_tiles<M1, ANY, I8X, !M1 && !I8X>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
+                                        g.size, g.d0, m, lds, pro);
   if constexpr (M1 && !I8X) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
