@@ -1471,7 +1471,10 @@ __device__ __forceinline__ WideItem wide_item(const Src &src, int32_t t, int32_t
   return it;
 }
 
-template <class Src>
+// PRIO: wave priority by progress (set_progress_prio); measured on MI355X
+// it shortens the persistent step (m = 32: 337 → 333 µs) and slows the
+// standalone matvec slightly, so only the step launch takes it.
+template <bool PRIO, class Src>
 __device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t stride,
                            int32_t m, float *lds) {
   uint8_t *wl = (uint8_t *)lds;
@@ -1494,6 +1497,7 @@ __device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t s
     for (int r = 0; r < 4; r++) best[c][r] = 0ull;
   for (;;) {
     if (cur.kc == 0) {
+      if constexpr (PRIO) set_progress_prio((end - 1 - t) / stride, (end - 1 - first) / stride + 1);
 #pragma unroll
       for (int rg = 0; rg < 2; rg++)
 #pragma unroll
@@ -1645,7 +1649,7 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
 __global__ void __launch_bounds__(kWG, 2) wide_mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
-  wide_tiles(src, blockIdx.x, tiles_of(d), gridDim.x, m, lds);
+  wide_tiles<false>(src, blockIdx.x, tiles_of(d), gridDim.x, m, lds);
 }
 
 __global__ void __launch_bounds__(kWG, 2)
@@ -1655,7 +1659,7 @@ wide_step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  wide_tiles(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, m, lds);
+  wide_tiles<true>(src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, m, lds);
 }
 
 // ---- argmax over f32 logits ---------------------------------------------
