@@ -1150,16 +1150,19 @@ __device__ __forceinline__ void run_prologue(const Prologue *p, float *xs, float
 }
 
 // Wave priority from the share of a workgroup's tiles still to come (left
-// of total): 3 while more than three quarters remain, down to 0 for the
-// last quarter.  The SIMD's arbiter prefers older waves, so of the
+// of total): 3 until the last three eighths, then 2, 1 and 0 for each
+// further eighth.  The SIMD's arbiter prefers older waves, so of the
 // workgroups sharing a CU the first dispatched streams its tiles fastest
 // and the last finishes well after it (measured on MI355X with equal tile
 // counts: 76 µs against 104 µs in one 197-matvec launch); priority to the
 // workgroups with more tiles left evens out their progress and shortens
-// the tail of launches with a few tiles per workgroup.  s_setprio takes an
+// the tail of launches with a few tiles per workgroup (the eighths were
+// measured against quarters, halves, sixteenths and tiles: fused lm_head
+// 29.5 µs against 30.3, 31.0, 29.9, 29.4; m = 8 step 152.9 µs against
+// 153.4, 156.3, 155.1, 159.4).  s_setprio takes an
 // immediate, hence the branches (uniform: scalar).
 __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
-  const int32_t b = left * 4 / (total + 1);
+  const int32_t b = min(3, left * 8 / (total + 1));
   if (b >= 3) __builtin_amdgcn_s_setprio(3);
   else if (b == 2) __builtin_amdgcn_s_setprio(2);
   else if (b == 1) __builtin_amdgcn_s_setprio(1);
