@@ -1177,8 +1177,9 @@ __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
 // ANY: some matvec of the launch takes the direct or generic path; PRIO:
 // wave priority by progress (set_progress_prio), for the launches where it
 // was measured faster on MI355X — standalone matvecs (fused lm_head 31.6 →
-// 30.4 µs) and the batched matrix-core step (m = 8: 170 → 154 µs); the
-// m = 1 and int8-activation steps run slower with it (+1–3 %).
+// 29.6 µs, with int8 activations 30.2 → 28.8 µs; not batched int8, where
+// it is neutral) and the batched matrix-core step (m = 8: 170 → 153 µs);
+// the m = 1 and int8-activation steps run slower with it (+1–3 %).
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
 template <bool M1, bool ANY, bool I8X, bool PRIO, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
@@ -1619,7 +1620,7 @@ mv_kernel(StepDesc d, int32_t m) {
   // four consecutive tiles on one XCD (as the step's groups)
   const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
   const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
-  run_tiles<M1, ANY, I8X, !I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X, M1 || !I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
