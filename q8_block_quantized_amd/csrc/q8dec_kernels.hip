@@ -1161,6 +1161,11 @@ __device__ __forceinline__ void run_prologue(const Prologue *p, float *xs, float
 // 29.5 µs against 30.3, 31.0, 29.9, 29.4; m = 8 step 152.9 µs against
 // 153.4, 156.3, 155.1, 159.4).  s_setprio takes an
 // immediate, hence the branches (uniform: scalar).
+// Workgroups with fewer tiles keep the default priority: for launches of
+// one or two tiles per workgroup (the chain graph's matvecs, the decode
+// step's nodes) the priority was measured slower (197-node chain 711 →
+// 747 µs).
+constexpr int32_t kPrioMinTiles = 4;
 __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
   const int32_t b = min(3, left * 8 / (total + 1));
   if (b >= 3) __builtin_amdgcn_s_setprio(3);
@@ -1238,7 +1243,8 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   for (;;) {
     const int32_t tn = t + stride;
     const int32_t bpr = cur.d.n >> 5;
-    if constexpr (PRIO) set_progress_prio((end - 1 - t) / stride, total);
+    if constexpr (PRIO)
+      if (total >= kPrioMinTiles) set_progress_prio((end - 1 - t) / stride, total);
     const bool x_changed = cur.d.x != xptr || cur.d.n != xn;
     const bool new_x = x_in_lds(cur) && x_changed;
     __syncthreads();  // the previous tile's readers of LDS are done
