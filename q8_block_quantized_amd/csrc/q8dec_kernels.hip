@@ -1097,50 +1097,64 @@ __device__ __forceinline__ Job job_at(int32_t desc, const StepDesc &d, int32_t t
 // workgroup into the padded LDS layout of its x region while its first tile
 // loads, and stored to memory by one workgroup (`keep`).  It replaces a
 // last-workgroup epilogue on the launch before, whose chain (completion
-// wait, arrival counters, device-scope loads) followed the last tile.
-// red: 4 floats of LDS not otherwise in use.
-__device__ __forceinline__ void run_prologue(const Prologue *p, float *xs, float *red,
-                                             bool keep) {
-  constexpr int K = kProMaxN / (4 * kWG);  // float4 chunks per thread
+// wait, arrival counters, device-scope loads) followed the last tile.  Its
+// loads (pro_load, the norm weight included) are issued before the first
+// tile's: loads complete in issue order, so issued after the tile's bytes
+// they would wait for them.
+constexpr int kProChunks = kProMaxN / (4 * kWG);  // float4 chunks per thread
+struct ProRegs {
+  f32x4 a[kProChunks], b[kProChunks], c[kProChunks], w[kProChunks];
+};
+
+__device__ __forceinline__ void pro_load(const Prologue *p, ProRegs &r) {
   const int32_t chunks = p->n >> 2;
   const bool norm = p->op == kProAddNorm;
-  f32x4 va[K], vb[K], vc[K];
 #pragma unroll
-  for (int k = 0; k < K; k++) {
+  for (int k = 0; k < kProChunks; k++) {
     const int32_t c = (int32_t)threadIdx.x + k * kWG;
-    va[k] = vb[k] = vc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    r.a[k] = r.b[k] = r.c[k] = r.w[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < chunks) {
-      va[k] = gp((const f32x4 *)p->a)[c];
-      vb[k] = gp((const f32x4 *)p->b)[c];
-      if (norm && p->c) vc[k] = gp((const f32x4 *)p->c)[c];
+      r.a[k] = gp((const f32x4 *)p->a)[c];
+      r.b[k] = gp((const f32x4 *)p->b)[c];
+      if (norm) {
+        if (p->c) r.c[k] = gp((const f32x4 *)p->c)[c];
+        r.w[k] = gp((const f32x4 *)p->w)[c];
+      }
     }
   }
+}
+
+// The prologue's arithmetic on the values pro_load fetched.  red: 4 floats
+// of LDS not otherwise in use.
+__device__ __forceinline__ void pro_finish(const Prologue *p, ProRegs &r, float *xs,
+                                           float *red, bool keep) {
+  const int32_t chunks = p->n >> 2;
+  const bool norm = p->op == kProAddNorm;
   float inv = 0.f;
   if (norm) {  // the residual sum in the order the adds run: (a + b) + c
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < K; k++) {
-      va[k] = va[k] + vb[k];
-      if (p->c) va[k] = va[k] + vc[k];
+    for (int k = 0; k < kProChunks; k++) {
+      r.a[k] = r.a[k] + r.b[k];
+      if (p->c) r.a[k] = r.a[k] + r.c[k];
 #pragma unroll
-      for (int e = 0; e < 4; e++) ss += va[k][e] * va[k][e];
+      for (int e = 0; e < 4; e++) ss += r.a[k][e] * r.a[k][e];
     }
     ss = dec::block_sum(ss, red);
     inv = 1.0f / sqrtf(ss / (float)p->n + p->eps);
   }
 #pragma unroll
-  for (int k = 0; k < K; k++) {
+  for (int k = 0; k < kProChunks; k++) {
     const int32_t c = (int32_t)threadIdx.x + k * kWG;
     if (c < chunks) {
       f32x4 o;
       if (norm) {
-        const f32x4 w = gp((const f32x4 *)p->w)[c];
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = va[k][e] * inv * w[e];
-        if (keep && p->resid) gpw((f32x4 *)p->resid)[c] = va[k];
+        for (int e = 0; e < 4; e++) o[e] = r.a[k][e] * inv * r.w[k][e];
+        if (keep && p->resid) gpw((f32x4 *)p->resid)[c] = r.a[k];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = va[k][e] / (1.0f + expf(-va[k][e])) * vb[k][e];
+        for (int e = 0; e < 4; e++) o[e] = r.a[k][e] / (1.0f + expf(-r.a[k][e])) * r.b[k][e];
       }
       const int32_t i = 4 * c;
       *(f32x4 *)&xs[36 * (i >> 5) + (i & 31)] = o;
@@ -1220,6 +1234,10 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   Job cur = job_at(di, src.get(di), t, m);
   bool more = t + stride < end;
   Job nxt = more ? job_after(cur, t + stride) : cur;
+  ProRegs prr;
+  if constexpr (M1 && !I8X) {
+    if (pro) pro_load(pro, prr);  // before the tile's loads: see pro_load
+  }
   if (staged(cur) || mfma(cur))
     pf.load_w(cur.d.w + (uint64_t)cur.r0 * (cur.d.n >> 5) * 34u,
               cur.rows * (cur.d.n >> 5) * 34);
@@ -1229,7 +1247,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   int32_t xn = 0, xan = 0;
   if constexpr (M1 && !I8X) {
     if (pro) {  // the launch's x is pro->out, computed here while the first tile loads
-      run_prologue(pro, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
+      pro_finish(pro, prr, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
       xptr = pro->out;
       xn = pro->n;
     }
