@@ -141,12 +141,13 @@ struct StepPlan {
   bool i8x = false;
 };
 
-// Workgroups per group of the persistent step.  m = 1: groups of 32
-// streaming neighbouring tiles were fastest on MI355X (a sweep of 1..4096).
-// Batched: a workgroup reloads its slice of x at every new matvec, so each
-// keeps a contiguous range of its own (groups of 2: 165 us per m = 8 step
-// against 206 us with 32).
-constexpr int kStepGroupSize = 32;
+// Workgroups per group of the persistent step.  m = 1: groups of 32 to 64
+// streaming neighbouring tiles were fastest on MI355X (a sweep of 1..4096),
+// 64 since the wave-priority and prologue changes (m = 1 step 101.0 µs
+// against 102.6 µs with 32, interleaved A/B).  Batched: a workgroup reloads
+// its slice of x at every new matvec, so each keeps a contiguous range of
+// its own (kStepGroupSizeBatched).
+constexpr int kStepGroupSize = 64;
 #ifndef Q8_STEP_MIN_TILES
 #define Q8_STEP_MIN_TILES 512
 #endif
