@@ -724,3 +724,90 @@ ALL_PINS = [
     pin_decode_layer_mlp_branch,
     pin_decode_step_head,
 ]
+
+
+# ---- the parity bar (oracle.matvec_errors, oracle.argmax_accepted) ----------
+#
+# These two helpers turn the oracle's values into pass/fail for every GPU
+# test, so a slip in them would loosen every parity claim at once.  The
+# pins below are hand cases whose answers follow from the bar's definition
+# (inferno.rs "IV.4", "The correctness ladder": an assert_close bar per
+# output and the tie rule of the argmax; the bound itself is
+# |err| <= 1e-4 * sum|scale*q*x| + 1e-6 per output, and an argmax is correct
+# when it is the oracle's index or the two logits lie within the sum of
+# their bounds).  All values are dyadic, so every comparison is exact.
+# Each pin takes the module that holds the two helpers.
+
+def bar_pin_matvec_errors(bar):
+    """err = |y - y_ref| / tol, exactly 1 at the bound and above it past it;
+    equal values (infinities included) and NaN against NaN are 0; NaN
+    against a number, or a finite value against an infinity, is inf."""
+    nan, inf = float("nan"), float("inf")
+    eps = 2.0 ** -40
+    y_ref = np.array([1.0, 1.0, 1.0, -2.0, 0.0, inf, -inf, nan, nan, 3.0, inf, 5.0,
+                      1.0, 1.0])
+    tol = np.array([0.25, 0.25, 0.25, 0.5, 0.125, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0,
+                    0.25, 4.0])
+    y = np.array([1.0, 1.25, 1.25 + eps, -2.5, -0.0625, inf, -inf, nan, 1.0, nan, 7.0,
+                  -inf, 0.75, 9.0])
+    want = np.array([0.0, 1.0, 1.0 + eps / 0.25, 1.0, 0.5, 0.0, 0.0, 0.0, inf, inf, inf,
+                     inf, 1.0, 2.0])
+    got = bar.matvec_errors(y, y_ref, tol)
+    assert got.shape == y.shape
+    assert np.array_equal(got, want), (got, want)
+    assert got[1] <= 1.0 and got[2] > 1.0  # at the bound passes, just past it fails
+    assert got[12] <= 1.0 and bar.matvec_errors([0.75 - eps], [1.0], [0.25])[0] > 1.0
+    # per-output tolerance: each output is divided by its own bound
+    got2 = bar.matvec_errors([2.0, 2.0], [1.0, 1.0], [1.0, 0.5])
+    assert np.array_equal(got2, [1.0, 2.0]), got2
+    # +inf against -inf, and a sign error, fail
+    assert bar.matvec_errors([inf], [-inf], [1.0])[0] == inf
+    assert bar.matvec_errors([-1.0], [1.0], [1.0])[0] == 2.0
+    # batched shapes keep their layout
+    g3 = bar.matvec_errors(np.ones((2, 3)), np.zeros((2, 3)), np.full((2, 3), 0.5))
+    assert g3.shape == (2, 3) and np.all(g3 == 2.0)
+
+
+def bar_pin_argmax_accepted(bar):
+    """The oracle's index is always accepted; another index only when its
+    logit lies within tol[best] + tol[g] of the best (the sum of the two
+    bounds, not one of them, not twice it); -1, out-of-range indices and
+    NaN logits never."""
+    nan = float("nan")
+    eps = 2.0 ** -40
+    y = np.array([0.5, 1.0, 0.75, 0.75 - eps, 0.875])
+    tol = np.array([0.0, 0.0625, 0.1875, 0.1875, 0.0])
+    assert bar.argmax_accepted(1, y, tol)                 # the oracle's index
+    assert bar.argmax_accepted(2, y, tol)                 # 0.25 == 0.0625 + 0.1875
+    assert not bar.argmax_accepted(3, y, tol)             # just outside the band
+    assert not bar.argmax_accepted(0, y, tol)             # far outside
+    # index 4 lies within tol[best] = 0.0625 * 2 but not within tol[best] + tol[4]
+    assert not bar.argmax_accepted(4, y, tol)
+    # asymmetric bounds: only their sum accepts index 2 (0.25 = 0.0625 + 0.1875)
+    y2 = np.array([1.0, 0.75])
+    assert bar.argmax_accepted(1, y2, np.array([0.0625, 0.1875]))
+    assert bar.argmax_accepted(1, y2, np.array([0.1875, 0.0625]))
+    assert not bar.argmax_accepted(1, y2, np.array([0.0625, 0.0625]))
+    assert not bar.argmax_accepted(1, y2, np.array([0.0, 0.125]))
+    # -1 and out of range: rejected even when the wrapped index would be close
+    y3 = np.array([0.0, 1.0, 1.0 - eps])
+    t3 = np.array([0.5, 0.5, 0.5])
+    assert bar.argmax_accepted(2, y3, t3)
+    assert not bar.argmax_accepted(-1, y3, t3)
+    assert not bar.argmax_accepted(3, y3, t3)
+    assert not bar.argmax_accepted(-2, y3, t3)
+    # NaN logits: never the answer; all-NaN rows accept exactly -1
+    y4 = np.array([nan, 1.0, 0.999])
+    t4 = np.array([1.0, 0.5, 0.5])
+    assert bar.argmax_accepted(1, y4, t4)
+    assert not bar.argmax_accepted(0, y4, t4)
+    yn = np.array([nan, nan])
+    assert bar.argmax_accepted(-1, yn, np.ones(2))
+    assert not bar.argmax_accepted(0, yn, np.ones(2))
+    # ties: the lowest index is the oracle's, the other one is in the band
+    y5 = np.array([2.0, 2.0])
+    assert bar.argmax_accepted(0, y5, np.zeros(2))
+    assert bar.argmax_accepted(1, y5, np.zeros(2))
+
+
+BAR_PINS = [bar_pin_matvec_errors, bar_pin_argmax_accepted]
