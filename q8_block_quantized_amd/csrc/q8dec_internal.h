@@ -24,10 +24,15 @@ struct ArgmaxGroup {
 static_assert(sizeof(ArgmaxGroup) == 384, "group layout");
 static_assert(offsetof(ArgmaxGroup, counter) == 256, "counter line");
 
-#ifndef Q8_ARGMAX_TEAMS
-#define Q8_ARGMAX_TEAMS 32
-#endif
-constexpr int kArgmaxTeams = Q8_ARGMAX_TEAMS;
+// Argmax teams.  One value for every translation unit: the slot's size and
+// the offset of its `host` pointer follow from it, so the code that
+// allocates a slot and the kernels that index it must agree.  The last
+// arrival collects the team keys with one lane per team of a single
+// 64-lane wave (argmax_arrive), so at most 64 teams can be collected and
+// cleared.
+constexpr int kArgmaxTeams = 32;
+static_assert(kArgmaxTeams >= 1 && kArgmaxTeams <= 64,
+              "the final exchange reads one team per lane of one wave");
 
 // Argmax workspace of one matvec.  An arriving workgroup g joins team
 // g % kArgmaxTeams; the last arrival of a team forwards the team's keys to
@@ -44,9 +49,6 @@ struct ArgmaxSlot {
 };
 
 // One matvec of a launch, as the kernels see it.
-#ifndef Q8_XCD_SLOTS
-#define Q8_XCD_SLOTS 1
-#endif
 
 struct StepDesc {
   const uint8_t *w;
@@ -81,7 +83,7 @@ static_assert(sizeof(WgGroup) == 32, "group layout");
 // offsets are dealt so that consecutive tiles run on one XCD: their outputs
 // share 128-byte lines, which one L2 then writes back whole.
 __host__ __device__ inline int32_t group_slot(int32_t j, int32_t first, int32_t size) {
-  if (!Q8_XCD_SLOTS || (first & 7) || (size & 7)) return j;
+  if ((first & 7) || (size & 7)) return j;
   return (j & 7) * (size >> 3) + (j >> 3);
 }
 
@@ -148,10 +150,7 @@ struct StepPlan {
 // its slice of x at every new matvec, so each keeps a contiguous range of
 // its own (kStepGroupSizeBatched).
 constexpr int kStepGroupSize = 64;
-#ifndef Q8_STEP_MIN_TILES
-#define Q8_STEP_MIN_TILES 512
-#endif
-constexpr int kStepMinTiles = Q8_STEP_MIN_TILES;  // fewer: staged m = 1 tiles get shorter
+constexpr int kStepMinTiles = 512;  // fewer: staged m = 1 tiles get shorter
 constexpr int kStepMinRows = 8;                   // only heights above one pass halve
 // m > 1: every workgroup its own contiguous tile range (groups of 1; with
 // the wave priority by progress, 1 measured fastest of 1–512 for m = 4, 8,

@@ -332,13 +332,7 @@ __device__ void argmax_arrive(const unsigned long long (*lk)[MR], int m,
 //  kWide   : 8 < m <= 32, n a multiple of 256 (see wide_tiles).
 enum Path : int { kStaged = 0, kDirect = 1, kGeneric = 2, kMfma = 3, kWide = 4 };
 
-#ifndef Q8_TILE_BYTES
-#define Q8_TILE_BYTES 26112  // 8 rows of 3072 columns
-#endif
-#ifndef Q8_MIN_WGS_PER_CU
-#define Q8_MIN_WGS_PER_CU 1
-#endif
-constexpr int kTileMaxBytes = Q8_TILE_BYTES;
+constexpr int kTileMaxBytes = 26112;  // 8 rows of 3072 columns
 constexpr int kStageChunks = (kTileMaxBytes + 16 * kWG - 1) / (16 * kWG);
 constexpr int kXMaxFloats = 8192;     // m * n of x kept in LDS (32 KB)
 constexpr int kMaxLdsBlocks = 96;     // n <= 3072 for the LDS paths
@@ -1636,7 +1630,7 @@ __device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t s
 // grid (gridDim.x <= tiles, so every workgroup arrives at the argmax): at
 // any moment the grid streams one contiguous window of the weights.
 template <bool M1, bool ANY, bool I8X>
-__global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
+__global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
@@ -1653,7 +1647,7 @@ mv_kernel(StepDesc d, int32_t m) {
 // epi (or NULL; m = 1 with binary32 activations only): element-wise work
 // that the last workgroup to finish runs once every tile is written.
 template <bool M1, bool ANY, bool I8X>
-__global__ void __launch_bounds__(kWG, (M1 || I8X) ? Q8_MIN_WGS_PER_CU : 2)
+__global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
             const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro) {
