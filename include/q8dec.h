@@ -38,10 +38,16 @@
  *     be NULL only when its buffer holds zero bytes.
  *   - Every argument is validated before any HIP call; a refused call does
  *     no GPU work and returns a nonzero Q8_ERR_* status.  Q8_OK is 0.
- *   - The argmax entry points keep a small per-device workspace inside the
- *     library (allocated by q8_init or on first use, outside any stream
- *     capture).  Two argmax calls that run at the same time on one device
- *     share it and race; issue them in one stream order.
+ *   - The argmax entry points (q8_argmax, q8_matvec_argmax,
+ *     q8_matvec_argmax_i8x) keep a small workspace (12.4 KB) inside the
+ *     library for each stream they run on, so calls on different streams
+ *     never share one and calls on one stream are ordered by it.  The null
+ *     stream's is allocated by q8_init (or the first call of any entry
+ *     point); another stream's by its first argmax call, which clears it in
+ *     that stream's order.  That first call must not be made while the
+ *     stream is capturing a graph: it is refused with Q8_ERR_GRAPH.  At most
+ *     256 streams per device get a workspace (Q8_ERR_COUNT beyond); each is
+ *     kept until the process ends.
  */
 #ifndef Q8DEC_H
 #define Q8DEC_H
@@ -91,9 +97,10 @@ int q8_last_hip_error(void);
 /* Number of visible HIP devices (0 when none), without selecting one. */
 int q8_device_count(int32_t *count);
 
-/* Checks the current device (gfx950, kernels loadable) and allocates its
- * argmax workspace.  Optional: every entry point does it on first use.  A
- * failure is remembered for that device and returned again (sticky). */
+/* Checks the current device (gfx950, kernels loadable) and allocates the
+ * null stream's argmax workspace.  Optional: every entry point does it on
+ * first use.  A failure is remembered for that device and returned again
+ * (sticky). */
 int q8_init(void);
 
 /* ---- matvec ------------------------------------------------------------ */
@@ -242,12 +249,27 @@ int q8_step_graph_destroy(q8_step_graph *g);
  * o projection -> add_inplace into x -> rms_norm_row -> gate, up ->
  * silu_hadamard -> down projection -> add_inplace; then the final norm, the
  * lm_head and argmax_row ("Eight kernels" defines each operation).  The
- * pages encode 18 dispatches per layer; here a layer is 5 kernel nodes (the
+ * pages encode 18 dispatches per layer; here a layer is 5 kernel nodes: the
  * q/k/v matvecs; the attention with the QK-norm, RoPE and append folded in;
- * the o matvec whose last workgroup adds into x and norms; gate/up whose
- * last workgroup applies SwiGLU; down, adding into x and norming for the
- * next layer), plus one norm node before the first layer and the fused
- * lm_head argmax: 5 * n_layers + 2 nodes.  Everything is binary32. */
+ * o; gate/up; down.  Before the first layer one node copies x_in into the
+ * residual stream and norms it; after the last the fused lm_head argmax
+ * runs: 5 * n_layers + 2 nodes.  The element-wise work between matvecs (the
+ * residual adds, the norms, SwiGLU) runs in one of two places:
+ *   - prologue form, taken when every matvec width is a multiple of 256 up
+ *     to 3072 and hidden, inter <= 3072 (Qwen3-0.6B's shapes): every
+ *     workgroup of the launch that consumes the vector computes it into its
+ *     staged x while its first weight tile loads, and workgroup 0 stores it
+ *     (gate/up: xn2 = norm(R + attn_out); down: h = silu(gate) * up; the
+ *     next layer's q/k/v, or the lm_head: R' = (R + attn_out) + ffn_out and
+ *     its norm).  The residual stream alternates between buf->x and a
+ *     workspace buffer from layer to layer, and after the last layer it is
+ *     in buf->x;
+ *   - epilogue form, for every other shape: the last workgroup of the
+ *     launch that produces the vector computes it once every output of that
+ *     launch is stored (o: x += attn_out and xn2; gate/up: h; down:
+ *     x += ffn_out and the next norm); the residual stream stays in buf->x.
+ * Both forms give the same values (the adds run in the pages' order).
+ * Everything is binary32. */
 
 #define Q8_GRAPH_DECODE 4  /* mode of graphs from q8_decode_graph_build */
 

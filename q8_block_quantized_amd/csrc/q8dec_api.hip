@@ -39,31 +39,50 @@ int hip_fail(hipError_t e) {
 
 constexpr int kMaxDevices = 64;
 
+// The standalone argmax calls keep one workspace (an ArgmaxSlot) per stream
+// they run on, so calls on different streams never share one; calls on one
+// stream are ordered by it.  At most kMaxStreamSlots streams per device.
+constexpr int kMaxStreamSlots = 256;
+struct StreamSlot {
+  hipStream_t stream;
+  q8::ArgmaxSlot *slot;
+};
+
 struct DeviceState {
   int status = -1;                  // -1 unchecked, else a Q8 status
-  q8::ArgmaxSlot *slot = nullptr;   // workspace of the standalone argmax calls
+  std::vector<StreamSlot> slots;    // argmax workspaces by stream (null stream first)
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
-// Selects nothing: checks the current device and sets it up once.
-int ensure_device(int *dev_out) {
-  int count = 0;
-  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
-    (void)hipGetLastError();
-    return Q8_ERR_NO_DEVICE;
-  }
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+// An argmax workspace, zeroed in the order of `stream` (the stream whose
+// argmax calls will use it), or, for the null stream's, before returning.
+int alloc_slot(q8::ArgmaxSlot **out, hipStream_t stream, bool on_stream) {
+  void *p = nullptr;
+  hipError_t e = hipMalloc(&p, sizeof(q8::ArgmaxSlot));
   if (e != hipSuccess) return hip_fail(e);
-  if (dev < 0 || dev >= kMaxDevices) return Q8_ERR_NO_DEVICE;
-  if (dev_out) *dev_out = dev;
-  std::lock_guard<std::mutex> lock(g_mu);
+  if (on_stream) {
+    e = hipMemsetAsync(p, 0, sizeof(q8::ArgmaxSlot), stream);
+  } else {
+    e = hipMemset(p, 0, sizeof(q8::ArgmaxSlot));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e);
+  }
+  *out = (q8::ArgmaxSlot *)p;
+  return Q8_OK;
+}
+
+// The current device, checked once (gfx950, kernels loadable); allocates
+// nothing.  Caller holds g_mu.
+int check_device_locked(int dev) {
   DeviceState &st = g_dev[dev];
   if (st.status >= 0) return st.status;
   hipDeviceProp_t prop;
-  e = hipGetDeviceProperties(&prop, dev);
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return hip_fail(e);
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
     st.status = Q8_ERR_ARCH;
@@ -76,16 +95,72 @@ int ensure_device(int *dev_out) {
     st.status = Q8_ERR_CODE_OBJECT;
     return st.status;
   }
-  void *p = nullptr;
-  e = hipMalloc(&p, sizeof(q8::ArgmaxSlot));
-  if (e != hipSuccess) return hip_fail(e);
-  e = hipMemset(p, 0, sizeof(q8::ArgmaxSlot));
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return hip_fail(e);
-  }
-  st.slot = (q8::ArgmaxSlot *)p;
   st.status = Q8_OK;
+  return Q8_OK;
+}
+
+int current_device(int *dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return Q8_ERR_NO_DEVICE;
+  }
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (*dev < 0 || *dev >= kMaxDevices) return Q8_ERR_NO_DEVICE;
+  return Q8_OK;
+}
+
+// Selects nothing: checks the current device and sets it up once (the
+// null stream's argmax workspace included).
+int ensure_device(int *dev_out) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st) return st;
+  if (dev_out) *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if ((st = check_device_locked(dev))) return st;
+  DeviceState &ds = g_dev[dev];
+  if (ds.slots.empty()) {
+    q8::ArgmaxSlot *slot = nullptr;
+    if ((st = alloc_slot(&slot, nullptr, false))) return st;
+    ds.slots.push_back(StreamSlot{nullptr, slot});
+  }
+  return Q8_OK;
+}
+
+// Checks the current device without allocating anything.
+int check_device(int *dev_out) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st) return st;
+  if (dev_out) *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_mu);
+  return check_device_locked(dev);
+}
+
+// The argmax workspace of `stream` on device dev (after ensure_device),
+// allocated on the stream's first argmax call and cleared in its order.
+// That first call must not be made while the stream is capturing
+// (Q8_ERR_GRAPH): the clearing is not something to record into a graph.
+int stream_slot(int dev, hipStream_t stream, q8::ArgmaxSlot **out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState &ds = g_dev[dev];
+  for (const StreamSlot &s : ds.slots)
+    if (s.stream == stream) {
+      *out = s.slot;
+      return Q8_OK;
+    }
+  if ((int)ds.slots.size() >= kMaxStreamSlots) return Q8_ERR_COUNT;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cap != hipStreamCaptureStatusNone) return Q8_ERR_GRAPH;
+  q8::ArgmaxSlot *slot = nullptr;
+  int st = alloc_slot(&slot, stream, true);
+  if (st) return st;
+  ds.slots.push_back(StreamSlot{stream, slot});
+  *out = slot;
   return Q8_OK;
 }
 
@@ -391,8 +466,9 @@ int q8_argmax(const float *logits, int32_t m, int32_t p, int32_t *idx,
   int dev = 0;
   int st = ensure_device(&dev);
   if (st) return st;
-  hipError_t e = q8::launch_argmax(logits, m, p, g_dev[dev].slot, idx,
-                                   (hipStream_t)stream);
+  q8::ArgmaxSlot *slot = nullptr;
+  if ((st = stream_slot(dev, (hipStream_t)stream, &slot))) return st;
+  hipError_t e = q8::launch_argmax(logits, m, p, slot, idx, (hipStream_t)stream);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
@@ -404,8 +480,10 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
   if (st) return st;
   int dev = 0;
   if ((st = ensure_device(&dev))) return st;
+  q8::ArgmaxSlot *slot = nullptr;
+  if ((st = stream_slot(dev, (hipStream_t)stream, &slot))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
-                                   g_dev[dev].slot, idx, (hipStream_t)stream);
+                                   slot, idx, (hipStream_t)stream);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
@@ -429,8 +507,10 @@ int q8_matvec_argmax_i8x(const void *w, const float *x, float *y_or_null,
   if (m > Q8_MAX_M_NARROW || (n > 0 && !q8::i8x_shape_ok(n))) return Q8_ERR_SHAPE;
   int dev = 0;
   if ((st = ensure_device(&dev))) return st;
+  q8::ArgmaxSlot *slot = nullptr;
+  if ((st = stream_slot(dev, (hipStream_t)stream, &slot))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
-                                   g_dev[dev].slot, idx, (hipStream_t)stream, n > 0);
+                                   slot, idx, (hipStream_t)stream, n > 0);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 

@@ -143,3 +143,73 @@ def test_fused_all_nan_row_is_minus_one(cuda):
     blk[:, :, 0], blk[:, :, 1] = 0x00, 0x7E  # every scale NaN
     idx, _ = gpu_fused(w, x, cuda, False)
     assert idx[0] == -1
+
+
+def test_streams_have_their_own_workspace(cuda):
+    """Fused lm_head argmax calls on four streams at once, interleaved over
+    many rounds: each stream's argmax workspace is its own, so every call
+    returns its own input's token (checked against the oracle) and the
+    standalone argmax on the same streams agrees."""
+    import torch
+    import q8_block_quantized_amd as q8
+    p, n, S = 151936, 1024, 4
+    w = gen.weights(p, n, seed=40, index=0)
+    wd = to_dev(w.reshape(-1), cuda)
+    xs = gen.activations(S, n, seed=40, index=1)
+    xd = [to_dev(xs[i:i + 1], cuda) for i in range(S)]
+    streams = [torch.cuda.Stream(device=cuda) for _ in range(S)]
+    want = []
+    for i in range(S):
+        ref, tol = oracle.get().matvec_mt(w, xs[i], 16)[:2]
+        y = torch.empty((1, p), dtype=torch.float32, device=cuda)
+        idx = torch.empty(1, dtype=torch.int32, device=cuda)
+        q8.q8_matvec_argmax(wd, xd[i], idx, p, y=y)
+        torch.cuda.synchronize()
+        assert oracle.argmax_accepted(int(idx.item()), ref, tol)
+        want.append((int(idx.item()), y))
+    torch.cuda.synchronize()
+    outs = [torch.full((20,), -7, dtype=torch.int32, device=cuda) for _ in range(S)]
+    outs2 = [torch.full((20,), -7, dtype=torch.int32, device=cuda) for _ in range(S)]
+    torch.cuda.synchronize()  # the fills above ran on the default stream
+    for k in range(20):
+        for i in range(S):
+            q8.q8_matvec_argmax(wd, xd[i], outs[i][k:k + 1], p, stream=streams[i])
+            q8.q8_argmax(want[i][1], outs2[i][k:k + 1], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(S):
+        assert torch.all(outs[i] == want[i][0]), (i, outs[i])
+        assert torch.all(outs2[i] == want[i][0]), (i, outs2[i])
+
+
+def test_first_call_on_a_capturing_stream_is_refused(cuda):
+    """A stream's argmax workspace is allocated and cleared on its first
+    argmax call; made while the stream is capturing, that call is refused
+    with Q8_ERR_GRAPH (8) before any GPU work, and the same call outside the
+    capture then runs normally."""
+    import ctypes
+    import torch
+    import q8_block_quantized_amd as q8
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
+    p, n = 5000, 1024
+    w = gen.weights(p, n, seed=41, index=0)
+    x = gen.activations(1, n, seed=41, index=1)
+    wd, xd = to_dev(w.reshape(-1), cuda), to_dev(x, cuda)
+    idx = torch.full((1,), -7, dtype=torch.int32, device=cuda)
+    torch.cuda.synchronize()
+    s = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+    assert hip.hipStreamBeginCapture(s, 2) == 0  # relaxed mode
+    st = q8.load().q8_matvec_argmax(wd.data_ptr(), xd.data_ptr(), None, idx.data_ptr(),
+                                    1, n, p, s)
+    graph = ctypes.c_void_p()
+    assert hip.hipStreamEndCapture(s, ctypes.byref(graph)) == 0
+    if graph.value:
+        hip.hipGraphDestroy(graph)
+    assert st == 8, q8.q8_status_name(st)
+    st = q8.load().q8_matvec_argmax(wd.data_ptr(), xd.data_ptr(), None, idx.data_ptr(),
+                                    1, n, p, s)
+    assert st == 0
+    assert hip.hipStreamSynchronize(s) == 0
+    assert hip.hipStreamDestroy(s) == 0
+    ref, tol = oracle.matvec(w, x[0])
+    assert oracle.argmax_accepted(int(idx.item()), ref, tol)
