@@ -55,6 +55,18 @@ def gpu_batched(w: np.ndarray, x: np.ndarray, device) -> np.ndarray:
     return yd.cpu().numpy()
 
 
+def oracle_rows(w: np.ndarray, x: np.ndarray, threads: int = 16):
+    """The oracle's y and tol ([m, p]) for every row of x [m, n], rows of W
+    split over `threads` host threads (bit-identical to one thread)."""
+    x = np.atleast_2d(x)
+    p = w.shape[0]
+    ref = np.empty((x.shape[0], p))
+    tol = np.empty((x.shape[0], p))
+    for r in range(x.shape[0]):
+        ref[r], tol[r] = oracle.get().matvec_mt(w, x[r], threads)[:2]
+    return ref, tol
+
+
 def assert_parity(y_gpu, y_ref, tol, label: str) -> float:
     err = oracle.matvec_errors(y_gpu, y_ref, tol)
     worst = int(np.argmax(err)) if err.size else 0

@@ -9,7 +9,7 @@ import pytest
 
 import gen
 import oracle
-from tests.gpu_helpers import assert_parity, cuda, say, to_dev  # noqa: F401
+from tests.gpu_helpers import assert_parity, cuda, oracle_rows, say, to_dev  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -131,31 +131,28 @@ def test_batched_step(cuda, mode):
     g.close()
 
 
-def test_full_batched_step_sampled(cuda):
+def test_full_batched_step_every_output(cuda):
     """m = 8 through all 197 shapes of a step (28 layers + lm_head), in the
-    persistent launch the benchmark times: every matvec checked on 64
-    sampled rows (first, last, and a seeded spread) for all 8 x rows, and
-    the lm_head's 8 tokens against the oracle's full logits."""
+    persistent launch the benchmark times: every output of every matvec for
+    all 8 x rows against the oracle, and the lm_head's 8 tokens."""
     import torch
     m = 8
     say("full m=8 step: generating 197 matvecs")
     shapes, ws, xs = step_inputs(28, 151936, m, seed=2)
     descs = device_step(shapes, ws, xs, m, cuda)
     g, host = run_graph(descs, m, 1, cuda)
+    assert g.info() == (1, 0)
     g.launch()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(2)
-    say("full m=8 step: checking sampled rows against the oracle")
+    say("full m=8 step: checking every output against the oracle")
     for i, (name, n, p) in enumerate(shapes):
         y = descs[i]["y"].cpu().numpy()
-        rows = np.unique(np.concatenate([[0, p - 1], rng.integers(0, p, 62)]))
-        ref, tol = oracle.matvec_batched(ws[i][rows], xs[i])
-        assert_parity(y[:, rows], ref, tol, f"m=8 {name}")
-    ref, tol = oracle.matvec_batched(ws[-1], xs[-1])
-    y = descs[-1]["y"].cpu().numpy()
-    for r in range(m):
-        assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
-        assert int(host[r]) == oracle.argmax_f32(y[r])
+        ref, tol = oracle_rows(ws[i], xs[i])
+        assert_parity(y, ref, tol, f"m=8 {name}")
+        if i == len(shapes) - 1:
+            for r in range(m):
+                assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+                assert int(host[r]) == oracle.argmax_f32(y[r])
     g.close()
 
 
@@ -231,6 +228,38 @@ def test_levels_step_equals_standalone(cuda, m):
         for d, w_ in zip(descs, want):
             assert torch.equal(d["y"], w_)
         assert torch.equal(host, idx.cpu())
+    g.close()
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_levels_step_against_oracle(cuda, m):
+    """The levels graph (one persistent node per dependency level: q|k|v, o,
+    gate|up, down per layer, then the lm_head) against the oracle itself:
+    two layers and a 20,000-row lm_head, every output of every matvec for
+    every x row, the tokens accepted by the oracle and equal to the argmax
+    of the logits the graph wrote."""
+    import torch
+    import q8_block_quantized_amd as q8
+    shapes, ws, xs = step_inputs(2, 20000, m, seed=10 + m)
+    descs = device_step(shapes, ws, xs, m, cuda)
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, device=cuda, levels=layer_levels(2))
+    assert g.info() == (9, 0)
+    for launch in (g.launch, g.launch_kernel):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        host[:] = -9
+        torch.cuda.synchronize()
+        launch()
+        torch.cuda.synchronize()
+        for i, (name, n, p) in enumerate(shapes):
+            y = descs[i]["y"].cpu().numpy()
+            ref, tol = oracle.matvec_batched(ws[i], xs[i])
+            assert_parity(y, ref, tol, f"levels m={m} {name}")
+            if i == len(shapes) - 1:
+                for r in range(m):
+                    assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+                    assert int(host[r]) == oracle.argmax_f32(y[r])
     g.close()
 
 
