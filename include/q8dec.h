@@ -133,6 +133,24 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
                      int32_t *idx, int32_t m, int32_t n, int32_t p,
                      void *stream);
 
+/* q8_matvec_argmax for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and results (bit for bit) as
+ * q8_matvec_argmax, but the argmax workspace is a fixed 12,736-byte array
+ * in the library's own device memory (one per device, held until the
+ * process ends) instead of a per-stream allocation: this call, and the
+ * device set-up it may do on its first call on a device, call no hipMalloc,
+ * hipFree or other allocating routine.  The array holds the keys of at most
+ * Q8_MAX_M (32) activation rows: a larger m is refused with Q8_ERR_SHAPE.
+ * Every q8_matvec_argmax_noalloc call on one device shares that array, so
+ * two such calls that overlap in time on one device race and may return
+ * wrong indices: issue them in one stream order.  The array is zero when
+ * the library loads and each call leaves it zero.  Other arguments, layouts
+ * and errors as q8_matvec_argmax. */
+int q8_matvec_argmax_noalloc(const void *w, const float *x, float *y_or_null,
+                             int32_t *idx, int32_t m, int32_t n, int32_t p,
+                             void *stream);
+
 /* ---- int8-activation variant ----------------------------------------------- */
 
 /* The CPU's sdot form (inferno.rs "IV.4", the prose after the q8_matvec

@@ -94,6 +94,7 @@ def load(path: str = LIB_PATH):
         "q8_matvec_batched": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         "q8_argmax": (ctypes.c_int, [vp, i32, i32, vp, vp]),
         "q8_matvec_argmax": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
+        "q8_matvec_argmax_noalloc": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
         "q8_matvec_i8x": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         "q8_matvec_argmax_i8x": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp]),
         "q8_step_graph_build": (ctypes.c_int, [ctypes.POINTER(MatvecDesc), i32,
@@ -241,6 +242,25 @@ def q8_matvec_argmax(w, x, idx, p: int, y=None, stream=None) -> None:
     _check_w(w, n, p, x.device)
     _check(load().q8_matvec_argmax(_ptr(w), _ptr(x2), _ptr(y), _ptr(idx),
                                    m, n, p, _stream(stream, x.device)))
+
+
+def q8_matvec_argmax_noalloc(w, x, idx, p: int, y=None, stream=None) -> None:
+    """q8_matvec_argmax with the library's fixed per-device workspace (no
+    allocation; calls that overlap on one device race)."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    _need(idx, torch.int32, "idx", x.device)
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    m, n = x2.shape
+    if idx.numel() != m:
+        raise ValueError("idx must hold one int32 per row")
+    if y is not None:
+        _need(y, torch.float32, "y", x.device)
+        if y.numel() != m * p:
+            raise ValueError("y must hold m * p floats")
+    _check_w(w, n, p, x.device)
+    _check(load().q8_matvec_argmax_noalloc(_ptr(w), _ptr(x2), _ptr(y), _ptr(idx),
+                                           m, n, p, _stream(stream, x.device)))
 
 
 def q8_matvec_i8x(w, x, y, stream=None) -> None:

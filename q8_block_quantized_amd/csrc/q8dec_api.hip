@@ -56,6 +56,19 @@ struct DeviceState {
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 
+// Workspace of q8_matvec_argmax_noalloc: one argmax slot (team keys and
+// arrival counters for up to Q8_MAX_M activation rows), in the code
+// object's own device memory, so that entry point allocates nothing.  Each
+// device holds its own copy until the process ends; its address on a
+// device comes from hipGetSymbolAddress at that device's set-up
+// (g_scratch), never from the name in host code.  It is zero when the code
+// object loads, and every launch that uses it leaves it zero again (the
+// last arrival clears the keys and counters it used; `expected` and `host`
+// are never written, so they stay 0 and NULL).
+constexpr size_t kScratchBytes = sizeof(q8::ArgmaxSlot);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *g_scratch[kMaxDevices];  // per device, under g_mu
+
 // An argmax workspace, zeroed in the order of `stream` (the stream whose
 // argmax calls will use it), or, for the null stream's, before returning.
 int alloc_slot(q8::ArgmaxSlot **out, hipStream_t stream, bool on_stream) {
@@ -95,6 +108,15 @@ int check_device_locked(int dev) {
     st.status = Q8_ERR_CODE_OBJECT;
     return st.status;
   }
+  // this device's copy of the no-allocation workspace (dev is current)
+  void *ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    st.status = Q8_ERR_CODE_OBJECT;
+    return st.status;
+  }
+  g_scratch[dev] = ptr;
   st.status = Q8_OK;
   return Q8_OK;
 }
@@ -484,6 +506,27 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
   if ((st = stream_slot(dev, (hipStream_t)stream, &slot))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p,
                                    slot, idx, (hipStream_t)stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_matvec_argmax_noalloc(const void *w, const float *x, float *y_or_null,
+                             int32_t *idx, int32_t m, int32_t n, int32_t p,
+                             void *stream) {
+  if (!idx) return Q8_ERR_NULL;
+  // m <= Q8_MAX_M is also the scratch's limit: one key per row per group
+  int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
+  if (st) return st;
+  static_assert(sizeof(q8::ArgmaxSlot) <= kScratchBytes, "one slot fits the scratch");
+  int dev = 0;
+  if ((st = check_device(&dev))) return st;
+  q8::ArgmaxSlot *slot = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    slot = (q8::ArgmaxSlot *)g_scratch[dev];
+  }
+  if (!slot) return Q8_ERR_CODE_OBJECT;
+  hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y_or_null, m, n, p, slot, idx,
+                                   (hipStream_t)stream);
   return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
