@@ -13,8 +13,12 @@ is exactly --steps steps, bracketed by device synchronisation, after an
 untimed settling run (~0.3 s of the same work: the clocks' steady state) and
 --warmup steps.  Each step is
 one graph launch followed by a wait for the token: a spin on the pinned
-host slot that the kernel stores last (headline), and in a second timed run
-a full stream synchronisation (every output of the step complete).
+host slot that the argmax's last arrival stores (headline; other workgroups
+may still be finishing their last tiles then, but the next step's launch
+waits for them in stream order, so the average over the timed steps counts
+every step whole), and in a second timed run a full stream synchronisation
+after each step (every output complete), whose per-step times give the
+spread.
 """
 from __future__ import annotations
 
@@ -137,8 +141,12 @@ def time_graph_steps(torch, graphs, host, steps: int, warmup: int,
                      poll: bool = False, spread: dict = None):
     """Wall seconds per step of: launch the step graph, wait, read the token.
     The wait is a stream synchronisation (every output complete), or with
-    poll=True a spin on the pinned token slot, which the kernel writes last
-    (the token is on the host; the kernel may still be retiring).  The
+    poll=True a spin on the pinned token slot, which the argmax's last
+    arrival writes (the token is on the host; workgroups holding other
+    matvecs' last tiles may still be running, and the next launch queues
+    behind them on the stream).  The average is over the whole timed run,
+    closed by a synchronisation, so it counts every step whole; per-step
+    times (`spread`) are only meaningful with the synchronising wait.  The
     timed steps follow a settling run (see settle) and `warmup` steps."""
     stream = torch.cuda.current_stream()
     hv = host.numpy()
@@ -179,12 +187,12 @@ def time_graph_steps(torch, graphs, host, steps: int, warmup: int,
     return sec, toks
 
 
-def event_time(torch, fn, count: int, warmup: int = 3) -> float:
+def event_time(torch, fn, count: int, warmup: int = 3, settle_s: float = SETTLE_S) -> float:
     """Average HIP-event time (s) per call of fn(k), k = 0..count-1, issued
     back to back on torch's current stream between one pair of events (the
     GPU never waits on the host inside the bracket), after a settling run
     (see settle)."""
-    settle(torch, fn)
+    settle(torch, fn, settle_s)
     for k in range(warmup):
         fn(k)
     torch.cuda.synchronize()
@@ -198,37 +206,203 @@ def event_time(torch, fn, count: int, warmup: int = 3) -> float:
     return a.elapsed_time(b) * 1e-3 / count
 
 
-def cpu_baseline(sets, m_host, threads_req: int, budget_s: float):
-    """The oracle on the host cores over the first weight set's step, and a
-    parity check of the GPU outputs of that step against it."""
+BENCH_LIB = os.path.join(ROOT, "q8_block_quantized_amd", "libq8bench.so")
+
+
+def read_ceiling(torch, dev, nbytes: int = 1 << 31, reps: int = 20) -> dict:
+    """HBM read ceiling: a plain read of an `nbytes` buffer (2 GiB, far beyond
+    the 256 MB Infinity Cache) with coalesced 16-byte loads
+    (q8bench_read_stream), HIP-event timed over `reps` back-to-back reads for
+    a few grid sizes; the fastest is the ceiling."""
+    import ctypes
+    if not os.path.exists(BENCH_LIB):
+        raise RuntimeError(f"{BENCH_LIB} not built; run python -m q8_block_quantized_amd._build")
+    lib = ctypes.CDLL(BENCH_LIB)
+    lib.q8bench_read_stream.restype = ctypes.c_int
+    lib.q8bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(0x5A)
+    grids = [1024, 2048, 4096, 8192]
+    sink = torch.zeros(max(grids) * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    best, sweep = None, {}
+    for loads in (4, 8, 16):
+        for g in grids:
+            def one(k, g=g, loads=loads):
+                st = lib.q8bench_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), g,
+                                             loads, stream)
+                if st:
+                    raise RuntimeError(f"q8bench_read_stream: status {st}")
+            t = event_time(torch, one, reps, settle_s=0.05)
+            sweep[f"{loads}x{g}"] = round(nbytes / t / 1e9, 1)
+            if best is None or t < best[0]:
+                best = (t, g, loads)
+    del buf, sink
+    torch.cuda.empty_cache()
+    t, g, loads = best
+    return {"GBps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_us": round(t * 1e6, 2), "bytes": nbytes, "grid": g, "loads_per_thread": loads,
+            "sweep_GBps": sweep,
+            "kernel": "q8bench_read_stream: contiguous tiles of 256 x loads 16-byte "
+                      "chunks dealt round-robin to the workgroups, nontemporal loads; "
+                      "the fastest of loads 4, 8, 16 x grids 1024..8192"}
+
+
+def matvec_chain(torch, q8, dev, sets, copies: int = 240, reps: int = 10) -> dict:
+    """One matvec 1024 -> 2048 as graph nodes: a chain graph of `copies`
+    matvecs over distinct weight copies (535 MB, beyond the Infinity Cache),
+    launched back to back; the time per node is the GPU's per-matvec cost
+    without host dispatch."""
+    qs = [d["w"] for s in sets for d in s.descs if d["p"] == 2048 and d["n"] == 1024]
+    qs += [torch.from_numpy(gen.weights(2048, 1024, seed=0, index=4000 + c)
+                            .reshape(-1)).to(dev) for c in range(copies - len(qs))]
+    x = sets[0].descs[0]["x"]
+    ys = [torch.empty((1, 2048), dtype=torch.float32, device=dev) for _ in range(4)]
+    descs = [dict(w=qs[c], x=x, y=ys[c % 4], idx=None, n=1024, p=2048) for c in range(copies)]
+    g = q8.StepGraph(descs, 1, mode=q8.Q8_GRAPH_CHAIN)
+    assert g.info() == (copies, 0)
+    t = event_time(torch, lambda k: g.launch(), reps, warmup=2)
+    g.close()
+    sb = alg_bytes(1024, 2048, 1, True, False)
+    per = t / copies
+    return {"graph_us": round(t * 1e6, 2), "nodes": copies, "per_matvec_us": round(per * 1e6, 3),
+            "GBps": round(sb / per / 1e9, 1), "matvecs_per_s": round(1.0 / per, 1),
+            "alg_bytes": sb,
+            "note": f"chain graph of {copies} matvecs over distinct weight copies "
+                    f"({copies * weight_bytes_of(1024, 2048) / 1e6:.0f} MB), graphs "
+                    "launched back to back, HIP events"}
+
+
+def weight_bytes_of(n: int, p: int) -> int:
+    return p * (n // 32) * 34
+
+
+def layer_graphs(torch, q8, sets, layers: int = 32, reps: int = 10) -> dict:
+    """One layer's 7 matvecs as graph nodes: `layers` distinct layer copies
+    (535 MB) as a chain graph (7 nodes per layer) and as a levels graph
+    (q|k|v, o, gate|up, down: 4 nodes per layer), launched back to back."""
+    all_layers = [s.descs[7 * l:7 * l + 7] for s in sets for l in range(28)][:layers]
+    descs = [d for L in all_layers for d in L]
+    lyb = sum(alg_bytes(n, p, 1, True, False) for _, n, p in gen.LAYER_SHAPES)
+    out = {"alg_bytes_per_layer": lyb, "layers": layers}
+    chain = q8.StepGraph(descs, 1, mode=q8.Q8_GRAPH_CHAIN)
+    assert chain.info() == (7 * layers, 0)
+    t = event_time(torch, lambda k: chain.launch(), reps, warmup=2)
+    chain.close()
+    out["chain"] = {"nodes": 7 * layers, "per_layer_us": round(t / layers * 1e6, 2),
+                    "per_node_us": round(t / (7 * layers) * 1e6, 3),
+                    "GBps": round(lyb * layers / t / 1e9, 1)}
+    lv = []
+    for l in range(layers):
+        lv += [4 * l] * 3 + [4 * l + 1] + [4 * l + 2] * 2 + [4 * l + 3]
+    lg = q8.StepGraph(descs, 1, levels=lv)
+    assert lg.info() == (4 * layers, 0)
+    t = event_time(torch, lambda k: lg.launch(), reps, warmup=2)
+    lg.close()
+    out["levels"] = {"nodes": 4 * layers, "per_layer_us": round(t / layers * 1e6, 2),
+                     "per_node_us": round(t / (4 * layers) * 1e6, 3),
+                     "GBps": round(lyb * layers / t / 1e9, 1)}
+    out["note"] = (f"{layers} distinct layers' weights (535 MB), one graph launched back "
+                   "to back, HIP events")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_time(fn, runs: int) -> float:
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts)
+
+
+def cpu_configs(m_host, m8_x, ncpu: int, runs: int = 5) -> dict:
+    """The oracle (test infrastructure, plain binary64 C) timed on the host
+    cores for the five measured configurations, single-threaded and with
+    rows split over `ncpu` threads, the median of `runs` runs each.  Rates
+    use the same algorithmic bytes as the GPU figures.  Config 5 single-
+    threaded runs on a sample (layer 0's 7 matvecs and the lm_head, 29 % of
+    the step's bytes) to bound the time; every other entry is the whole
+    configuration."""
     import oracle
     orc = oracle.get()
-    s0 = sets
-    ws = [w for w in m_host["w"]]
-    xs = m_host["x"]
-    times = []
-    used = 1
-    worst = 0.0
-    ok_idx = True
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        ys = []
-        for i, (name, n, p) in enumerate(s0.shapes):
-            y, tol, used = orc.matvec_mt(ws[i], xs[i][0], threads_req)
-            ys.append((y, tol))
-        times.append(time.perf_counter() - t0)
-        if len(times) >= 3 or time.perf_counter() - t_start > budget_s:
-            break
-    # parity of the GPU step outputs (written by the last launch of set 0)
-    for i, d in enumerate(s0.descs):
-        y, tol = ys[i]
+    ws, xs = m_host["w"], m_host["x"]
+    shapes = gen.step_shapes()
+    lm = len(shapes) - 1
+
+    def mt(ids, x_of, threads):
+        def f():
+            for i in ids:
+                for r in range(x_of(i).shape[0]):
+                    orc.matvec_mt(ws[i], x_of(i)[r], threads)
+        return f
+
+    def st_batched(ids, x_of):
+        def f():
+            for i in ids:
+                orc.matvec_batched(ws[i], x_of(i))
+        return f
+
+    def nbytes(ids, m, logits=True):
+        return sum(alg_bytes(shapes[i][1], shapes[i][2], m, logits or i != lm, i == lm)
+                   for i in ids)
+
+    x1 = lambda i: xs[i]  # noqa: E731
+    x8 = lambda i: m8_x[i]  # noqa: E731
+    layer0 = list(range(7))
+    step = list(range(len(shapes)))
+    cfgs = {
+        "1_matvec_1024x2048": (lambda th: mt([0], x1, th) if th > 1 else st_batched([0], x1),
+                               nbytes([0], 1), None),
+        "2_layer_7_matvecs": (lambda th: mt(layer0, x1, th) if th > 1 else st_batched(layer0, x1),
+                              nbytes(layer0, 1), None),
+        "3_lm_head_argmax": (lambda th: mt([lm], x1, th) if th > 1 else st_batched([lm], x1),
+                             nbytes([lm], 1, logits=False), None),
+        "4_full_step_m1": (lambda th: mt(step, x1, th) if th > 1 else st_batched(step, x1),
+                           nbytes(step, 1, logits=False), None),
+        "5_full_step_m8": (lambda th: mt(step, x8, th) if th > 1 else st_batched(layer0 + [lm], x8),
+                           nbytes(step, 8, logits=False), nbytes(layer0 + [lm], 8, logits=False)),
+    }
+    out = {}
+    for name, (mk, b, b_sample) in cfgs.items():
+        t1 = _median_time(mk(1), runs)
+        tn = _median_time(mk(ncpu), runs)
+        b1 = b_sample if b_sample is not None else b
+        out[name] = {"single_thread_us": round(t1 * 1e6, 1),
+                     "single_thread_GBps": round(b1 / t1 / 1e9, 3),
+                     "all_cores_us": round(tn * 1e6, 1),
+                     "all_cores_GBps": round(b / tn / 1e9, 3)}
+        if b_sample is not None:
+            out[name]["single_thread_sample"] = "layer 0's 7 matvecs + lm_head at m = 8"
+    return out
+
+
+def cpu_parity(step_set, m_host, threads: int):
+    """The oracle over the first weight set's step (rows split over the host
+    cores) against the GPU outputs of that step: the worst err/tol and
+    whether the token is accepted."""
+    import oracle
+    orc = oracle.get()
+    worst, ok_idx, used = 0.0, True, 1
+    for i, d in enumerate(step_set.descs):
+        y, tol, used = orc.matvec_mt(m_host["w"][i], m_host["x"][i][0], threads)
         if d["y"] is not None:
             g = d["y"].cpu().numpy()[0]
             worst = max(worst, float(oracle.matvec_errors(g, y, tol).max()))
         if d["idx"] is not None:
             ok_idx = ok_idx and oracle.argmax_accepted(int(d["idx"][0].item()), y, tol)
-    return statistics.median(times), used, worst, ok_idx
+    return worst, ok_idx, used
 
 
 def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
@@ -275,6 +449,61 @@ def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
     }
 
 
+def trace_summary(path: str, name_filter: str = "q8", group: int = 0,
+                  skip_groups: int = 0) -> dict:
+    """Per-kernel durations and the idle gaps between consecutive dispatches
+    from a rocprofv3 kernel trace (``--kernel-trace --output-format csv``:
+    columns Kernel_Name, Start_Timestamp, End_Timestamp in ns).  Dispatches
+    whose name contains `name_filter` are kept, in start order.  With
+    `group` = nodes per graph launch, the dispatches form consecutive groups
+    of that many (the first `skip_groups` groups, warm-up and settling, are
+    dropped): gaps inside a group are the graph's own launch gaps, gaps
+    between groups the host's; each group's span runs from its first start
+    to its last end."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            if name_filter in name:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    rows.sort()
+    if group > 0:
+        rows = rows[skip_groups * group:]
+        rows = rows[:len(rows) // group * group]
+
+    def stats(v):
+        v = sorted(v)
+        if not v:
+            return None
+        return {"count": len(v), "p10": round(v[len(v) // 10] / 1e3, 3),
+                "median": round(statistics.median(v) / 1e3, 3),
+                "mean": round(sum(v) / len(v) / 1e3, 3),
+                "p90": round(v[(9 * len(v)) // 10] / 1e3, 3)}
+
+    per = {}
+    for a, b, n in rows:
+        per.setdefault(n[:100], []).append(b - a)
+    out = {"dispatches": len(rows),
+           "duration_us": {n: stats(v) for n, v in per.items()}}
+    gaps_in, gaps_between = [], []
+    for i in range(len(rows) - 1):
+        gap = rows[i + 1][0] - rows[i][1]
+        if group > 0 and (i + 1) % group == 0:
+            gaps_between.append(gap)
+        else:
+            gaps_in.append(gap)
+    out["gap_us" if group <= 0 else "gap_in_graph_us"] = stats(gaps_in)
+    if group > 0:
+        out["gap_between_graphs_us"] = stats(gaps_between)
+        spans = [rows[i + group - 1][1] - rows[i][0] for i in range(0, len(rows), group)]
+        busy = [sum(b - a for a, b, _ in rows[i:i + group]) for i in range(0, len(rows), group)]
+        out["graph_span_us"] = stats(spans)
+        out["graph_busy_us"] = stats(busy)
+        out["nodes_per_graph"] = group
+    return out
+
+
 def only_workload(args, torch, q8, dev) -> int:
     """One configuration alone, for a kernel trace or counters of its kernel."""
     out = {"workload": args.only, "steps": args.steps}
@@ -300,6 +529,23 @@ def only_workload(args, torch, q8, dev) -> int:
                    per_row_us=round(sw * 1e6 / m, 2), alg_bytes=bw)
         for g in gw:
             g.close()
+    elif args.only == "stream":
+        out.update(read_ceiling(torch, dev, reps=args.steps))
+    elif args.only in ("matvec_graph", "layer_graphs", "chain"):
+        sets = [StepSet(torch, dev, 0, 0, 1, False), StepSet(torch, dev, 0, 1000, 1, False)]
+        if args.only == "matvec_graph":
+            out.update(matvec_chain(torch, q8, dev, sets, reps=args.steps))
+        elif args.only == "layer_graphs":
+            out.update(layer_graphs(torch, q8, sets, reps=args.steps))
+        else:
+            host = torch.zeros(1, dtype=torch.int32).pin_memory()
+            chain = [q8.StepGraph(s.descs, 1, host_idx=host, mode=q8.Q8_GRAPH_CHAIN)
+                     for s in sets]
+            csec, _ = time_graph_steps(torch, chain, host, args.steps, args.warmup, poll=True)
+            out.update(step_latency_us=round(csec * 1e6, 2), nodes=197,
+                       per_node_us=round(csec * 1e6 / 197, 3))
+            for g in chain:
+                g.close()
     elif args.only == "decode":
         out.update(decode_step(torch, q8, dev, 1023, 4096, args.steps, args.warmup))
     elif args.only == "i8x_step":
@@ -336,17 +582,33 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode", "wide"],
+    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode", "wide",
+                                       "stream", "matvec_graph", "layer_graphs", "chain"],
                     default=None,
                     help="only time one other configuration (for profiling runs): "
                          "the fused lm_head (1024 -> 151,936 + argmax, m = 1), "
                          "the m = 8 step, the int8-activation step, the whole "
-                         "decode step at position 1023, or the m = 32 step; prints "
-                         "one JSON line")
+                         "decode step at position 1023, the m = 32 step, the HBM "
+                         "read ceiling, one matvec as a 240-node chain graph, one "
+                         "layer as chain and levels graphs, or the 197-node chain "
+                         "step; prints one JSON line")
+    ap.add_argument("--trace-summary", metavar="CSV", default=None,
+                    help="summarise a rocprofv3 kernel trace (csv) instead of "
+                         "measuring: per-kernel durations and gaps; no GPU use")
+    ap.add_argument("--trace-filter", default="q8",
+                    help="kernel-name substring kept by --trace-summary")
+    ap.add_argument("--trace-group", type=int, default=0,
+                    help="nodes per graph launch for --trace-summary")
+    ap.add_argument("--trace-skip", type=int, default=0,
+                    help="leading graph launches dropped by --trace-summary")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary, args.trace_filter,
+                                       args.trace_group, args.trace_skip), indent=1))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X "
               "and has no multi-GPU path; use --gpus 1", file=sys.stderr)
@@ -380,12 +642,13 @@ def main() -> int:
 
     log(f"headline: {args.steps} persistent-graph steps")
     # the headline waits for the token the way a decode loop does: spinning
-    # on the pinned slot the kernel writes last; the fully synchronised
-    # figure (every output of the step complete) is reported beside it
+    # on the pinned slot the argmax's last arrival writes; the fully
+    # synchronised figure (every output of the step complete) is reported
+    # beside it, with the spread of its per-step times
     spread = {}
-    sec, toks = time_graph_steps(torch, pers, host, args.steps, args.warmup,
-                                 poll=True, spread=spread)
-    ssec, stoks = time_graph_steps(torch, pers, host, args.steps, args.warmup)
+    sec, toks = time_graph_steps(torch, pers, host, args.steps, args.warmup, poll=True)
+    ssec, stoks = time_graph_steps(torch, pers, host, args.steps, args.warmup,
+                                   spread=spread)
     assert stoks == toks, "token differs between the two waits"
     # the same recorded step submitted as one kernel launch instead of a
     # hipGraphLaunch (reported beside the headline, never as it)
@@ -427,8 +690,8 @@ def main() -> int:
             "graph_nodes": {"kernel": 1, "memcpy": 0},
         },
         "step_latency_us": round(sec * 1e6, 2),
-        "step_latency_spread_us": spread,
         "step_latency_synchronized_us": round(ssec * 1e6, 2),
+        "step_latency_synchronized_spread_us": spread,
         "step_latency_kernel_launch_us": round(ksec * 1e6, 2),
         "pct_of_hbm_peak": round(100 * step_bytes / sec / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -506,6 +769,12 @@ def main() -> int:
             "GBps": round(lb0 / lt0 / 1e9, 1),
         }
 
+        log("HBM read ceiling (plain 16-byte-load read of 2 GiB)")
+        result["hbm_read_ceiling"] = read_ceiling(torch, dev)
+        log("single matvec 1024->2048 as graph nodes (240-node chain, 535 MB)")
+        extra["single_matvec_1024x2048_graph"] = matvec_chain(torch, q8, dev, sets)
+        log("one layer's 7 matvecs as graph nodes (32 layers: chain and levels)")
+        extra["layer_7_matvecs_graph"] = layer_graphs(torch, q8, sets)
         log("single matvec 1024->2048 (rotating 240 copies, 535 MB)")
         qs = [d["w"] for s in sets for d in s.descs if d["p"] == 2048 and d["n"] == 1024]
         qs += [torch.from_numpy(gen.weights(2048, 1024, seed=0, index=4000 + c)
@@ -520,8 +789,10 @@ def main() -> int:
             "GBps": round(sb / st / 1e9, 1),
             "matvecs_per_s": round(1.0 / st, 1),
             "hot_avg_us": round(hot * 1e6, 2),
-            "note": ("back-to-back launches over 240 distinct weight copies (535 MB, "
-                     "beyond the 256 MB Infinity Cache); hot: one copy, cached"),
+            "note": ("back-to-back launches from Python over 240 distinct weight "
+                     "copies (535 MB, beyond the 256 MB Infinity Cache); hot: one copy, "
+                     "cached; bound by the host's dispatch, not the GPU (the graph "
+                     "figures above are the GPU's)"),
         }
         del qs
 
@@ -536,6 +807,7 @@ def main() -> int:
         extra["layer_7_matvecs_stream"] = {
             "avg_us": round(lt2 * 1e6, 2),
             "GBps": round(lyb / lt2 / 1e9, 1),
+            "note": "7 launches from Python per layer: host-dispatch bound",
         }
 
         log("int8-activation step (persistent graph, x quantised per 32-block)")
@@ -605,27 +877,36 @@ def main() -> int:
         result["extra"] = extra
 
     if not args.no_cpu:
-        log("cpu baseline: the oracle on the host cores")
+        log("cpu baseline: the oracle on the host cores (configs 1-5, 1 thread and all)")
         try:
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:  # pragma: no cover
             ncpu = os.cpu_count() or 1
         m_host = {"w": [], "x": []}
+        m8_x = []
         for i, (name, n, p) in enumerate(sets[0].shapes):
             m_host["w"].append(gen.weights(p, n, seed=0, index=i))
             m_host["x"].append(gen.activations(1, n, seed=0, index=i))
+            m8_x.append(gen.activations(8, n, seed=0, index=5000 + i))
         # the GPU outputs compared below come from one launch of set 0
         pers[0].launch()
         torch.cuda.synchronize()
-        csec_, used, worst, ok_idx = cpu_baseline(sets[0], m_host, ncpu, 20.0)
+        worst, ok_idx, used = cpu_parity(sets[0], m_host, ncpu)
+        cfg = cpu_configs(m_host, m8_x, ncpu)
+        head = cfg["4_full_step_m1"]
         result["cpu_baseline"] = {
-            "value": round(step_bytes / csec_ / 1e9, 3),
+            "value": head["all_cores_GBps"],
             "unit": "GB/s",
             "cores": used,
             "kind": "oracle",
-            "sample": ("the full 197-matvec step (set 0) computed by the oracle, "
-                       "rows split over the host cores; median of up to 3 runs"),
-            "step_latency_us": round(csec_ * 1e6, 1),
+            "sample": ("the full 197-matvec step (weight set 0, m = 1) computed by the "
+                       "oracle with rows split over the host cores, median of 5 runs; "
+                       "configs: each measured configuration single-threaded and on "
+                       "all cores"),
+            "cpu_model": cpu_model(),
+            "runs": 5,
+            "step_latency_us": head["all_cores_us"],
+            "configs": cfg,
             "gpu_parity_max_err_over_tol": round(worst, 5),
             "gpu_argmax_accepted": bool(ok_idx),
         }

@@ -16,6 +16,9 @@ SOURCES = [os.path.join(CSRC, "q8dec_api.hip"),
            os.path.join(CSRC, "q8dec_kernels.hip"),
            os.path.join(CSRC, "q8dec_decode.hip")]
 LIB = os.path.join(HERE, "libq8dec.so")
+# the benchmark's read-stream helper (not part of the decode path)
+BENCH_SOURCES = [os.path.join(CSRC, "q8bench.hip")]
+BENCH_LIB = os.path.join(HERE, "libq8bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -29,20 +32,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(sources, lib, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libq8dec")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
     if verbose:
         noise = "packed-fp32-ops"
         for line in (res.stdout + res.stderr).splitlines():
             if noise not in line:
                 print(line)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles libq8dec.so and the benchmark's libq8bench.so."""
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -45,6 +45,29 @@ def test_exports_every_declared_function(lib):
     assert set(names) <= exported
 
 
+def test_bench_helper_exports_its_header():
+    """libq8bench.so (the benchmark's read-stream helper) exports every
+    function include/q8bench.h declares, and refuses bad arguments before
+    launching anything."""
+    path = os.path.join(ROOT, "q8_block_quantized_amd", "libq8bench.so")
+    with open(os.path.join(ROOT, "include", "q8bench.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(q8bench_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["q8bench_read_stream"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path],
+                         capture_output=True, text=True, check=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (q8bench_[a-z0-9_]+)", out))
+    b = ctypes.CDLL(path)
+    b.q8bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert b.q8bench_read_stream(None, 16, X, 1, 4, None) == 1
+    assert b.q8bench_read_stream(W, 16, None, 1, 4, None) == 1
+    assert b.q8bench_read_stream(W, 17, X, 1, 4, None) == 2
+    assert b.q8bench_read_stream(W + 4, 16, X, 1, 4, None) == 2
+    assert b.q8bench_read_stream(W, 16, X, 0, 4, None) == 2
+    assert b.q8bench_read_stream(W, 16, X, 1, 5, None) == 2
+
+
 def test_status_names(lib):
     want = {0: "q8_ok", 1: "q8_err_null", 2: "q8_err_shape", 3: "q8_err_align",
             4: "q8_err_no_device", 5: "q8_err_arch", 6: "q8_err_code_object",
