@@ -1193,8 +1193,11 @@ __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
 // 29.6 µs, with int8 activations 30.2 → 28.8 µs; not batched int8, where
 // it is neutral) and the batched matrix-core step (m = 8: 170 → 153 µs);
 // the m = 1 and int8-activation steps run slower with it (+1–3 %).
+// NBLS: 0, or the blocks per lane (1, 2, 3) of every matvec of the launch,
+// known at compile time (a standalone staged matvec), so the kernel holds
+// one copy of the row loop instead of one per width and output mode.
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
-template <bool M1, bool ANY, bool I8X, bool PRIO, class Src>
+template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr) {
@@ -1300,9 +1303,9 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const bool more2 = more && tn2 < end;
     const Job nxt2 = more2 ? job_after(nxt, tn2) : nxt;
     const bool keys = cur.d.idx != nullptr;
-    const bool devy = M1 && !I8X && (cur.d.flags & kDescDeviceOut);
+    const bool devy = M1 && !I8X && NBLS == 0 && (cur.d.flags & kDescDeviceOut);
     if (I8X) {
-      const int nbl = nbl_of(cur.d.n);
+      const int nbl = NBLS ? NBLS : nbl_of(cur.d.n);
       if (M1) {
         if (nbl == 1) staged_m1_i8<1>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
         else if (nbl == 2) staged_m1_i8<2>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
@@ -1313,7 +1316,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         else staged_mb_i8<3>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
       }
     } else if (staged(cur)) {
-      const int nbl = nbl_of(cur.d.n);
+      const int nbl = NBLS ? NBLS : nbl_of(cur.d.n);
       if (devy) {  // outputs read by the launch's epilogue (decode step levels)
         if (nbl == 1) staged_m1<1, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
         else if (nbl == 2) staged_m1<2, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
@@ -1629,7 +1632,7 @@ __device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t s
 // One matvec (descriptor passed by value), its tiles round-robin over the
 // grid (gridDim.x <= tiles, so every workgroup arrives at the argmax): at
 // any moment the grid streams one contiguous window of the weights.
-template <bool M1, bool ANY, bool I8X>
+template <bool M1, bool ANY, bool I8X, int NBLS>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -1638,7 +1641,7 @@ mv_kernel(StepDesc d, int32_t m) {
   // four consecutive tiles on one XCD (as the step's groups)
   const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
   const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
-  run_tiles<M1, ANY, I8X, M1 || !I8X>(src, first, d.tile_end, gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X, M1 || !I8X, NBLS>(src, first, d.tile_end, gridDim.x, 0, m, lds);
 }
 
 // The decode step: every tile of every descriptor of a device-side table
@@ -1655,7 +1658,7 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY, I8X, !M1 && !I8X>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
+  run_tiles<M1, ANY, I8X, !M1 && !I8X, 0>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
                                         g.size, g.d0, m, lds, pro);
   if constexpr (M1 && !I8X) {
     if (epi) {
@@ -1745,7 +1748,7 @@ int resident_wgs(K kernel, size_t lds, int dev) {
 
 // Occupancy-limited grid of a single-matvec kernel variant, cached per
 // device, for the largest LDS a launch of that variant can ask for.
-template <bool M1, bool ANY, bool I8X>
+template <bool M1, bool ANY, bool I8X, int NBLS>
 int mv_grid_cap(int dev) {
   static int cache[64] = {0};
   int &c = cache[dev & 63];
@@ -1754,7 +1757,7 @@ int mv_grid_cap(int dev) {
                        : M1 ? kTileMaxBytes + (size_t)kMaxLdsBlocks * 36 * 4
                             : kMfmaTileBytes + (size_t)kRedFloats * 4 +
                                   (ANY ? (size_t)kXMaxFloats / 32 * 36 * 4 : 0);
-    c = resident_wgs(mv_kernel<M1, ANY, I8X>, lds, dev);
+    c = resident_wgs(mv_kernel<M1, ANY, I8X, NBLS>, lds, dev);
   }
   return c;
 }
@@ -1766,11 +1769,11 @@ int wide_grid_cap(int dev) {
   return c;
 }
 
-template <bool M1, bool ANY, bool I8X>
+template <bool M1, bool ANY, bool I8X, int NBLS = 0>
 hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  const int cap = mv_grid_cap<M1, ANY, I8X>(dev);
+  const int cap = mv_grid_cap<M1, ANY, I8X, NBLS>(dev);
   // Every workgroup takes whole rounds of tiles, so the last round may be
   // part-empty.  Among tile heights from the largest down to three quarters
   // of it, take the one whose busiest workgroup costs least, counting a
@@ -1792,7 +1795,7 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   const int32_t ntiles = tiles_of(d);
   d.tile_end = ntiles;
   const int grid = ntiles < cap ? ntiles : cap;
-  hipLaunchKernelGGL((mv_kernel<M1, ANY, I8X>), dim3(grid), dim3(kWG),
+  hipLaunchKernelGGL((mv_kernel<M1, ANY, I8X, NBLS>), dim3(grid), dim3(kWG),
                      I8X ? lds_bytes_i8x(m, d.n) : lds_bytes_for(m, d.n), s, d, m);
   return hipGetLastError();
 }
@@ -1864,12 +1867,21 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
            (p + d.rows_per_tile - 1) / d.rows_per_tile < 512)
       d.rows_per_tile >>= 1;
   }
-  if (i8x)
-    return m == 1 ? launch_mv<true, false, true>(d, m, s) : launch_mv<false, false, true>(d, m, s);
+  // one matvec at m = 1 on the staged path: the kernel for its width
+  const int nbl = nbl_of(n);
+  if (i8x) {
+    if (m > 1) return launch_mv<false, false, true>(d, m, s);
+    return nbl == 1 ? launch_mv<true, false, true, 1>(d, m, s)
+           : nbl == 2 ? launch_mv<true, false, true, 2>(d, m, s)
+                      : launch_mv<true, false, true, 3>(d, m, s);
+  }
   const bool staged = path == kStaged || path == kMfma;
-  if (m == 1)
-    return staged ? launch_mv<true, false, false>(d, m, s)
-                  : launch_mv<true, true, false>(d, m, s);
+  if (m == 1) {
+    if (!staged) return launch_mv<true, true, false>(d, m, s);
+    return nbl == 1 ? launch_mv<true, false, false, 1>(d, m, s)
+           : nbl == 2 ? launch_mv<true, false, false, 2>(d, m, s)
+                      : launch_mv<true, false, false, 3>(d, m, s);
+  }
   return staged ? launch_mv<false, false, false>(d, m, s)
                 : launch_mv<false, true, false>(d, m, s);
 }
