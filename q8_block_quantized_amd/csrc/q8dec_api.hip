@@ -226,6 +226,7 @@ struct SegmentLaunch {
   int kind = kStepNode;
   const q8::Epilogue *epi = nullptr;
   const q8::Prologue *pro = nullptr;
+  bool dec = false;  // the decode step's kernel variant
   q8::AttnArgs attn{};
   const float *nx = nullptr, *nw = nullptr;
   float *nout = nullptr, *ncopy = nullptr;
@@ -242,7 +243,7 @@ hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
     return q8::launch_step_start(L.nx, L.nw, L.nout, L.ncopy, L.ndim, L.neps, L.npos,
                                  L.nfreq, L.rope_out, s);
   return q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
-                         L.all_staged, s, i8x, L.epi, L.pro);
+                         L.all_staged, s, i8x, L.epi, L.pro, L.dec);
 }
 
 struct q8_step_graph {
@@ -309,7 +310,7 @@ namespace q8 {
 // workgroups with contiguous tile ranges of about equal weight bytes, and
 // for every argmax descriptor the arrivals each argmax team waits for.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan, bool i8x) {
+              int group_size, StepPlan &plan, bool i8x, bool dec) {
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
   plan.i8x = i8x;
@@ -358,7 +359,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   const int32_t ntiles = (int32_t)tiles;
   plan.lds = widest;
   if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;
-  int grid = step_grid(dev, m, plan.lds, plan.all_staged, i8x);
+  int grid = step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
   if (group_size < 1) group_size = 1;
@@ -835,7 +836,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   std::vector<q8::StepPlan> plans(lv.size());
   for (size_t i = 0; i < lv.size(); i++) {
     st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
-                       plans[i]);
+                       plans[i], false, true);
     if (st) return st;
   }
   // The element-wise steps between matvecs run as prologues when every
@@ -1000,6 +1001,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
                     (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged};
     L.epi = epi;
     L.pro = pro;
+    L.dec = true;
     g->launches.push_back(L);
   };
   {

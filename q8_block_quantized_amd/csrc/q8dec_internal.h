@@ -113,10 +113,14 @@ hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
 // once every tile of the launch is written (see Epilogue).
 struct Epilogue;
 struct Prologue;
+// `dec`: the decode step's kernel variant (prologues and epilogues; m = 1,
+// binary32 activations), kept apart so the other launches do not carry its
+// code.
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x = false,
-                       const Epilogue *epi = nullptr, const Prologue *pro = nullptr);
+                       const Epilogue *epi = nullptr, const Prologue *pro = nullptr,
+                       bool dec = false);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
@@ -129,7 +133,8 @@ int step_rows_per_tile(int n, int m, bool i8x = false);
 size_t step_lds_bytes(int m, int n, bool i8x = false);
 
 // Workgroups of the step kernel resident at once on `device` (the grid).
-int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x = false);
+int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x = false,
+              bool dec = false);
 
 // Everything a persistent step launch needs, worked out on the host.
 struct StepPlan {
@@ -247,5 +252,5 @@ struct q8_matvec_desc;
 namespace q8 {
 // Plans a persistent step (q8dec_api.hip) with groups of `group_size`.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan, bool i8x = false);
+              int group_size, StepPlan &plan, bool i8x = false, bool dec = false);
 }  // namespace q8

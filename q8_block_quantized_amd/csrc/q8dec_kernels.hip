@@ -1197,7 +1197,7 @@ __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
 // known at compile time (a standalone staged matvec), so the kernel holds
 // one copy of the row loop instead of one per width and output mode.
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
-template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, class Src>
+template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr) {
@@ -1232,7 +1232,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   bool more = t + stride < end;
   Job nxt = more ? job_after(cur, t + stride) : cur;
   ProRegs prr;
-  if constexpr (M1 && !I8X) {
+  if constexpr (DEC) {
     if (pro) pro_load(pro, prr);  // before the tile's loads: see pro_load
   }
   if (staged(cur) || mfma(cur))
@@ -1242,7 +1242,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   // share x (the same pointer and width) are staged once
   const float *xptr = nullptr, *xaptr = nullptr;
   int32_t xn = 0, xan = 0;
-  if constexpr (M1 && !I8X) {
+  if constexpr (DEC) {
     if (pro) {  // the launch's x is pro->out, computed here while the first tile loads
       pro_finish(pro, prr, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
       xptr = pro->out;
@@ -1303,7 +1303,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const bool more2 = more && tn2 < end;
     const Job nxt2 = more2 ? job_after(nxt, tn2) : nxt;
     const bool keys = cur.d.idx != nullptr;
-    const bool devy = M1 && !I8X && NBLS == 0 && (cur.d.flags & kDescDeviceOut);
+    const bool devy = DEC && (cur.d.flags & kDescDeviceOut);
     if (I8X) {
       const int nbl = NBLS ? NBLS : nbl_of(cur.d.n);
       if (M1) {
@@ -1641,26 +1641,30 @@ mv_kernel(StepDesc d, int32_t m) {
   // four consecutive tiles on one XCD (as the step's groups)
   const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
   const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
-  run_tiles<M1, ANY, I8X, M1 || !I8X, NBLS>(src, first, d.tile_end, gridDim.x, 0, m, lds);
+  run_tiles<M1, ANY, I8X, M1 || !I8X, NBLS, false>(src, first, d.tile_end, gridDim.x, 0, m,
+                                                     lds);
 }
 
-// The decode step: every tile of every descriptor of a device-side table
-// (count entries in tile order), with no ordering between descriptors.
-// Workgroups form groups; a group interleaves its contiguous tile range.
-// epi (or NULL; m = 1 with binary32 activations only): element-wise work
-// that the last workgroup to finish runs once every tile is written.
-template <bool M1, bool ANY, bool I8X>
+// The persistent step: every tile of every descriptor of a device-side
+// table (count entries in tile order), with no ordering between
+// descriptors.  Workgroups form groups; a group interleaves its contiguous
+// tile range.  DEC (m = 1 with binary32 activations only): the whole decode
+// step's variant, with the prologue (pro, or NULL) and the epilogue (epi, or
+// NULL: element-wise work that the last workgroup to finish runs once every
+// tile is written); the other launches do not carry that code.
+template <bool M1, bool ANY, bool I8X, bool DEC>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
             const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro) {
+  static_assert(!DEC || (M1 && !I8X), "the decode variant is m = 1, binary32");
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<M1, ANY, I8X, !M1 && !I8X, 0>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
-                                        g.size, g.d0, m, lds, pro);
-  if constexpr (M1 && !I8X) {
+  run_tiles<M1, ANY, I8X, !M1 && !I8X, 0, DEC>(src, g.t0 + group_slot(j, g.first, g.size),
+                                               g.t1, g.size, g.d0, m, lds, pro);
+  if constexpr (DEC) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
       dec::run_epilogue(epi, blockIdx.x, gridDim.x, lds);
@@ -1820,16 +1824,19 @@ bool wide_shape_ok(int n) { return n > 0 && n % 256 == 0; }
 
 bool i8x_shape_ok(int n) { return path_of(1, n) == kStaged; }
 
-int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x) {
+int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x, bool dec) {
   if (m > kMaxM) return resident_wgs(wide_step_kernel, lds, device);
   if (i8x)
-    return m == 1 ? resident_wgs(step_kernel<true, false, true>, lds, device)
-                  : resident_wgs(step_kernel<false, false, true>, lds, device);
+    return m == 1 ? resident_wgs(step_kernel<true, false, true, false>, lds, device)
+                  : resident_wgs(step_kernel<false, false, true, false>, lds, device);
+  if (m == 1 && dec)
+    return all_staged ? resident_wgs(step_kernel<true, false, false, true>, lds, device)
+                      : resident_wgs(step_kernel<true, true, false, true>, lds, device);
   if (m == 1)
-    return all_staged ? resident_wgs(step_kernel<true, false, false>, lds, device)
-                      : resident_wgs(step_kernel<true, true, false>, lds, device);
-  return all_staged ? resident_wgs(step_kernel<false, false, false>, lds, device)
-                    : resident_wgs(step_kernel<false, true, false>, lds, device);
+    return all_staged ? resident_wgs(step_kernel<true, false, false, false>, lds, device)
+                      : resident_wgs(step_kernel<true, true, false, false>, lds, device);
+  return all_staged ? resident_wgs(step_kernel<false, false, false, false>, lds, device)
+                    : resident_wgs(step_kernel<false, true, false, false>, lds, device);
 }
 
 hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
@@ -1889,40 +1896,33 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi,
-                       const Prologue *pro) {
-  // m = 1 binary32 only, and a prologue only where every tile is staged
-  if ((epi || pro) && (m != 1 || i8x)) return hipErrorInvalidValue;
+                       const Prologue *pro, bool dec) {
+  // prologues and epilogues: the decode variant (m = 1, binary32), and a
+  // prologue only where every tile is staged
+  if ((epi || pro) && !dec) return hipErrorInvalidValue;
+  if (dec && (m != 1 || i8x)) return hipErrorInvalidValue;
   if (pro && !all_staged) return hipErrorInvalidValue;
+#define Q8_STEP(M1, ANY, I8X, DEC)                                                          \
+  hipLaunchKernelGGL((step_kernel<M1, ANY, I8X, DEC>), dim3(grid), dim3(kWG), lds, s, descs, \
+                     count, groups, group_size, m, epi, pro)
   if (m > kMaxM) {
     if (i8x) return hipErrorInvalidValue;
     hipLaunchKernelGGL(wide_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,
                        group_size, m);
-    return hipGetLastError();
-  }
-  if (i8x) {
-    if (m == 1)
-      hipLaunchKernelGGL((step_kernel<true, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
-    else
-      hipLaunchKernelGGL((step_kernel<false, false, true>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
-    return hipGetLastError();
-  }
-  if (m == 1) {
-    if (all_staged)
-      hipLaunchKernelGGL((step_kernel<true, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
-    else
-      hipLaunchKernelGGL((step_kernel<true, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
+  } else if (i8x) {
+    if (m == 1) Q8_STEP(true, false, true, false);
+    else Q8_STEP(false, false, true, false);
+  } else if (dec) {
+    if (all_staged) Q8_STEP(true, false, false, true);
+    else Q8_STEP(true, true, false, true);
+  } else if (m == 1) {
+    if (all_staged) Q8_STEP(true, false, false, false);
+    else Q8_STEP(true, true, false, false);
   } else {
-    if (all_staged)
-      hipLaunchKernelGGL((step_kernel<false, false, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
-    else
-      hipLaunchKernelGGL((step_kernel<false, true, false>), dim3(grid), dim3(kWG), lds,
-                         s, descs, count, groups, group_size, m, epi, pro);
+    if (all_staged) Q8_STEP(false, false, false, false);
+    else Q8_STEP(false, true, false, false);
   }
+#undef Q8_STEP
   return hipGetLastError();
 }
 
