@@ -51,20 +51,29 @@ def step_shapes():
     return out
 
 
-def build() -> None:
-    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", _LIB, "-lm", "-lpthread"],
+def build(out: str = _LIB, cc: str = "gcc", extra=()) -> str:
+    """Compile the generator (optionally elsewhere, with another compiler
+    and extra flags: the sanitizer test builds an instrumented copy)."""
+    subprocess.run([cc, *CFLAGS, *extra, _SRC, "-o", out, "-lm", "-lpthread"],
                    check=True)
+    return out
 
 
 _lib = None
 
 
-def _load():
+def load(path: str = _LIB):
+    """Loads the generator library (builds the default one if absent); a
+    later call with another path is ignored once one is loaded."""
+    return _load(path)
+
+
+def _load(path: str = _LIB):
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if path == _LIB and not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         u64, i64, u32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_uint32
         lib.q8g_stream_key.restype = u64
         lib.q8g_stream_key.argtypes = [u64, u32, u32, u32]

@@ -29,9 +29,10 @@ REL_TOL = 1e-4
 ABS_TOL = 1e-6
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle (optionally another source, for mutation tests)."""
-    subprocess.run(["gcc", *CFLAGS, src, "-o", out, "-lm", "-lpthread"],
+def build(src: str = _SRC, out: str = _LIB, cc: str = "gcc", extra=()) -> str:
+    """Compile the oracle (optionally another source, for mutation tests, or
+    with another compiler and extra flags, for the sanitizer test)."""
+    subprocess.run([cc, *CFLAGS, *extra, src, "-o", out, "-lm", "-lpthread"],
                    check=True)
     return out
 

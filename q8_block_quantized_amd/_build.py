@@ -32,9 +32,15 @@ FLAGS = [
 ]
 
 
-def _compile(sources, lib, verbose: bool) -> str:
+# Host-code sanitizers for the CPU test of the library's host logic: each
+# -fsanitize= applies to the host pass only (the GPU code is built as usual).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-g"]
+
+
+def _compile(sources, lib, verbose: bool, extra=()) -> str:
     tmp = lib + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra, *sources, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
@@ -52,6 +58,12 @@ def build(verbose: bool = False) -> str:
     """Compiles libq8dec.so and the benchmark's libq8bench.so."""
     _compile(BENCH_SOURCES, BENCH_LIB, verbose)
     return _compile(SOURCES, LIB, verbose)
+
+
+def build_sanitized(out: str) -> str:
+    """libq8dec with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code, at `out` (for the CPU test; never the library that ships)."""
+    return _compile(SOURCES, out, False, SANITIZE_FLAGS)
 
 
 if __name__ == "__main__":

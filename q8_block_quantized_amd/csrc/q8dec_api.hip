@@ -610,8 +610,9 @@ int capture_graph(q8_step_graph *g, q8_step_graph **out, F record) {
 // persistent kernel node, the nodes in level order.
 int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t count,
                 int32_t m, int32_t *host_idx, int32_t mode, q8_step_graph **out) {
-  if (!out || !descs) return Q8_ERR_NULL;
-  *out = nullptr;
+  if (!out) return Q8_ERR_NULL;
+  *out = nullptr;  // on every failure the caller holds no handle
+  if (!descs) return Q8_ERR_NULL;
   if (count < 1 || count > Q8_MAX_DESCS) return Q8_ERR_COUNT;
   if (mode != Q8_GRAPH_CHAIN && mode != Q8_GRAPH_PERSISTENT &&
       mode != Q8_GRAPH_PERSISTENT_I8X && mode != Q8_GRAPH_LEVELS)

@@ -1,0 +1,206 @@
+// Host-side checks of libq8dec, built with AddressSanitizer and
+// UndefinedBehaviorSanitizer on its host code (tests/test_sanitizers.py
+// builds both and runs this program on a machine without a GPU).
+//
+// 1. Every entry point refuses bad arguments with its named status before
+//    any GPU work (the Algenta "Metal LLM decode" page's refusals with
+//    status codes), and the status names cover every code.
+// 2. The persistent-step planner (q8::plan_step), on the host with no
+//    device (the occupancy queries fall back to one workgroup per compute
+//    unit): for a set of step shapes, the workgroup groups partition the
+//    tiles exactly, and the arrivals each argmax team waits for equal a
+//    count taken by walking every workgroup's tiles one by one.
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../include/q8dec.h"
+#include "../q8_block_quantized_amd/csrc/q8dec_internal.h"
+
+static int g_fail = 0;
+#define CHECK(c)                                                        \
+  do {                                                                  \
+    if (!(c)) {                                                         \
+      std::fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #c); \
+      g_fail++;                                                         \
+    }                                                                   \
+  } while (0)
+
+// aligned addresses that are never dereferenced (every call fails first)
+static void *const W = (void *)0x10000;
+static float *const X = (float *)0x20000;
+static float *const Y = (float *)0x30000;
+static int32_t *const I = (int32_t *)0x40000;
+
+static void refusals() {
+  for (int s = -3; s < 20; s++) CHECK(q8_status_name(s) != nullptr);
+  CHECK(std::strcmp(q8_status_name(12), "q8_err_levels") == 0);
+  CHECK(std::strcmp(q8_status_name(13), "q8_code_out_of_range") == 0);
+  int32_t count = -1;
+  CHECK(q8_device_count(nullptr) == Q8_ERR_NULL);
+  CHECK(q8_device_count(&count) == Q8_OK && count >= 0);
+  (void)q8_last_hip_error();
+
+  CHECK(q8_matvec(nullptr, X, Y, 32, 1, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_matvec(W, X, Y, 33, 1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec(W, X, Y, 32, -1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec(W, X, Y, Q8_MAX_N + 32, 1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec((char *)W + 2, X, Y, 32, 1, nullptr) == Q8_ERR_ALIGN);
+  CHECK(q8_matvec(W, X + 1, Y, 32, 1, nullptr) == Q8_ERR_ALIGN);
+  CHECK(q8_matvec_batched(W, X, Y, 0, 32, 1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_batched(W, X, Y, 33, 256, 1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_batched(W, X, Y, 9, 288, 1, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_argmax(X, 0, 5, I, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_argmax(X, 1, 0, I, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_argmax(nullptr, 1, 5, I, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_argmax(X, 1, 5, (int32_t *)((char *)I + 2), nullptr) == Q8_ERR_ALIGN);
+  CHECK(q8_matvec_argmax(W, X, nullptr, nullptr, 1, 32, 5, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_matvec_argmax(W, X, nullptr, I, 1, 32, 0, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_argmax_noalloc(W, X, nullptr, nullptr, 1, 32, 5, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_matvec_argmax_noalloc(W, X, nullptr, I, 33, 256, 5, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_i8x(W, X, Y, 1, 96, 4, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_i8x(W, X, Y, 9, 256, 4, nullptr) == Q8_ERR_SHAPE);
+  CHECK(q8_matvec_argmax_i8x(W, X, nullptr, I, 1, 4096, 4, nullptr) == Q8_ERR_SHAPE);
+
+  q8_matvec_desc d{W, X, Y, nullptr, 256, 8};
+  q8_step_graph *g = (q8_step_graph *)0x1;
+  CHECK(q8_step_graph_build(&d, 1, 1, nullptr, 0, nullptr, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_step_graph_build(nullptr, 1, 1, nullptr, 0, nullptr, &g) == Q8_ERR_NULL && !g);
+  CHECK(q8_step_graph_build(&d, 0, 1, nullptr, 0, nullptr, &g) == Q8_ERR_COUNT);
+  CHECK(q8_step_graph_build(&d, Q8_MAX_DESCS + 1, 1, nullptr, 0, nullptr, &g) == Q8_ERR_COUNT);
+  CHECK(q8_step_graph_build(&d, 1, 1, nullptr, 7, nullptr, &g) == Q8_ERR_MODE);
+  CHECK(q8_step_graph_build(&d, 1, 1, nullptr, Q8_GRAPH_LEVELS, nullptr, &g) == Q8_ERR_MODE);
+  CHECK(q8_step_graph_build(&d, 1, 0, nullptr, 0, nullptr, &g) == Q8_ERR_SHAPE);
+  const int32_t lv_bad[2] = {1, 0};
+  q8_matvec_desc two[2] = {d, d};
+  CHECK(q8_step_graph_build_levels(two, nullptr, 2, 1, nullptr, nullptr, &g) == Q8_ERR_NULL);
+  CHECK(q8_step_graph_build_levels(two, lv_bad, 2, 1, nullptr, nullptr, &g) == Q8_ERR_LEVELS);
+  CHECK(q8_step_graph_launch(nullptr, nullptr) == Q8_ERR_BAD_HANDLE);
+  CHECK(q8_step_graph_launch_kernel(nullptr, nullptr) == Q8_ERR_BAD_HANDLE);
+  CHECK(q8_step_graph_info(nullptr, nullptr, nullptr) == Q8_ERR_BAD_HANDLE);
+  CHECK(q8_step_graph_destroy(nullptr) == Q8_ERR_BAD_HANDLE);
+  int stack_word = 0;  // a pointer that is no handle: refused, never dereferenced
+  CHECK(q8_step_graph_destroy((q8_step_graph *)&stack_word) == Q8_ERR_BAD_HANDLE);
+
+  q8_decode_model md{};
+  q8_decode_buffers bf{};
+  CHECK(q8_decode_graph_build(nullptr, &bf, nullptr, nullptr, &g) == Q8_ERR_NULL);
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, nullptr) == Q8_ERR_NULL);
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, &g) == Q8_ERR_SHAPE);
+  md.n_layers = 1;
+  md.hidden = 1024;
+  md.n_heads = 16;
+  md.n_kv_heads = 8;
+  md.head_dim = 64;  // only 128 is taken
+  md.inter = 3072;
+  md.vocab = 10;
+  md.cache_rows = 64;
+  md.eps = 1e-6f;
+  md.theta = 1e6f;
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, &g) == Q8_ERR_SHAPE);
+  md.head_dim = 128;
+  md.n_heads = 40;  // 5 query heads per key/value head
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, &g) == Q8_ERR_SHAPE);
+  md.n_heads = 16;
+  md.eps = -1.f;
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, &g) == Q8_ERR_SHAPE);
+  md.eps = 1e-6f;
+  CHECK(q8_decode_graph_build(&md, &bf, nullptr, nullptr, &g) == Q8_ERR_NULL);  // no layers
+}
+
+// Walks every workgroup's tiles of a plan one by one and checks the plan.
+static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int group_size,
+                       bool i8x) {
+  q8::StepPlan plan;
+  const int st = q8::plan_step(descs.data(), (int32_t)descs.size(), m, 0, group_size, plan, i8x);
+  CHECK(st == Q8_OK);
+  if (st != Q8_OK) return;
+  // descriptors: consecutive tile ranges covering every row
+  int64_t ntiles = 0;
+  for (size_t i = 0; i < descs.size(); i++) {
+    const q8::StepDesc &t = plan.descs[i];
+    CHECK(t.tile_begin == ntiles);
+    CHECK(t.rows_per_tile >= 1);
+    const int64_t tiles = ((int64_t)descs[i].p + t.rows_per_tile - 1) / t.rows_per_tile;
+    CHECK(t.tile_end == t.tile_begin + tiles);
+    ntiles += tiles;
+  }
+  CHECK(plan.grid >= 1 && plan.grid <= ntiles);
+  // groups: contiguous ranges that partition [0, ntiles); each workgroup's
+  // tiles t0 + slot, + size, ... cover its group's range exactly once
+  std::vector<int> owner(ntiles, -1);
+  int32_t prev = 0;
+  int wgs = 0;
+  for (const q8::WgGroup &gr : plan.groups) {
+    CHECK(gr.t0 == prev && gr.t1 >= gr.t0 && gr.first == wgs);
+    CHECK(gr.size >= 1 && gr.size <= plan.group_size);
+    CHECK(gr.d0 >= 0 && gr.d0 < (int32_t)descs.size());
+    CHECK(plan.descs[gr.d0].tile_begin <= gr.t0);
+    prev = gr.t1;
+    wgs += gr.size;
+    for (int j = 0; j < gr.size; j++)
+      for (int64_t t = gr.t0 + q8::group_slot(j, gr.first, gr.size); t < gr.t1; t += gr.size) {
+        CHECK(owner[t] == -1);
+        owner[t] = gr.first + j;
+      }
+  }
+  CHECK(prev == ntiles && wgs == plan.grid);
+  for (int64_t t = 0; t < ntiles; t++) CHECK(owner[t] >= 0);
+  // argmax arrivals per team: the workgroups that hold a tile of the matvec
+  size_t a = 0;
+  for (size_t i = 0; i < descs.size(); i++) {
+    if (!descs[i].idx) continue;
+    CHECK(a < plan.expected.size());
+    if (a >= plan.expected.size()) return;
+    std::vector<uint32_t> team(q8::kArgmaxTeams, 0);
+    std::vector<char> seen(plan.grid, 0);
+    for (int64_t t = plan.descs[i].tile_begin; t < plan.descs[i].tile_end; t++)
+      if (!seen[owner[t]]) {
+        seen[owner[t]] = 1;
+        team[owner[t] % q8::kArgmaxTeams]++;
+      }
+    CHECK(plan.expected[a] == team);
+    a++;
+  }
+  CHECK(a == plan.expected.size());
+}
+
+static void planner() {
+  int32_t idx[8];
+  auto mv = [&](int n, int p, bool argmax) {
+    return q8_matvec_desc{W, X, Y, argmax ? idx : nullptr, n, p};
+  };
+  // the decode step's 197 matvecs, m = 1, 8 and 32
+  std::vector<q8_matvec_desc> step;
+  const int shapes[7][2] = {{1024, 2048}, {1024, 1024}, {1024, 1024}, {2048, 1024},
+                            {1024, 3072}, {1024, 3072}, {3072, 1024}};
+  for (int l = 0; l < 28; l++)
+    for (auto &s : shapes) step.push_back(mv(s[0], s[1], false));
+  step.push_back(mv(1024, 151936, true));
+  for (int m : {1, 8, 32}) check_plan(step, m, m == 1 ? q8::kStepGroupSize : 1, false);
+  check_plan(step, 1, q8::kStepGroupSize, true);
+  check_plan(step, 4, 1, true);
+  // ragged and empty descriptors, several argmax descriptors, odd widths
+  std::vector<q8_matvec_desc> mixed = {mv(96, 0, false),  mv(256, 5, true), mv(160, 77, false),
+                                       mv(1024, 1, true), mv(96, 0, false), mv(3072, 4099, true),
+                                       mv(32, 3, false),  mv(2048, 17, true)};
+  for (int gs : {1, 3, 8, 64}) check_plan(mixed, 1, gs, false);
+  check_plan(mixed, 2, 1, false);
+  // a few tiles only (the decode step's levels): heights halve to fill workgroups
+  check_plan({mv(2048, 1024, false)}, 1, q8::kStepGroupSize, false);
+  check_plan({mv(1024, 2048, false), mv(1024, 1024, false), mv(1024, 1024, false)}, 1,
+             q8::kStepGroupSize, false);
+  check_plan({mv(256, 1, true)}, 1, q8::kStepGroupSize, false);
+}
+
+int main() {
+  refusals();
+  planner();
+  if (g_fail) {
+    std::fprintf(stderr, "%d check(s) failed\n", g_fail);
+    return 1;
+  }
+  std::printf("sanitize_driver: all checks passed\n");
+  return 0;
+}
