@@ -48,6 +48,17 @@
  *     stream is capturing a graph: it is refused with Q8_ERR_GRAPH.  At most
  *     256 streams per device get a workspace (Q8_ERR_COUNT beyond); each is
  *     kept until the process ends.
+ *   - Split-K: q8_matvec, q8_matvec_batched and q8_matvec_argmax with one
+ *     activation row (m = 1) and a width n above 3072 that is a multiple of
+ *     256 cut W's columns into slices of at most 3072 (ceil(n / 3072)
+ *     slices of equal width in multiples of 256, the last one narrower),
+ *     compute each slice's partial sums, then add them in slice order (the
+ *     rvllm page's K-split, "The matmul pain story").  The partial sums live
+ *     in the stream's workspace, (slices * p) floats, allocated or grown by
+ *     the call that needs more (after the stream's earlier work is done);
+ *     such a call is refused with Q8_ERR_GRAPH while the stream is
+ *     capturing.  Results are deterministic (fixed slice order) and within
+ *     the same bound as any other summation order.
  */
 #ifndef Q8DEC_H
 #define Q8DEC_H

@@ -39,13 +39,17 @@ int hip_fail(hipError_t e) {
 
 constexpr int kMaxDevices = 64;
 
-// The standalone argmax calls keep one workspace (an ArgmaxSlot) per stream
-// they run on, so calls on different streams never share one; calls on one
-// stream are ordered by it.  At most kMaxStreamSlots streams per device.
+// The standalone calls keep one workspace per stream they run on: an
+// ArgmaxSlot for the argmax entry points, and the split-K partial sums of
+// the matvecs wider than the staged path (grown as needed).  Calls on
+// different streams never share one; calls on one stream are ordered by it.
+// At most kMaxStreamSlots streams per device.
 constexpr int kMaxStreamSlots = 256;
 struct StreamSlot {
   hipStream_t stream;
   q8::ArgmaxSlot *slot;
+  float *part = nullptr;
+  size_t part_floats = 0;
 };
 
 struct DeviceState {
@@ -184,6 +188,54 @@ int stream_slot(int dev, hipStream_t stream, q8::ArgmaxSlot **out) {
   ds.slots.push_back(StreamSlot{stream, slot});
   *out = slot;
   return Q8_OK;
+}
+
+// The split-K partial-sum buffer of `stream` on device dev (after
+// stream_slot), at least `floats` long.  Growing it waits for the stream's
+// work (the old buffer may still be read), and is refused with Q8_ERR_GRAPH
+// while the stream is capturing.  Every partial is written before it is
+// read, so the buffer needs no clearing.
+int stream_part(int dev, hipStream_t stream, size_t floats, float **out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (StreamSlot &s : g_dev[dev].slots) {
+    if (s.stream != stream) continue;
+    if (s.part_floats < floats) {
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      hipError_t e = hipStreamIsCapturing(stream, &cap);
+      if (e != hipSuccess) return hip_fail(e);
+      if (cap != hipStreamCaptureStatusNone) return Q8_ERR_GRAPH;
+      if (s.part) {
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e);
+        (void)hipFree(s.part);
+        s.part = nullptr;
+        s.part_floats = 0;
+      }
+      void *p = nullptr;
+      if ((e = hipMalloc(&p, floats * sizeof(float))) != hipSuccess) return hip_fail(e);
+      s.part = (float *)p;
+      s.part_floats = floats;
+    }
+    *out = s.part;
+    return Q8_OK;
+  }
+  return Q8_ERR_HIP;  // stream_slot was not called for this stream
+}
+
+// One activation row of a matrix wider than the staged path: split-K over
+// the stream's partial-sum buffer (y and/or the argmax).
+int matvec_split(const void *w, const float *x, float *y, int32_t *idx, int32_t n,
+                 int32_t p, hipStream_t stream) {
+  int dev = 0;
+  int st = ensure_device(&dev);
+  if (st) return st;
+  q8::ArgmaxSlot *slot = nullptr;
+  if ((st = stream_slot(dev, stream, &slot))) return st;
+  float *part = nullptr;
+  if ((st = stream_part(dev, stream, (size_t)q8::split_slices(n, nullptr) * (size_t)p, &part)))
+    return st;
+  hipError_t e = q8::launch_matvec_split((const uint8_t *)w, x, y, n, p, part,
+                                         idx ? slot : nullptr, idx, stream);
+  return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
 // ---- argument checks (no HIP calls) -----------------------------------
@@ -465,6 +517,8 @@ int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
               void *stream) {
   int st = check_matvec(w, x, y, nullptr, 1, n, p, true);
   if (st) return st;
+  if (p > 0 && q8::split_shape_ok(1, n))
+    return matvec_split(w, x, y, nullptr, n, p, (hipStream_t)stream);
   if ((st = ensure_device(nullptr))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, 1, n, p, nullptr,
                                    nullptr, (hipStream_t)stream);
@@ -475,6 +529,8 @@ int q8_matvec_batched(const void *w, const float *x, float *y, int32_t m,
                       int32_t n, int32_t p, void *stream) {
   int st = check_matvec(w, x, y, nullptr, m, n, p, true);
   if (st) return st;
+  if (p > 0 && q8::split_shape_ok(m, n))
+    return matvec_split(w, x, y, nullptr, n, p, (hipStream_t)stream);
   if ((st = ensure_device(nullptr))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, m, n, p, nullptr,
                                    nullptr, (hipStream_t)stream);
@@ -501,6 +557,8 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
   if (!idx) return Q8_ERR_NULL;
   int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
   if (st) return st;
+  if (q8::split_shape_ok(m, n))
+    return matvec_split(w, x, y_or_null, idx, n, p, (hipStream_t)stream);
   int dev = 0;
   if ((st = ensure_device(&dev))) return st;
   q8::ArgmaxSlot *slot = nullptr;

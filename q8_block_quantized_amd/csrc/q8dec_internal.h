@@ -65,6 +65,13 @@ struct StepDesc {
 // y is stored with device-scope stores, so that the launch's epilogue (m = 1)
 // can read it (see Epilogue); otherwise y takes plain stores.
 constexpr int32_t kDescDeviceOut = 1;
+// A descriptor may cover a column slice of a wider matrix (split-K): w then
+// points at the slice's first block of row 0, n is the slice's width, and
+// flags bits 8..23 hold the matrix's row pitch in 16-byte units.
+constexpr int kDescPitchShift = 8;
+__host__ __device__ inline int32_t desc_pitch16(int32_t flags) {
+  return (flags >> kDescPitchShift) & 0xFFFF;
+}
 static_assert(sizeof(StepDesc) == 64, "descriptor layout");
 
 // Workgroups g in [first, first + size) of a persistent step share the
@@ -97,6 +104,18 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 // Widths the int8-activation variant takes: the staged ones (n/32 a
 // multiple of 8, n <= 3072).
 bool i8x_shape_ok(int n);
+
+// Split-K for one activation row of a matrix wider than the staged path
+// takes (n > 3072, n a multiple of 256): the columns are cut into
+// split_slices(n) slices of sb blocks (a multiple of 8, at most 96; the
+// last one narrower), each slice's tiles staged, each slice's partial sums
+// written to part + i * p (part: split_slices(n) * p floats of device
+// memory), then added in slice order into y (when set) and, when idx is set,
+// the argmax taken over the sums.  Two launches on s.
+bool split_shape_ok(int m, int n);
+int split_slices(int n, int32_t *sb);
+hipError_t launch_matvec_split(const uint8_t *w, const float *x, float *y, int n, int p,
+                               float *part, ArgmaxSlot *slot, int32_t *idx, hipStream_t s);
 
 // Widths a wide batch (8 < m <= 32) takes: n a positive multiple of 256.
 bool wide_shape_ok(int n);

@@ -970,6 +970,27 @@ struct Prefetch {
       *(u32x4 *)((uint8_t *)tl + off) = w[j];
     }
   }
+  // `bytes` bytes of whole rows of `rb` bytes each (a multiple of 16) that
+  // lie `pitch` bytes apart in memory (a column slice of a wider matrix),
+  // packed in the registers as load_w packs contiguous rows.
+  __device__ __forceinline__ void load_w_strided(const uint8_t *base, int32_t bytes,
+                                                 int32_t rb, int32_t pitch) {
+    const __attribute__((address_space(1))) uint8_t *b = gp(base);
+    const int32_t cpr = rb >> 4;  // chunks per row
+    // chunk c of row c / cpr: c < 2^12 and c / cpr is at least 1 / (2 cpr)
+    // from an integer, far above the rounding of the product
+    const float rcp = 1.0f / (float)cpr;
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
+      off = off < bytes - 16 ? off : bytes - 16;
+      const int32_t c = off >> 4;
+      const int32_t row = (int32_t)(((float)c + 0.5f) * rcp);
+      w[j] = __builtin_nontemporal_load(
+          (const __attribute__((address_space(1))) u32x4 *)(b + (int64_t)row * pitch +
+                                                            16 * (c - row * cpr)));
+    }
+  }
   // Same, with kMfmaRowPad bytes after every row of `pitch` bytes (a
   // multiple of 16, so no chunk straddles two rows).
   __device__ __forceinline__ void store_w_rows(uint32_t *tl, int32_t bytes,
@@ -1041,6 +1062,32 @@ struct OneSrc {
   StepDesc d;
   __device__ __forceinline__ int32_t find(int32_t, int32_t) const { return 0; }
   __device__ __forceinline__ StepDesc get(int32_t) const { return d; }
+};
+
+// One matvec cut into column slices (split-K, m = 1): slice i covers
+// blocks [i * sb, min((i + 1) * sb, bpr)) of every row, owns tiles
+// [i * tps, (i + 1) * tps) (the same row tiles in every slice) and writes its
+// partial sums to part + i * p.  Its descriptor is derived, not stored.
+struct SliceSrc {
+  StepDesc base;   // the whole matvec; rows_per_tile is a slice's
+  float *part;
+  int32_t slices, sb, tps, pitch16;
+  __device__ __forceinline__ int32_t find(int32_t t, int32_t) const { return t / tps; }
+  __device__ __forceinline__ StepDesc get(int32_t i) const {
+    StepDesc d = base;
+    const int32_t b0 = i * sb, bpr = base.n >> 5;
+    const int32_t nb = bpr - b0 < sb ? bpr - b0 : sb;
+    d.w = base.w + (int64_t)b0 * 34;
+    d.x = base.x + (int64_t)b0 * 32;
+    d.n = nb * 32;
+    d.y = part + (int64_t)i * base.p;
+    d.idx = nullptr;
+    d.slot = nullptr;
+    d.tile_begin = i * tps;
+    d.tile_end = d.tile_begin + tps;
+    d.flags = pitch16 << kDescPitchShift;
+    return d;
+  }
 };
 
 struct TableSrc {
@@ -1197,7 +1244,8 @@ __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
 // known at compile time (a standalone staged matvec), so the kernel holds
 // one copy of the row loop instead of one per width and output mode.
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
-template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src>
+template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src,
+          bool STRIDED = false>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr) {
@@ -1235,9 +1283,16 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   if constexpr (DEC) {
     if (pro) pro_load(pro, prr);  // before the tile's loads: see pro_load
   }
-  if (staged(cur) || mfma(cur))
-    pf.load_w(cur.d.w + (uint64_t)cur.r0 * (cur.d.n >> 5) * 34u,
-              cur.rows * (cur.d.n >> 5) * 34);
+  // a tile's weight bytes: whole rows, or (STRIDED) rows of a column slice
+  auto load_tile = [&](const Job &j) {
+    const int32_t rb = (j.d.n >> 5) * 34;
+    if (STRIDED)
+      pf.load_w_strided(j.d.w + (uint64_t)j.r0 * desc_pitch16(j.d.flags) * 16u, j.rows * rb, rb,
+                        desc_pitch16(j.d.flags) * 16);
+    else
+      pf.load_w(j.d.w + (uint64_t)j.r0 * rb, j.rows * rb);
+  };
+  if (staged(cur) || mfma(cur)) load_tile(cur);
   // the x staged in LDS (and the batched path's operand A): matvecs that
   // share x (the same pointer and width) are staged once
   const float *xptr = nullptr, *xaptr = nullptr;
@@ -1290,9 +1345,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       // streamed bytes, so its latency overlaps theirs rather than following
       if (x_in_lds(nxt) && (nxt.d.x != xptr || nxt.d.n != xn))
         pf.load_x(nxt.d.x, m * nxt.d.n);
-      if (staged(nxt) || mfma(nxt))
-        pf.load_w(nxt.d.w + (uint64_t)nxt.r0 * (nxt.d.n >> 5) * 34u,
-                  nxt.rows * (nxt.d.n >> 5) * 34);
+      if (staged(nxt) || mfma(nxt)) load_tile(nxt);
     }
     // The job two tiles ahead.  A new matvec's descriptor is read from the
     // table here, so its scalar loads complete while this tile is computed:
@@ -1645,6 +1698,37 @@ mv_kernel(StepDesc d, int32_t m) {
                                                      lds);
 }
 
+// One matvec at m = 1 cut into column slices (SliceSrc), each slice's tiles
+// staged like mv_kernel's; the partial sums go to the slices' vectors and
+// reduce_slices adds them.
+template <int NBLS>
+__global__ void __launch_bounds__(kWG, 1) mv_split_kernel(SliceSrc src) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int32_t b = (int32_t)blockIdx.x, b0 = b & ~31;
+  const int32_t first = b0 + 32 <= (int32_t)gridDim.x ? b0 + group_slot(b & 31, 0, 32) : b;
+  run_tiles<true, false, false, true, NBLS, false, SliceSrc, true>(
+      src, first, src.slices * src.tps, gridDim.x, 0, 1, lds);
+}
+
+// y[e] = part[e] + part[p + e] + ... (slices in order, one row), and the
+// argmax of y when idx is set (every workgroup arrives once).
+__global__ void __launch_bounds__(kWG)
+reduce_slices(const float *__restrict__ part, int32_t slices, int32_t p, float *__restrict__ y,
+              ArgmaxSlot *__restrict__ slot, int32_t *__restrict__ idx) {
+  unsigned long long key = 0ull;
+  for (int32_t e = blockIdx.x * kWG + threadIdx.x; e < p; e += gridDim.x * kWG) {
+    float v = gp(part)[e];
+    for (int32_t i = 1; i < slices; i++) v += gp(part)[(int64_t)i * p + e];
+    if (y) gpw(y)[e] = v;
+    key = umax64(key, argmax_key(v, (uint32_t)e));
+  }
+  if (!idx) return;
+  __shared__ unsigned long long lk[kWaves][1];
+  key = wave_max64(key);
+  if ((threadIdx.x & 63) == 0) lk[threadIdx.x >> 6][0] = key;
+  argmax_arrive(lk, 1, slot, idx, blockIdx.x, gridDim.x);
+}
+
 // The persistent step: every tile of every descriptor of a device-side
 // table (count entries in tile order), with no ordering between
 // descriptors.  Workgroups form groups; a group interleaves its contiguous
@@ -1932,6 +2016,72 @@ hipError_t launch_argmax(const float *logits, int m, int p, ArgmaxSlot *slot,
   int gx = (int)(per < 1 ? 1 : (per > 512 ? 512 : per));
   hipLaunchKernelGGL(argmax_rows, dim3(gx, m), dim3(kWG), 0, s, logits, m, p,
                      slot, idx);
+  return hipGetLastError();
+}
+
+bool split_shape_ok(int m, int n) {
+  return m == 1 && n > kMaxLdsBlocks * 32 && n % 256 == 0;
+}
+
+int split_slices(int n, int32_t *sb) {
+  const int32_t bpr = n >> 5;
+  int32_t s = (bpr + kMaxLdsBlocks - 1) / kMaxLdsBlocks;  // slices of at most 96 blocks
+  int32_t b = (bpr + s - 1) / s;
+  b = (b + 7) & ~7;  // a multiple of 8 blocks: 16-byte aligned slices, staged widths
+  s = (bpr + b - 1) / b;
+  if (sb) *sb = b;
+  return s;
+}
+
+namespace {
+template <int NBLS>
+int split_grid_cap(int dev) {
+  static int cache[64] = {0};
+  int &c = cache[dev & 63];
+  if (!c)
+    c = resident_wgs(mv_split_kernel<NBLS>,
+                     kTileMaxBytes + (size_t)kMaxLdsBlocks * 36 * sizeof(float), dev);
+  return c;
+}
+}  // namespace
+
+hipError_t launch_matvec_split(const uint8_t *w, const float *x, float *y, int n, int p,
+                               float *part, ArgmaxSlot *slot, int32_t *idx, hipStream_t s) {
+  if (p <= 0 || !split_shape_ok(1, n)) return hipErrorInvalidValue;
+  int32_t sb = 0;
+  const int32_t slices = split_slices(n, &sb);
+  SliceSrc src{};
+  src.base.w = w;
+  src.base.x = x;
+  src.base.n = n;
+  src.base.p = p;
+  src.part = part;
+  src.slices = slices;
+  src.sb = sb;
+  src.pitch16 = (n >> 5) * 34 / 16;
+  // rows per tile of a full-width slice, halved (down to one pass) while the
+  // launch has fewer than 512 tiles
+  int32_t rows = tile_rows_of(1, sb * 32);
+  while (rows > kRowsPerPass && slices * ((p + rows - 1) / rows) < 512) rows >>= 1;
+  src.base.rows_per_tile = rows;
+  src.tps = (p + rows - 1) / rows;
+  const int32_t tiles = slices * src.tps;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const int nbl = nbl_of(sb * 32);
+  const int cap = nbl == 1 ? split_grid_cap<1>(dev) : nbl == 2 ? split_grid_cap<2>(dev)
+                                                                : split_grid_cap<3>(dev);
+  const int grid = tiles < cap ? tiles : cap;
+  const size_t lds = lds_bytes_for(1, sb * 32);
+  if (nbl == 1) hipLaunchKernelGGL(mv_split_kernel<1>, dim3(grid), dim3(kWG), lds, s, src);
+  else if (nbl == 2) hipLaunchKernelGGL(mv_split_kernel<2>, dim3(grid), dim3(kWG), lds, s, src);
+  else hipLaunchKernelGGL(mv_split_kernel<3>, dim3(grid), dim3(kWG), lds, s, src);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the sums: about 8 outputs per thread, at most 512 workgroups
+  int64_t per = ((int64_t)p + kWG * 8 - 1) / (kWG * 8);
+  const int gx = (int)(per < 1 ? 1 : (per > 512 ? 512 : per));
+  hipLaunchKernelGGL(reduce_slices, dim3(gx), dim3(kWG), 0, s, part, slices, p, y, slot, idx);
   return hipGetLastError();
 }
 
