@@ -245,6 +245,8 @@ struct AttnArgs {
   float *kc, *vc;                // [cache_rows][n_kv*128]
   const int32_t *pos;            // device int32
   const float *rope;             // [64][2] cos, sin of pos * freq (step_start)
+  const float *freq;             // [64] the RoPE frequencies (the persistent step
+                                 // takes cos, sin of pos * freq itself), or NULL
   float *out;                    // [n_heads*128]
   float *part;                   // [n_heads][chunks][kAttnPart]
   ArgmaxSlot *arrive;            // [n_kv], zeroed (counters only)
