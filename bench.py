@@ -424,11 +424,12 @@ def cpu_parity(step_set, m_host, threads: int):
 
 
 def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
-                seed: int = 0) -> dict:
+                seed: int = 0, form: int = 0) -> dict:
     """The whole Qwen3-0.6B-shaped decode step (q8_decode_graph_build) at
-    position pos with a cache of `rows` rows: token latency of the graph
-    launch (and of its kernels launched directly), waiting on the token the
-    kernel stores into pinned memory.  Algorithmic bytes: the weights, the
+    position pos with a cache of `rows` rows, in one form (a kernel node per
+    stage, or the persistent launch): token latency of the graph launch (and
+    of its kernels launched directly), waiting on the token the kernel
+    stores into pinned memory.  Algorithmic bytes: the weights, the
     norm weights, the pos + 1 key and value rows each layer reads, and the
     activations (x, caches written: one row per layer)."""
     model = gen.decode_model(gen.QWEN3_DIMS, cache_rows=rows, seed=seed)
@@ -441,7 +442,7 @@ def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
     bufs["x_in"].copy_(torch.from_numpy(model["x_in"]))
     bufs["pos"].fill_(pos)
     host = torch.zeros(1, dtype=torch.int32).pin_memory()
-    g = q8.DecodeGraph(dims, layers, out_norm, lm_head, bufs, host_token=host)
+    g = q8.DecodeGraph(dims, layers, out_norm, lm_head, bufs, host_token=host, form=form)
     nodes = g.info()
     sec, toks = time_graph_steps(torch, [g], host, steps, warmup, poll=True)
     ksec, ktoks = time_graph_steps(torch, [_KernelLaunch(g)], host, steps, warmup, poll=True)
@@ -457,6 +458,7 @@ def decode_step(torch, q8, dev, pos: int, rows: int, steps: int, warmup: int,
     del layers, lm_head, bufs
     torch.cuda.empty_cache()
     return {
+        "form": "persistent" if form == q8.Q8_DECODE_PERSISTENT else "nodes",
         "pos": pos, "cache_rows": rows, "token": toks[-1],
         "token_latency_us": round(sec * 1e6, 2),
         "kernel_launches_token_latency_us": round(ksec * 1e6, 2),
@@ -566,7 +568,11 @@ def only_workload(args, torch, q8, dev) -> int:
             for g in chain:
                 g.close()
     elif args.only == "decode":
-        out.update(decode_step(torch, q8, dev, 1023, 4096, args.steps, args.warmup))
+        forms = {"nodes": [q8.Q8_DECODE_NODES], "persistent": [q8.Q8_DECODE_PERSISTENT],
+                 "both": [q8.Q8_DECODE_NODES, q8.Q8_DECODE_PERSISTENT]}[args.decode_form]
+        for f in forms:
+            r = decode_step(torch, q8, dev, 1023, 4096, args.steps, args.warmup, form=f)
+            out[r["form"]] = r
     elif args.only == "i8x_step":
         sets1 = [StepSet(torch, dev, 0, 1000 * j, 1, False) for j in range(2)]
         host = torch.zeros(1, dtype=torch.int32).pin_memory()
@@ -611,6 +617,8 @@ def main() -> int:
                          "read ceiling, one matvec as a 240-node chain graph, one "
                          "layer as chain and levels graphs, or the 197-node chain "
                          "step; prints one JSON line")
+    ap.add_argument("--decode-form", choices=["nodes", "persistent", "both"], default="both",
+                    help="--only decode: the decode step's form(s)")
     ap.add_argument("--trace-summary", metavar="CSV", default=None,
                     help="summarise a rocprofv3 kernel trace (csv) instead of "
                          "measuring: per-kernel durations and gaps; no GPU use")
@@ -894,9 +902,11 @@ def main() -> int:
         del sets32, p32
 
         for dpos in (1023, 4095):
-            log(f"whole decode step (norms, attention, SwiGLU; 142 nodes), pos {dpos}")
-            extra[f"decode_step_pos{dpos}"] = decode_step(torch, q8, dev, dpos, 4096,
-                                                           steps2, 3)
+            for form, tag in ((q8.Q8_DECODE_NODES, ""), (q8.Q8_DECODE_PERSISTENT, "_persistent")):
+                log(f"whole decode step (norms, attention, SwiGLU), "
+                    f"{'one persistent launch' if tag else '142 nodes'}, pos {dpos}")
+                extra[f"decode_step_pos{dpos}{tag}"] = decode_step(
+                    torch, q8, dev, dpos, 4096, steps2, 3, form=form)
     if extra:
         result["extra"] = extra
 

@@ -280,24 +280,26 @@ int q8_step_graph_destroy(q8_step_graph *g);
  * lm_head and argmax_row ("Eight kernels" defines each operation).  The
  * pages encode 18 dispatches per layer; here a layer is 5 kernel nodes: the
  * q/k/v matvecs; the attention with the QK-norm, RoPE and append folded in;
- * o; gate/up; down.  Before the first layer one node copies x_in into the
- * residual stream and norms it; after the last the fused lm_head argmax
- * runs: 5 * n_layers + 2 nodes.  The element-wise work between matvecs (the
+ * o; gate/up; down.  Before the first layer one node computes the RoPE
+ * rotation of position pos; after the last the fused lm_head argmax runs:
+ * 5 * n_layers + 2 nodes.  The element-wise work between matvecs (the
  * residual adds, the norms, SwiGLU) runs in one of two places:
  *   - prologue form, taken when every matvec width is a multiple of 256 up
  *     to 3072 and hidden, inter <= 3072 (Qwen3-0.6B's shapes): every
  *     workgroup of the launch that consumes the vector computes it into its
  *     staged x while its first weight tile loads, and workgroup 0 stores it
- *     (gate/up: xn2 = norm(R + attn_out); down: h = silu(gate) * up; the
- *     next layer's q/k/v, or the lm_head: R' = (R + attn_out) + ffn_out and
- *     its norm).  The residual stream alternates between buf->x and a
+ *     (the first q/k/v: R = x_in and xn = norm(x_in); gate/up: xn2 =
+ *     norm(R + attn_out); down: h = silu(gate) * up; the next layer's q/k/v,
+ *     or the lm_head: R' = (R + attn_out) + ffn_out and its norm).  The residual stream alternates between buf->x and a
  *     workspace buffer from layer to layer, and after the last layer it is
  *     in buf->x;
- *   - epilogue form, for every other shape: the last workgroup of the
- *     launch that produces the vector computes it once every output of that
- *     launch is stored (o: x += attn_out and xn2; gate/up: h; down:
- *     x += ffn_out and the next norm); the residual stream stays in buf->x.
- * Both forms give the same values (the adds run in the pages' order).
+ *   - epilogue form, for every other shape: the first node also copies
+ *     x_in into buf->x and norms it, and the last workgroup of the launch
+ *     that produces a vector computes it once every output of that launch
+ *     is stored (o: x += attn_out and xn2; gate/up: h; down: x += ffn_out
+ *     and the next norm); the residual stream stays in buf->x.
+ * The residual adds run in the pages' order in both; a norm's sum of squares
+ * is added in another order in each (results within the same bound).
  * Everything is binary32. */
 
 #define Q8_GRAPH_DECODE 4  /* mode of graphs from q8_decode_graph_build */
@@ -316,14 +318,28 @@ typedef struct {
 /* The model: shapes (1 <= n_layers <= 512; head_dim must be 128; n_heads a
  * multiple of n_kv_heads, at most 4 query heads per key/value head;
  * hidden <= 4096; hidden, inter multiples of 32; 1 <= cache_rows <= 65536;
- * eps >= 0 and theta > 0, finite), a HOST array of n_layers layers, and the
- * final norm and lm_head (device). */
+ * eps >= 0 and theta > 0, finite), a HOST array of n_layers layers, the
+ * final norm and lm_head (device), and the form of the recorded step:
+ *   Q8_DECODE_NODES (0): 5 kernel nodes per layer + 2, as described above;
+ *   Q8_DECODE_PERSISTENT (1): one kernel node that runs every phase (per
+ *     layer q/k/v, attention, o, gate/up, down; then the lm_head) with all
+ *     of its workgroups resident, meeting at a grid-wide barrier between
+ *     phases; each workgroup requests its next phase's first weight tile
+ *     (or cached rows) before it waits.  Takes the prologue form's shapes
+ *     only (hidden, the query width and inter multiples of 256, at most
+ *     3072; else Q8_ERR_SHAPE).  The launch must have the device to itself
+ *     (all workgroups resident at once): a wait at the barrier that runs
+ *     past 200 ms (another workgroup never arrived) ends the step with the
+ *     token -2, after which the graph must be destroyed and built again. */
+#define Q8_DECODE_NODES 0
+#define Q8_DECODE_PERSISTENT 1
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, cache_rows;
   float eps, theta;
   const q8_decode_layer *layers;
   const float *out_norm;                /* float32 [hidden] */
   const void *lm_head;                  /* Q8_0 [vocab][hidden/32 blocks] */
+  int32_t form;                         /* Q8_DECODE_NODES or Q8_DECODE_PERSISTENT */
 } q8_decode_model;
 
 /* The step's activations: device buffers owned by the caller, each sized

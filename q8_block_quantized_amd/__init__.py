@@ -25,6 +25,8 @@ Q8_GRAPH_PERSISTENT = 1
 Q8_GRAPH_PERSISTENT_I8X = 2
 Q8_GRAPH_LEVELS = 3
 Q8_GRAPH_DECODE = 4
+Q8_DECODE_NODES = 0
+Q8_DECODE_PERSISTENT = 1
 BLOCK = 32
 BLOCK_BYTES = 34
 
@@ -63,7 +65,7 @@ class DecodeModel(ctypes.Structure):
                  "vocab", "cache_rows")] + [
                 ("eps", ctypes.c_float), ("theta", ctypes.c_float),
                 ("layers", ctypes.c_void_p), ("out_norm", ctypes.c_void_p),
-                ("lm_head", ctypes.c_void_p)]
+                ("lm_head", ctypes.c_void_p), ("form", ctypes.c_int32)]
 
 
 class DecodeBuffers(ctypes.Structure):
@@ -416,11 +418,13 @@ class DecodeGraph(StepGraph):
     of LAYER_FIELDS (uint8 Q8_0 weights, float32 norms and caches).
     ``bufs``: the tensors of BUFFER_FIELDS (decode_buffers makes them;
     logits may be None).  Every tensor must stay alive while the graph
-    exists; this object keeps references to them.
+    exists; this object keeps references to them.  ``form``:
+    Q8_DECODE_NODES (a kernel node per stage) or Q8_DECODE_PERSISTENT (one
+    launch with a grid-wide barrier between phases).
     """
 
     def __init__(self, dims: dict, layers, out_norm, lm_head, bufs: dict,
-                 host_token=None, device=None):
+                 host_token=None, device=None, form=None):
         torch = _torch()
         dev = device if device is not None else bufs["x"].device
         H, hd = int(dims["hidden"]), int(dims["head_dim"])
@@ -466,12 +470,14 @@ class DecodeGraph(StepGraph):
         model = DecodeModel(int(dims["n_layers"]), H, int(dims["n_heads"]),
                             int(dims["n_kv_heads"]), hd, inter, int(dims["vocab"]), rows,
                             float(dims["eps"]), float(dims["theta"]),
-                            ctypes.addressof(arr), out_norm.data_ptr(), lm_head.data_ptr())
+                            ctypes.addressof(arr), out_norm.data_ptr(), lm_head.data_ptr(),
+                            Q8_DECODE_NODES if form is None else int(form))
         cb = DecodeBuffers(*bvals)
         self._keep += [arr, model, cb]
         self.host_idx = host_token
         self.m = 1
         self.mode = Q8_GRAPH_DECODE
+        self.form = Q8_DECODE_NODES if form is None else int(form)
         self.dims = dict(dims)
         handle = ctypes.c_void_p(None)
         hptr = host_token.data_ptr() if host_token is not None else None

@@ -27,6 +27,10 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # no packed FP32 (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a multiply and an add fuse only where one expression holds both (or
+    # fmaf says so): the rounding then follows the source alone, and two
+    # kernels that share a routine compute bit-identical values with it
+    "-ffp-contract=on",
     "-fno-gpu-rdc", "-Wall",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -267,8 +268,9 @@ constexpr uint32_t kGraphMagic = 0x51384447u;  // "Q8DG"
 
 // One persistent kernel launch of a step: the descriptor table and
 // workgroup ranges of its descriptors (device memory) and its shape.
-// Decode graphs add attention and norm nodes (kind).
-constexpr int kStepNode = 0, kAttnNode = 1, kNormNode = 2;
+// Decode graphs add attention and norm nodes (kind), or hold the one
+// launch of the persistent decode step (kDecodeNode).
+constexpr int kStepNode = 0, kAttnNode = 1, kNormNode = 2, kDecodeNode = 3;
 struct SegmentLaunch {
   const q8::StepDesc *table;
   const q8::WgGroup *groups;
@@ -287,10 +289,17 @@ struct SegmentLaunch {
   const int32_t *npos = nullptr;  // kNormNode: the position, the RoPE frequencies
   const float *nfreq = nullptr;   // and the cos/sin table it writes
   float *rope_out = nullptr;
+  const q8::DecPhase *phases = nullptr;  // kDecodeNode: the phase table,
+  int32_t nphases = 0;                   // the barrier and the query heads
+  q8::GridBarrier *bar = nullptr;        // per key/value head
+  int32_t heads_per_kv = 0;
 };
 
 hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
   if (L.kind == kAttnNode) return q8::launch_attention(L.attn, s);
+  if (L.kind == kDecodeNode)
+    return q8::launch_decode_persistent(L.phases, L.nphases, L.bar, L.grid, L.lds,
+                                        L.heads_per_kv, s);
   if (L.kind == kNormNode)
     return q8::launch_step_start(L.nx, L.nw, L.nout, L.ncopy, L.ndim, L.neps, L.npos,
                                  L.nfreq, L.rope_out, s);
@@ -307,6 +316,7 @@ struct q8_step_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;
   void *workspace;  // argmax slots, then each segment's table and ranges
+  void *act;        // decode graphs: activation buffers of the step's own
   int32_t m;
   bool i8x;
   // persistent modes: the recorded kernel launches in order, for
@@ -327,6 +337,7 @@ void release_graph(q8_step_graph *g) {
   if (g->exec) (void)hipGraphExecDestroy(g->exec);
   if (g->graph) (void)hipGraphDestroy(g->graph);
   if (g->workspace) (void)hipFree(g->workspace);
+  if (g->act) (void)hipFree(g->act);
   g->magic = 0;
   delete g;
 }
@@ -362,7 +373,7 @@ namespace q8 {
 // workgroups with contiguous tile ranges of about equal weight bytes, and
 // for every argmax descriptor the arrivals each argmax team waits for.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan, bool i8x, bool dec) {
+              int group_size, StepPlan &plan, bool i8x, bool dec, int grid_cap) {
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
   plan.i8x = i8x;
@@ -388,10 +399,37 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     plan.all_staged = plan.all_staged && step_all_staged(m, d.n, i8x);
   }
   if (tiles < 1) return Q8_ERR_SHAPE;  // nothing to run
-  // A launch of few tiles (the decode step's levels) spreads them over more
-  // workgroups: staged m = 1 tile heights above one pass (8 rows) halve
-  // until there are at least kStepMinTiles (as standalone matvecs do).
-  if (m == 1 && !i8x && plan.all_staged) {
+  if (grid_cap > 0 && m == 1 && !i8x && plan.all_staged) {
+    // The persistent decode step's phases: the least tile height h that
+    // leaves at most one tile per workgroup of the grid (each phase then
+    // costs one tile's latency), or the staged maximum where that is lower.
+    int64_t rows = 0, hmax = 1;
+    for (int32_t i = 0; i < count; i++) {
+      rows += descs[i].p;
+      hmax = plan.descs[i].rows_per_tile > hmax ? plan.descs[i].rows_per_tile : hmax;
+    }
+    int64_t h = (rows + grid_cap - 1) / grid_cap;
+    if (h < 1) h = 1;
+    for (;; h++) {
+      int64_t nt = 0;
+      for (int32_t i = 0; i < count; i++) {
+        const int64_t r = h < plan.descs[i].rows_per_tile ? h : plan.descs[i].rows_per_tile;
+        nt += (descs[i].p + r - 1) / r;
+      }
+      if (nt <= grid_cap || h >= hmax) break;
+    }
+    tiles = 0;
+    for (int32_t i = 0; i < count; i++) {
+      StepDesc &t = plan.descs[i];
+      if (h < t.rows_per_tile) t.rows_per_tile = (int32_t)h;
+      t.tile_begin = (int32_t)tiles;
+      tiles += (t.p + t.rows_per_tile - 1) / t.rows_per_tile;
+      t.tile_end = (int32_t)tiles;
+    }
+  } else if (m == 1 && !i8x && plan.all_staged) {
+    // A launch of few tiles (the decode step's levels) spreads them over more
+    // workgroups: staged m = 1 tile heights above one pass (8 rows) halve
+    // until there are at least kStepMinTiles (as standalone matvecs do).
     while (tiles < kStepMinTiles) {
       bool changed = false;
       tiles = 0;
@@ -411,7 +449,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   const int32_t ntiles = (int32_t)tiles;
   plan.lds = widest;
   if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;
-  int grid = step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
+  int grid = grid_cap > 0 ? grid_cap : step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
   if (group_size < 1) group_size = 1;
@@ -819,9 +857,23 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
 
 bool ok16(const void *p) { return p && aligned(p, 16); }
 
+// Device memory freed on scope exit unless released.
+struct DevBuf {
+  void *p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+  void *release() {
+    void *r = p;
+    p = nullptr;
+    return r;
+  }
+};
+
 // The whole decode step: argument checks, then the plans, the workspace and
 // the node list (norm; per layer q/k/v, attention, o + add + norm, gate/up +
-// SwiGLU, down + add + norm; lm_head argmax), then the capture.
+// SwiGLU, down + add + norm; lm_head argmax), or the phase table of the
+// persistent form, then the capture.
 int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t *host_token,
                  q8_step_graph **out) {
   if (!out) return Q8_ERR_NULL;
@@ -861,6 +913,9 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     }
   }
   if (host_token && !aligned(host_token, 4)) return Q8_ERR_ALIGN;
+  if (M.form != Q8_DECODE_NODES && M.form != Q8_DECODE_PERSISTENT) return Q8_ERR_MODE;
+  const bool pers = M.form == Q8_DECODE_PERSISTENT;
+  const int G = M.n_heads / M.n_kv_heads;
   int dev = 0;
   int st = ensure_device(&dev);
   if (st) return st;
@@ -870,8 +925,60 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
   }
 
-  // the matvec levels: per layer q/k/v (0), o (1), gate/up (2), down (3); then the lm_head
   const int H = M.hidden, QW = (int)qw, KVW = (int)kvw, I = M.inter;
+  // Activation buffers.  The node form uses the caller's for every layer
+  // (kernel boundaries order each write before the next read), with the
+  // residual stream after layer l, R_l, alternating between buf->x and a
+  // buffer of its own so that a launch never overwrites what its own
+  // workgroups read: R_l lives in buf->x when L - 1 - l is even (l = -1, the
+  // step's input, is copied there by the first launch), so the last is in
+  // buf->x.  The persistent form gives layers 0 .. L-2 their own buffers and
+  // R_{-1} .. R_{L-2} one each (the last layer and R_{L-1} use the caller's),
+  // so that the launch writes every buffer once (see decode_kernel).
+  struct LayerBufs {
+    float *xn, *q, *k, *v, *attn, *attn_out, *xn2, *gate, *up, *h, *ffn_out;
+  };
+  std::vector<LayerBufs> lb(M.n_layers, LayerBufs{B.xn, B.q, B.k, B.v, B.attn, B.attn_out,
+                                                  B.xn2, B.gate, B.up, B.h, B.ffn_out});
+  std::vector<float *> rs(M.n_layers + 1, B.x);  // rs[l + 1] = R_l
+  DevBuf act;
+  {
+    auto fl = [](int64_t n) { return (size_t)((n + 63) & ~(int64_t)63); };  // 256-byte pieces
+    const size_t per_layer = 4 * fl(H) + 2 * fl(QW) + 2 * fl(KVW) + 3 * fl(I);
+    const size_t floats = pers ? (size_t)(M.n_layers - 1) * per_layer + (size_t)M.n_layers * fl(H)
+                               : fl(H);
+    hipError_t e = hipMalloc(&act.p, floats * sizeof(float));
+    if (e != hipSuccess) return hip_fail(e);
+    float *f = (float *)act.p;
+    auto take_f = [&](int64_t n) {
+      float *r = f;
+      f += fl(n);
+      return r;
+    };
+    if (pers) {
+      for (int32_t l = 0; l + 1 < M.n_layers; l++) {
+        LayerBufs &b = lb[l];
+        b.xn = take_f(H);
+        b.q = take_f(QW);
+        b.k = take_f(KVW);
+        b.v = take_f(KVW);
+        b.attn = take_f(QW);
+        b.attn_out = take_f(H);
+        b.xn2 = take_f(H);
+        b.gate = take_f(I);
+        b.up = take_f(I);
+        b.h = take_f(I);
+        b.ffn_out = take_f(H);
+      }
+      for (int32_t l = -1; l + 1 < M.n_layers; l++) rs[l + 1] = take_f(H);
+    } else {
+      float *other = take_f(H);
+      for (int32_t l = -1; l < M.n_layers; l++)
+        rs[l + 1] = ((M.n_layers - 1 - l) % 2 + 2) % 2 ? other : B.x;
+    }
+  }
+  auto resid = [&](int32_t l) { return rs[l + 1]; };
+  // the matvec levels: per layer q/k/v (0), o (1), gate/up (2), down (3); then the lm_head
   auto mv = [](const void *w, const float *x, float *y, int32_t *idx, int n, int p) {
     q8_matvec_desc d;
     d.w = w;
@@ -885,11 +992,12 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   std::vector<std::vector<q8_matvec_desc>> lv;
   for (int32_t l = 0; l < M.n_layers; l++) {
     const q8_decode_layer &L = M.layers[l];
-    lv.push_back({mv(L.wq, B.xn, B.q, nullptr, H, QW), mv(L.wk, B.xn, B.k, nullptr, H, KVW),
-                  mv(L.wv, B.xn, B.v, nullptr, H, KVW)});
-    lv.push_back({mv(L.wo, B.attn, B.attn_out, nullptr, QW, H)});
-    lv.push_back({mv(L.w_gate, B.xn2, B.gate, nullptr, H, I), mv(L.w_up, B.xn2, B.up, nullptr, H, I)});
-    lv.push_back({mv(L.w_down, B.h, B.ffn_out, nullptr, I, H)});
+    const LayerBufs &b = lb[l];
+    lv.push_back({mv(L.wq, b.xn, b.q, nullptr, H, QW), mv(L.wk, b.xn, b.k, nullptr, H, KVW),
+                  mv(L.wv, b.xn, b.v, nullptr, H, KVW)});
+    lv.push_back({mv(L.wo, b.attn, b.attn_out, nullptr, QW, H)});
+    lv.push_back({mv(L.w_gate, b.xn2, b.gate, nullptr, H, I), mv(L.w_up, b.xn2, b.up, nullptr, H, I)});
+    lv.push_back({mv(L.w_down, b.h, b.ffn_out, nullptr, I, H)});
   }
   lv.push_back({mv(M.lm_head, B.xf, B.logits, B.token, H, M.vocab)});
   std::vector<q8::StepPlan> plans(lv.size());
@@ -906,6 +1014,26 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   // device-scope stores.
   bool pro_path = H <= q8::kProMaxN && I <= q8::kProMaxN;
   for (const auto &pl : plans) pro_path = pro_path && pl.all_staged;
+  // The persistent form: one launch of as many workgroups as are resident
+  // at once with LDS for the widest staged tile and x and for an attention
+  // block; every level is planned on that grid, and every output but the
+  // logits is read by other workgroups of the launch (device-scope stores).
+  int pgrid = 0;
+  size_t plds = 0;
+  if (pers) {
+    if (!pro_path) return Q8_ERR_SHAPE;
+    plds = q8::attention_lds_bytes(G);
+    for (const auto &pl : plans) plds = pl.lds > plds ? pl.lds : plds;
+    pgrid = q8::decode_persistent_grid(dev, G, plds);
+    if (pgrid < 1) return Q8_ERR_SHAPE;
+    for (size_t i = 0; i < lv.size(); i++) {
+      st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
+                         plans[i], false, true, pgrid);
+      if (st) return st;
+      if (i + 1 < lv.size())
+        for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
+    }
+  }
   if (!pro_path)
     for (size_t i = 0; i + 1 < lv.size(); i++)
       if (i % 4 != 0)  // o, gate/up, down: their outputs are read by the epilogue
@@ -918,6 +1046,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   g->mode = Q8_GRAPH_DECODE;
   g->m = 1;
   g->i8x = false;
+  g->act = act.release();
 
   // workspace (256-byte aligned pieces): the lm_head argmax slot, the
   // epilogues' arrival slot, the attention arrival slots, the epilogues,
@@ -934,11 +1063,14 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   const size_t o_earr = take(sizeof(q8::ArgmaxSlot));
   const size_t o_aarr = take(sizeof(q8::ArgmaxSlot) * (size_t)M.n_kv_heads);
   const size_t o_epi = take(sizeof(q8::Epilogue) * 3 * (size_t)M.n_layers);
-  const size_t o_pro = take(sizeof(q8::Prologue) * 3 * (size_t)M.n_layers);
-  const size_t o_res = take(sizeof(float) * (size_t)H);  // the second residual buffer
+  const size_t o_pro = take(sizeof(q8::Prologue) * (3 * (size_t)M.n_layers + 1));
   const size_t o_freq = take(sizeof(float) * q8::kAttnHeadDim / 2);
   const size_t o_rope = take(sizeof(float) * q8::kAttnHeadDim);
   const size_t o_part = take(sizeof(float) * (size_t)M.n_heads * chunks * q8::kAttnPart);
+  const int32_t nphases = pers ? 5 * M.n_layers + 1 : 0;
+  const size_t o_bar = take(pers ? sizeof(q8::GridBarrier) : 0);
+  const size_t o_phase = take(sizeof(q8::DecPhase) * (size_t)nphases);
+  const size_t o_attn = take(pers ? sizeof(q8::AttnArgs) * (size_t)M.n_layers : 0);
   std::vector<size_t> o_tab(plans.size()), o_grp(plans.size());
   for (size_t i = 0; i < plans.size(); i++) {
     o_tab[i] = take(plans[i].descs.size() * sizeof(q8::StepDesc));
@@ -955,13 +1087,6 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   q8::ArgmaxSlot *earr = (q8::ArgmaxSlot *)(ws + o_earr);
   q8::Epilogue *epis = (q8::Epilogue *)(ws + o_epi);
   q8::Prologue *pros = (q8::Prologue *)(ws + o_pro);
-  // Prologue path: the residual stream after layer l, R_l, is written by
-  // the launch after that layer and read by the launches of the next, so it
-  // alternates between B.x and the workspace buffer, and the last one is
-  // in B.x: R_l lives in B.x when L - 1 - l is even (l = -1: the step's
-  // input, copied there by the first node).
-  float *const rbuf[2] = {B.x, (float *)(ws + o_res)};
-  auto resid = [&](int32_t l) { return rbuf[((M.n_layers - 1 - l) % 2 + 2) % 2]; };
   {
     q8::StepPlan &pl = plans.back();
     q8::ArgmaxSlot hs;
@@ -985,32 +1110,33 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     E[0].n = H;
     E[0].eps = M.eps;
     E[0].x = B.x;
-    E[0].r = B.attn_out;
+    E[0].r = lb[l].attn_out;
     E[0].g = L.ffn_norm;
-    E[0].out = B.xn2;
+    E[0].out = lb[l].xn2;
     E[0].arrive = earr;
     E[1].op = q8::kEpiSiluMul;  // after gate/up: h = silu(gate) * up
     E[1].n = I;
-    E[1].r = B.up;
-    E[1].g = B.gate;
-    E[1].out = B.h;
+    E[1].r = lb[l].up;
+    E[1].g = lb[l].gate;
+    E[1].out = lb[l].h;
     E[1].arrive = earr;
     const bool lastl = l + 1 == M.n_layers;
     E[2].op = q8::kEpiAddNorm;  // after down: x += ffn_out; next layer's xn, or xf
     E[2].n = H;
     E[2].eps = M.eps;
     E[2].x = B.x;
-    E[2].r = B.ffn_out;
+    E[2].r = lb[l].ffn_out;
     E[2].g = lastl ? M.out_norm : M.layers[l + 1].attn_norm;
-    E[2].out = lastl ? B.xf : B.xn;
+    E[2].out = lastl ? B.xf : lb[l + 1].xn;
     E[2].arrive = earr;
   }
   if (e == hipSuccess)
     e = hipMemcpy(epis, he.data(), he.size() * sizeof(q8::Epilogue), hipMemcpyHostToDevice);
   // prologues of layer l: 3l the gate/up launch's norm, 3l + 1 the down
   // launch's SwiGLU, 3l + 2 the next layer's q/k/v launch's (or the
-  // lm_head's) residual add and norm
-  std::vector<q8::Prologue> hp(3 * (size_t)M.n_layers);
+  // lm_head's) residual add and norm; 3L the first q/k/v launch's norm of
+  // x_in
+  std::vector<q8::Prologue> hp(3 * (size_t)M.n_layers + 1);
   std::memset(hp.data(), 0, hp.size() * sizeof(q8::Prologue));
   for (int32_t l = 0; l < M.n_layers; l++) {
     const q8_decode_layer &L = M.layers[l];
@@ -1019,24 +1145,34 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     P[0].n = H;
     P[0].eps = M.eps;
     P[0].a = resid(l - 1);
-    P[0].b = B.attn_out;
+    P[0].b = lb[l].attn_out;
     P[0].w = L.ffn_norm;
-    P[0].out = B.xn2;
+    P[0].out = lb[l].xn2;
     P[1].op = q8::kProSiluMul;  // h = silu(gate) * up
     P[1].n = I;
-    P[1].a = B.gate;
-    P[1].b = B.up;
-    P[1].out = B.h;
+    P[1].a = lb[l].gate;
+    P[1].b = lb[l].up;
+    P[1].out = lb[l].h;
     const bool lastl = l + 1 == M.n_layers;
     P[2].op = q8::kProAddNorm;  // R_l = (R_{l-1} + attn_out) + ffn_out; the next xn, or xf
     P[2].n = H;
     P[2].eps = M.eps;
     P[2].a = resid(l - 1);
-    P[2].b = B.attn_out;
-    P[2].c = B.ffn_out;
+    P[2].b = lb[l].attn_out;
+    P[2].c = lb[l].ffn_out;
     P[2].w = lastl ? M.out_norm : M.layers[l + 1].attn_norm;
-    P[2].out = lastl ? B.xf : B.xn;
+    P[2].out = lastl ? B.xf : lb[l + 1].xn;
     P[2].resid = resid(l);
+  }
+  {
+    q8::Prologue &P = hp[3 * (size_t)M.n_layers];
+    P.op = q8::kProNorm;  // R_{-1} = x_in; xn = norm(x_in)
+    P.n = H;
+    P.eps = M.eps;
+    P.a = B.x_in;
+    P.w = M.layers[0].attn_norm;
+    P.out = lb[0].xn;
+    P.resid = resid(-1);
   }
   if (e == hipSuccess)
     e = hipMemcpy(pros, hp.data(), hp.size() * sizeof(q8::Prologue), hipMemcpyHostToDevice);
@@ -1047,6 +1183,74 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
       e = hipMemcpy(ws + o_grp[i], plans[i].groups.data(),
                     plans[i].groups.size() * sizeof(q8::WgGroup), hipMemcpyHostToDevice);
   }
+  auto attn_args = [&](int32_t l) {
+    const q8_decode_layer &Ly = M.layers[l];
+    q8::AttnArgs a{};
+    a.q = lb[l].q;
+    a.k = lb[l].k;
+    a.v = lb[l].v;
+    a.q_norm = Ly.q_norm;
+    a.k_norm = Ly.k_norm;
+    a.kc = Ly.k_cache;
+    a.vc = Ly.v_cache;
+    a.pos = B.pos;
+    a.rope = (const float *)(ws + o_rope);
+    a.freq = (const float *)(ws + o_freq);
+    a.out = lb[l].attn;
+    a.part = (float *)(ws + o_part);
+    a.arrive = (q8::ArgmaxSlot *)(ws + o_aarr);
+    a.n_heads = M.n_heads;
+    a.n_kv = M.n_kv_heads;
+    a.cache_rows = M.cache_rows;
+    a.chunks = chunks;
+    a.eps = M.eps;
+    return a;
+  };
+  if (pers && e == hipSuccess) {
+    // the phase table: per layer q/k/v (layer 0 normalises x_in, a later
+    // layer adds the residuals of the one before), attention, o, gate/up
+    // (its norm), down (the SwiGLU); then the lm_head (the last residual
+    // add and the final norm)
+    std::vector<q8::AttnArgs> ha(M.n_layers);
+    std::vector<q8::DecPhase> ph;
+    const q8::AttnArgs *dattn = (const q8::AttnArgs *)(ws + o_attn);
+    auto mphase = [&](size_t i, const q8::Prologue *pro) {
+      q8::DecPhase d{};
+      d.kind = q8::kPhaseMatvec;
+      d.count = (int32_t)plans[i].descs.size();
+      d.group_size = plans[i].group_size;
+      d.grid = plans[i].grid;
+      d.table = (const q8::StepDesc *)(ws + o_tab[i]);
+      d.groups = (const q8::WgGroup *)(ws + o_grp[i]);
+      d.pro = pro;
+      ph.push_back(d);
+    };
+    for (int32_t l = 0; l < M.n_layers; l++) {
+      ha[l] = attn_args(l);
+      mphase(4 * (size_t)l, l ? &pros[3 * (size_t)l - 1] : &pros[3 * (size_t)M.n_layers]);
+      q8::DecPhase d{};
+      d.kind = q8::kPhaseAttention;
+      d.attn = dattn + l;
+      ph.push_back(d);
+      mphase(4 * (size_t)l + 1, nullptr);
+      mphase(4 * (size_t)l + 2, &pros[3 * (size_t)l]);
+      mphase(4 * (size_t)l + 3, &pros[3 * (size_t)l + 1]);
+    }
+    mphase(plans.size() - 1, &pros[3 * (size_t)M.n_layers - 1]);
+    e = ph.size() == (size_t)nphases ? hipSuccess : hipErrorInvalidValue;
+    if (e == hipSuccess)
+      e = hipMemcpy(ws + o_attn, ha.data(), ha.size() * sizeof(q8::AttnArgs),
+                    hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(ws + o_phase, ph.data(), ph.size() * sizeof(q8::DecPhase),
+                    hipMemcpyHostToDevice);
+    // the barrier: counters zero (the workspace's memset), the token's
+    // addresses for a failed wait
+    int32_t *const tok[2] = {B.token, host_dev};
+    if (e == hipSuccess)
+      e = hipMemcpy(ws + o_bar + offsetof(q8::GridBarrier, idx), tok, sizeof(tok),
+                    hipMemcpyHostToDevice);
+  }
   if (e == hipSuccess) e = q8::launch_rope_freq(M.theta, (float *)(ws + o_freq), nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -1054,6 +1258,18 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     return hip_fail(e);
   }
 
+  if (pers) {
+    SegmentLaunch L{nullptr, nullptr, 0, 0, pgrid, plds, true};
+    L.kind = kDecodeNode;
+    L.phases = (const q8::DecPhase *)(ws + o_phase);
+    L.nphases = nphases;
+    L.bar = (q8::GridBarrier *)(ws + o_bar);
+    L.heads_per_kv = G;
+    g->launches.push_back(L);
+    return capture_graph(g, out, [&](hipStream_t cs) {
+      return run_segment(g->launches[0], 1, false, cs);
+    });
+  }
   auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Prologue *pro = nullptr) {
     const q8::StepPlan &pl = plans[i];
     SegmentLaunch L{(const q8::StepDesc *)(ws + o_tab[i]), (const q8::WgGroup *)(ws + o_grp[i]),
@@ -1065,11 +1281,11 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   };
   {
     SegmentLaunch L{nullptr, nullptr, 0, 0, 0, 0, true};
-    L.kind = kNormNode;
-    L.nx = B.x_in;
+    L.kind = kNormNode;  // the rotation; the first norm too without prologues
+    L.nx = pro_path ? nullptr : B.x_in;
     L.nw = M.layers[0].attn_norm;
     L.nout = B.xn;
-    L.ncopy = pro_path ? resid(-1) : B.x;
+    L.ncopy = B.x;
     L.ndim = H;
     L.neps = M.eps;
     L.npos = B.pos;
@@ -1078,27 +1294,12 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     g->launches.push_back(L);
   }
   for (int32_t l = 0; l < M.n_layers; l++) {
-    const q8_decode_layer &Ly = M.layers[l];
-    step_node(4 * (size_t)l, nullptr, pro_path && l ? &pros[3 * (size_t)l - 1] : nullptr);
+    const q8::Prologue *qkv_pro =
+        l ? &pros[3 * (size_t)l - 1] : &pros[3 * (size_t)M.n_layers];
+    step_node(4 * (size_t)l, nullptr, pro_path ? qkv_pro : nullptr);
     SegmentLaunch A{nullptr, nullptr, 0, 0, 0, 0, true};
     A.kind = kAttnNode;
-    A.attn.q = B.q;
-    A.attn.k = B.k;
-    A.attn.v = B.v;
-    A.attn.q_norm = Ly.q_norm;
-    A.attn.k_norm = Ly.k_norm;
-    A.attn.kc = Ly.k_cache;
-    A.attn.vc = Ly.v_cache;
-    A.attn.pos = B.pos;
-    A.attn.rope = (const float *)(ws + o_rope);
-    A.attn.out = B.attn;
-    A.attn.part = (float *)(ws + o_part);
-    A.attn.arrive = (q8::ArgmaxSlot *)(ws + o_aarr);
-    A.attn.n_heads = M.n_heads;
-    A.attn.n_kv = M.n_kv_heads;
-    A.attn.cache_rows = M.cache_rows;
-    A.attn.chunks = chunks;
-    A.attn.eps = M.eps;
+    A.attn = attn_args(l);
     g->launches.push_back(A);
     if (pro_path) {
       step_node(4 * (size_t)l + 1, nullptr);

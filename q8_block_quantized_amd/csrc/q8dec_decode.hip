@@ -23,9 +23,10 @@ __global__ void __launch_bounds__(dec::kThreads) attention_kernel(AttnArgs a) {
   dec::attention_block<G, false>(a, (int)blockIdx.x, S, [] {});
 }
 
-// The step's first node: x = x_in and xn = rms_norm_row(x_in) (first
-// layer's weight), and the RoPE cos/sin pairs of position *pos (the same for
-// every layer), rope[2i] = cos(pos * freq[i]), rope[2i + 1] = sin(...).
+// The step's first node: the RoPE cos/sin pairs of position *pos (the same
+// for every layer), rope[2i] = cos(pos * freq[i]), rope[2i + 1] = sin(...),
+// and, when x_in is set, x = x_in and xn = rms_norm_row(x_in) (the first
+// layer's weight; otherwise the first q/k/v launch's prologue computes xn).
 __global__ void __launch_bounds__(dec::kThreads)
 step_start_kernel(const float *x_in, const float *w, float *xn, float *x, int dim, float eps,
                   const int32_t *pos, const float *freq, float *rope) {
@@ -38,7 +39,7 @@ step_start_kernel(const float *x_in, const float *w, float *xn, float *x, int di
     rope[2 * threadIdx.x] = cs;
     rope[2 * threadIdx.x + 1] = sn;
   }
-  dec::norm_row(x_in, nullptr, x, w, xn, dim, eps, vs, red);
+  if (x_in) dec::norm_row(x_in, nullptr, x, w, xn, dim, eps, vs, red);
 }
 
 __global__ void rope_freq_kernel(float theta, float *freq) {

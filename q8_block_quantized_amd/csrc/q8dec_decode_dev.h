@@ -314,9 +314,10 @@ struct AttnLds {
 // trip.  `wait` is called once, after the cached rows' loads are issued and
 // before anything this token's step produced is read (a persistent launch
 // waits there for the rest of the grid; the cached rows are older).  COH
-// (the persistent launch): q, k, v are read and the output stored at device
-// scope (other XCDs wrote or read them within the launch), and the rotation
-// comes from freq instead of the rope table.
+// (the persistent launch): the output is stored at device scope (workgroups
+// on other XCDs read it in the next phase), and the rotation comes from
+// freq instead of the rope table.  q, k, v are plain loads in both forms:
+// the persistent launch writes each of them once, before this phase.
 template <int G, bool COH, class Wait>
 __device__ __forceinline__ void attention_block(const AttnArgs &a, int blk, AttnLds<G> &S,
                                                 Wait &&wait) {
@@ -375,8 +376,8 @@ __device__ __forceinline__ void attention_block(const AttnArgs &a, int blk, Attn
     if (vec < G + 2) {
       const float *src = vec < G ? a.q + (size_t)(g * G + vec) * HD
                                  : (vec == G ? a.k : a.v) + (size_t)g * HD;
-      x0[j] = COH ? ld_dev(src + lane) : src[lane];
-      x1[j] = COH ? ld_dev(src + lane + 64) : src[lane + 64];
+      x0[j] = src[lane];
+      x1[j] = src[lane + 64];
     }
   }
   const float wq0 = a.q_norm[lane], wq1 = a.q_norm[lane + 64];

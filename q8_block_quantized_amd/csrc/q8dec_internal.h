@@ -216,7 +216,9 @@ static_assert(sizeof(Epilogue) == 64, "epilogue layout");
 //   kProAddNorm: s = (a + b) + c (c may be NULL), out = s / sqrt(mean(s^2)
 //                + eps) * w (rms_norm_row of the residual stream), resid
 //                (or NULL) receives s.
-enum ProOp : int32_t { kProNone = 0, kProSiluMul = 1, kProAddNorm = 2 };
+//   kProNorm:    s = a, out = s / sqrt(mean(s^2) + eps) * w, resid (or NULL)
+//                receives s (the persistent step's first layer: x = x_in).
+enum ProOp : int32_t { kProNone = 0, kProSiluMul = 1, kProAddNorm = 2, kProNorm = 3 };
 struct Prologue {
   int32_t op, n;
   float eps;
@@ -256,12 +258,55 @@ struct AttnArgs {
 int attn_chunks(int cache_rows);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
-// The step's first node: x = x_in, xn = rms_norm_row(x_in) * w (dim <=
-// kNormMaxDim), and rope[2i], rope[2i + 1] = cos, sin of *pos * freq[i] for
-// i < 64.
+// The step's first node: rope[2i], rope[2i + 1] = cos, sin of *pos * freq[i]
+// for i < 64, and when x_in is set x = x_in, xn = rms_norm_row(x_in) * w
+// (dim <= kNormMaxDim).
 hipError_t launch_step_start(const float *x_in, const float *w, float *xn, float *x,
                              int dim, float eps, const int32_t *pos, const float *freq,
                              float *rope, hipStream_t s);
+
+// ---- the persistent decode step ------------------------------------------
+//
+// One launch runs every phase of the step (per layer: q/k/v, attention, o,
+// gate/up, down; then the lm_head and its argmax), workgroups meeting at a
+// grid-wide barrier between phases.  Every workgroup must be resident at
+// once (the grid is the kernel's resident capacity); a wait that runs past
+// its limit (another workgroup never arrived) marks the barrier failed,
+// stores -2 as the token and ends the workgroup, so no launch can hang.
+constexpr int32_t kPhaseMatvec = 0, kPhaseAttention = 1;
+struct DecPhase {
+  int32_t kind;        // kPhaseMatvec or kPhaseAttention
+  int32_t count;       // matvec: descriptors of the table
+  int32_t group_size;  // matvec: its plan's groups of workgroups
+  int32_t grid;        // matvec: workgroups with tiles (the rest only meet the barrier)
+  const StepDesc *table;
+  const WgGroup *groups;
+  const Prologue *pro;   // or NULL
+  const AttnArgs *attn;  // attention
+};
+static_assert(sizeof(DecPhase) == 48, "phase layout");
+
+// Grid barrier state, zeroed once (the graph's workspace): team j's arrival
+// counter and released generation each in their own 128-byte line.  The
+// counters only grow, so a barrier belongs to one grid size.
+struct GridBarrier {
+  uint32_t team[32][32];  // team j counts at [j][0]
+  uint32_t top[32];
+  uint32_t gen[32][32];   // the generation released to team j, at [j][0]
+  uint32_t error[32];     // [0]: nonzero once a wait ran past its limit
+  int32_t *idx;           // the step's token (device), -2 on failure
+  int32_t *host;          // its pinned host copy, or NULL
+  uint64_t pad[14];
+};
+constexpr int kGridTeams = 32;
+
+// Resident workgroups of the persistent decode kernel (G query heads per
+// key/value head, `lds` bytes of dynamic LDS) on `dev`.
+int decode_persistent_grid(int dev, int G, size_t lds);
+// LDS of one attention block with G query heads per key/value head.
+size_t attention_lds_bytes(int G);
+hipError_t launch_decode_persistent(const DecPhase *phases, int nphases, GridBarrier *bar,
+                                    int grid, size_t lds, int G, hipStream_t s);
 
 // freq[i] = 1 / theta^(i / 64) for i < 64, the power rounded to binary32
 // from binary64 and the quotient in binary32 (the RoPE frequencies).
@@ -272,6 +317,9 @@ hipError_t launch_rope_freq(float theta, float *freq, hipStream_t s);
 struct q8_matvec_desc;
 namespace q8 {
 // Plans a persistent step (q8dec_api.hip) with groups of `group_size`.
+// grid_cap > 0: the launch's grid (the persistent decode step's) instead of
+// the step kernel's resident capacity.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan, bool i8x = false, bool dec = false);
+              int group_size, StepPlan &plan, bool i8x = false, bool dec = false,
+              int grid_cap = 0);
 }  // namespace q8

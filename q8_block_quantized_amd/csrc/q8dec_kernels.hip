@@ -59,6 +59,14 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *gpw(T *p) {
   return (__attribute__((address_space(1))) T *)p;
 }
 
+// Four floats read at device scope (another XCD may have written them in
+// this launch; a plain load could return a stale L2 copy), and four stored
+// at device scope.
+__device__ __forceinline__ void st_dev4(float *p, const f32x4 &v) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) dec::st_dev(p + e, v[e]);
+}
+
 // A matvec output.  dev: stored at device scope (written through to where
 // every XCD sees it), so that a workgroup of the same launch can read it with
 // device-scope loads and no L2 write-back (the epilogue, see arrive_last).
@@ -1147,19 +1155,21 @@ struct ProRegs {
   f32x4 a[kProChunks], b[kProChunks], c[kProChunks], w[kProChunks];
 };
 
-__device__ __forceinline__ void pro_load(const Prologue *p, ProRegs &r) {
-  const int32_t chunks = p->n >> 2;
-  const bool norm = p->op == kProAddNorm;
+__device__ __forceinline__ void pro_load(const Prologue &p, ProRegs &r) {
+  const int32_t chunks = p.n >> 2;
+  const bool norm = p.op == kProAddNorm || p.op == kProNorm;
+  const bool add = p.op != kProNorm;
+  auto ld = [](const float *q, int32_t c) { return gp((const f32x4 *)q)[c]; };
 #pragma unroll
   for (int k = 0; k < kProChunks; k++) {
     const int32_t c = (int32_t)threadIdx.x + k * kWG;
     r.a[k] = r.b[k] = r.c[k] = r.w[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < chunks) {
-      r.a[k] = gp((const f32x4 *)p->a)[c];
-      r.b[k] = gp((const f32x4 *)p->b)[c];
+      r.a[k] = ld(p.a, c);
+      if (add) r.b[k] = ld(p.b, c);
       if (norm) {
-        if (p->c) r.c[k] = gp((const f32x4 *)p->c)[c];
-        r.w[k] = gp((const f32x4 *)p->w)[c];
+        if (add && p.c) r.c[k] = ld(p.c, c);
+        r.w[k] = gp((const f32x4 *)p.w)[c];
       }
     }
   }
@@ -1167,22 +1177,28 @@ __device__ __forceinline__ void pro_load(const Prologue *p, ProRegs &r) {
 
 // The prologue's arithmetic on the values pro_load fetched.  red: 4 floats
 // of LDS not otherwise in use.
-__device__ __forceinline__ void pro_finish(const Prologue *p, ProRegs &r, float *xs,
+// COH: workgroup 0's stores are device-scope (workgroups on other XCDs read
+// them in later phases of the launch).
+template <bool COH = false>
+__device__ __forceinline__ void pro_finish(const Prologue &p, ProRegs &r, float *xs,
                                            float *red, bool keep) {
-  const int32_t chunks = p->n >> 2;
-  const bool norm = p->op == kProAddNorm;
+  const int32_t chunks = p.n >> 2;
+  const bool norm = p.op == kProAddNorm || p.op == kProNorm;
+  const bool add = p.op == kProAddNorm;
   float inv = 0.f;
   if (norm) {  // the residual sum in the order the adds run: (a + b) + c
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < kProChunks; k++) {
-      r.a[k] = r.a[k] + r.b[k];
-      if (p->c) r.a[k] = r.a[k] + r.c[k];
+      if (add) {
+        r.a[k] = r.a[k] + r.b[k];
+        if (p.c) r.a[k] = r.a[k] + r.c[k];
+      }
 #pragma unroll
       for (int e = 0; e < 4; e++) ss += r.a[k][e] * r.a[k][e];
     }
     ss = dec::block_sum(ss, red);
-    inv = 1.0f / sqrtf(ss / (float)p->n + p->eps);
+    inv = 1.0f / sqrtf(ss / (float)p.n + p.eps);
   }
 #pragma unroll
   for (int k = 0; k < kProChunks; k++) {
@@ -1192,14 +1208,20 @@ __device__ __forceinline__ void pro_finish(const Prologue *p, ProRegs &r, float 
       if (norm) {
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = r.a[k][e] * inv * r.w[k][e];
-        if (keep && p->resid) gpw((f32x4 *)p->resid)[c] = r.a[k];
+        if (keep && p.resid) {
+          if (COH) st_dev4(p.resid + 4 * c, r.a[k]);
+          else gpw((f32x4 *)p.resid)[c] = r.a[k];
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = r.a[k][e] / (1.0f + expf(-r.a[k][e])) * r.b[k][e];
       }
       const int32_t i = 4 * c;
       *(f32x4 *)&xs[36 * (i >> 5) + (i & 31)] = o;
-      if (keep) gpw((f32x4 *)p->out)[c] = o;
+      if (keep) {
+        if (COH) st_dev4(p.out + 4 * c, o);
+        else gpw((f32x4 *)p.out)[c] = o;
+      }
     }
   }
 }
@@ -1244,11 +1266,24 @@ __device__ __forceinline__ void set_progress_prio(int32_t left, int32_t total) {
 // known at compile time (a standalone staged matvec), so the kernel holds
 // one copy of the row loop instead of one per width and output mode.
 // LDS: the staged tile, then (batched) the partial sums, then the padded x.
+// COH (the persistent decode step, with DEC): what the launch hands from one
+// phase to the next (the prologue's stores) is stored at device scope, and
+// `wait` (the grid barrier; false when it failed) runs after this
+// workgroup's first tile's weight bytes are requested and before anything
+// the launch produced is read, so the barrier's latency and the first
+// tile's overlap.  A workgroup without tiles only waits.  Its reads are
+// plain loads: each buffer they read is written once in the launch, before
+// the barrier that precedes the read, so no cache can hold an older copy
+// (see decode_kernel).
+struct NoWait {
+  __device__ bool operator()() const { return true; }
+};
 template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src,
-          bool STRIDED = false>
+          bool STRIDED = false, bool COH = false, class Wait = NoWait>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
-                          float *lds, const Prologue *pro = nullptr) {
+                          float *lds, const Prologue *pro = nullptr, Wait wait = Wait()) {
+  static_assert(!COH || DEC, "the persistent decode step: the decode variant");
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
   constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
@@ -1266,7 +1301,10 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     return M1 ? (!ANY || j.path != kGeneric) : (ANY && j.path == kDirect);
   };
   int32_t t = first;
-  if (t >= end) return;
+  if (t >= end) {
+    wait();
+    return;
+  }
   Prefetch<XC, CH> pf;
   // The job of tile tn, a later tile than `from`'s: the same matvec, or one
   // found in the table.
@@ -1280,8 +1318,14 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   bool more = t + stride < end;
   Job nxt = more ? job_after(cur, t + stride) : cur;
   ProRegs prr;
+  // the prologue's descriptor, read before the tiles' loads (and, in the
+  // persistent step, before the barrier): its fields address the loads
+  Prologue pr{};
   if constexpr (DEC) {
-    if (pro) pro_load(pro, prr);  // before the tile's loads: see pro_load
+    if (pro) pr = *pro;
+  }
+  if constexpr (DEC && !COH) {
+    if (pro) pro_load(pr, prr);  // before the tile's loads: see pro_load
   }
   // a tile's weight bytes: whole rows, or (STRIDED) rows of a column slice
   auto load_tile = [&](const Job &j) {
@@ -1293,18 +1337,23 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       pf.load_w(j.d.w + (uint64_t)j.r0 * rb, j.rows * rb);
   };
   if (staged(cur) || mfma(cur)) load_tile(cur);
+  if (!wait()) return;  // the weights are in flight; what follows may read this launch's values
+  if constexpr (DEC && COH) {
+    if (pro) pro_load(pr, prr);
+  }
   // the x staged in LDS (and the batched path's operand A): matvecs that
   // share x (the same pointer and width) are staged once
   const float *xptr = nullptr, *xaptr = nullptr;
   int32_t xn = 0, xan = 0;
   if constexpr (DEC) {
     if (pro) {  // the launch's x is pro->out, computed here while the first tile loads
-      pro_finish(pro, prr, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
-      xptr = pro->out;
-      xn = pro->n;
+      pro_finish<COH>(pr, prr, xs, lds, blockIdx.x == 0);  // the tile buffer is still free
+      xptr = pr.out;
+      xn = pr.n;
     }
   }
-  if (x_in_lds(cur) && (cur.d.x != xptr || cur.d.n != xn)) pf.load_x(cur.d.x, m * cur.d.n);
+  if (x_in_lds(cur) && (cur.d.x != xptr || cur.d.n != xn))
+    pf.load_x(cur.d.x, m * cur.d.n);
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
   u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
@@ -1756,6 +1805,155 @@ step_kernel(const StepDesc *__restrict__ table, int32_t count,
   }
 }
 
+// ---- the persistent decode step --------------------------------------------
+
+__device__ __forceinline__ uint32_t ld_dev_u32(uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A wait at the grid barrier gives up after this many ticks of the 100 MHz
+// clock (200 ms; a whole decode step takes about 1 ms).
+constexpr uint64_t kBarrierSpinTicks = 20000000ull;
+
+// This workgroup's arrival at the grid barrier that releases generation
+// `target`.  Every wave first waits until its stores are complete (the
+// values it hands on travel with device-scope stores), then thread 0 counts
+// the workgroup into its team (workgroup b in team b % 32, its counter in
+// its own line); the team's last arrival counts the team in, and the last
+// team's arrival writes `target` into every team's release line.  The
+// counters are never reset: after generation t is released team j's reads
+// size_j * t and the top counter nteams * t (modulo 2^32), so an arrival
+// knows it is the last one from the value its increment returns, and no
+// store has to be ordered before another.  Relaxed agent-scope atomics.
+__device__ __forceinline__ void grid_arrive(GridBarrier *b, uint32_t target) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x, T = kGridTeams, j = blockIdx.x % T;
+    const uint32_t size = (G - j + T - 1) / T, nteams = G < T ? G : T;
+    const uint32_t prev = __hip_atomic_fetch_add(&b->team[j][0], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1u == size * target) {
+      const uint32_t p2 = __hip_atomic_fetch_add(&b->top[0], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+      if (p2 + 1u == nteams * target)
+        for (uint32_t k = 0; k < T; k++) st_dev_u32(&b->gen[k][0], target);
+    }
+  }
+}
+
+// Waits (thread 0 polls its team's release line) until `target` is
+// released.  False in every thread once the barrier has failed: this wait
+// ran past kBarrierSpinTicks (it then marks the failure and stores -2 as
+// the step's token) or another workgroup's did.  flag: one word of LDS.
+__device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint32_t *flag) {
+  if (threadIdx.x == 0) {
+    uint32_t ok = 1u;
+    uint32_t *line = &b->gen[blockIdx.x % kGridTeams][0];
+    const uint64_t start = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      if ((int32_t)(ld_dev_u32(line) - target) >= 0) break;
+      if (ld_dev_u32(&b->error[0])) {
+        ok = 0u;
+        break;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - start > kBarrierSpinTicks) {
+        st_dev_u32(&b->error[0], 1u);
+        ok = 0u;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) {
+      int32_t *idx = gp(&b->idx)[0], *host = gp(&b->host)[0];
+      if (idx) __hip_atomic_store(idx, -2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (host) __hip_atomic_store(host, -2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag != 0u;
+  __syncthreads();  // the flag is rewritten by the next wait
+  return ok;
+}
+
+// The whole decode step in one launch (G query heads per key/value head):
+// the phases of a device-side table in order, every workgroup meeting the
+// others at the grid barrier between two phases.  A matvec phase runs the
+// decode step kernel's tiles (outputs stored at device scope); an attention
+// phase gives workgroup b the attention blocks b, b + grid, ...; a
+// workgroup with nothing to do in a phase only meets the barrier.  Between
+// its arrival and its wait a workgroup requests its next phase's first
+// weight tile (a matvec phase) or its cached key and value rows (an
+// attention phase), which do not depend on the phase before.
+// The values one phase hands to the next are written to buffers that the
+// launch writes once (each layer has its own, 256-byte aligned), stored at
+// device scope, so they are in memory before their writer arrives at the
+// barrier.  Their readers use plain loads: the caches were invalidated when
+// the launch started and no workgroup has read those lines since, so the
+// first read of a line by an XCD misses its L2 and fetches the stored
+// value, and the XCD's other workgroups then hit in its L2.  (Device-scope
+// loads instead go to memory for every workgroup: 512 workgroups reading
+// the same 4-24 KB vector took 1-3 us per phase on MI355X.)  The attention
+// partials, reused by every layer, are still read at device scope.
+// Two workgroups per CU: the compiler then keeps every value in registers
+// (224 VGPRs); asked for three or four it spills 56-261 of them.
+template <int G>
+__global__ void __launch_bounds__(kWG, 2)
+decode_kernel(const DecPhase *__restrict__ phases, int32_t nphases,
+              GridBarrier *__restrict__ bar) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ uint32_t flag;
+  if (threadIdx.x == 0)  // read before this workgroup's first arrival, so no
+                         // barrier of this launch has been released yet
+    flag = ld_dev_u32(&bar->gen[blockIdx.x % kGridTeams][0]);
+  __syncthreads();
+  const uint32_t base = flag;
+  __syncthreads();
+  bool ok = true;
+  for (int32_t i = 0; i < nphases && ok; i++) {
+    if (i > 0) grid_arrive(bar, base + (uint32_t)i);
+    const DecPhase ph = phases[i];
+    auto wait = [&]() -> bool {
+      if (i > 0 && ok) ok = grid_wait(bar, base + (uint32_t)i, &flag);
+      return ok;
+    };
+    if (ph.kind == kPhaseMatvec) {
+      const int32_t b = (int32_t)blockIdx.x;
+      if (b < ph.grid) {
+        TableSrc src{ph.table, ph.count};
+        const WgGroup g = ph.groups[b / ph.group_size];
+        const int32_t j = b - g.first;
+        run_tiles<true, false, false, false, 0, true, TableSrc, false, true>(
+            src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, g.d0, 1, lds, ph.pro,
+            wait);
+      } else {
+        wait();
+      }
+    } else {
+      const AttnArgs a = *ph.attn;
+      dec::AttnLds<G> &S = *(dec::AttnLds<G> *)lds;
+      bool waited = false;
+      auto wait_once = [&] {
+        if (!waited) {
+          waited = true;
+          wait();
+        }
+      };
+      for (int32_t blk = (int32_t)blockIdx.x; blk < a.n_kv * a.chunks && ok;
+           blk += (int32_t)gridDim.x) {
+        dec::attention_block<G, true>(a, blk, S, wait_once);
+        __syncthreads();  // S serves the next block
+      }
+      wait_once();
+    }
+    __syncthreads();  // the phase's readers of LDS are done
+  }
+}
+
 // Wide batches (8 < m <= 32): one matvec (tiles round-robin over the grid),
 // or every tile of a descriptor table in workgroup groups, as the kernels
 // above.
@@ -2082,6 +2280,45 @@ hipError_t launch_matvec_split(const uint8_t *w, const float *x, float *y, int n
   int64_t per = ((int64_t)p + kWG * 8 - 1) / (kWG * 8);
   const int gx = (int)(per < 1 ? 1 : (per > 512 ? 512 : per));
   hipLaunchKernelGGL(reduce_slices, dim3(gx), dim3(kWG), 0, s, part, slices, p, y, slot, idx);
+  return hipGetLastError();
+}
+
+namespace {
+template <int G>
+int decode_grid_of(int dev, size_t lds) {
+  return resident_wgs(decode_kernel<G>, lds, dev);
+}
+}  // namespace
+
+size_t attention_lds_bytes(int G) {
+  switch (G) {
+    case 1: return sizeof(dec::AttnLds<1>);
+    case 2: return sizeof(dec::AttnLds<2>);
+    case 3: return sizeof(dec::AttnLds<3>);
+    default: return sizeof(dec::AttnLds<4>);
+  }
+}
+
+int decode_persistent_grid(int dev, int G, size_t lds) {
+  switch (G) {
+    case 1: return decode_grid_of<1>(dev, lds);
+    case 2: return decode_grid_of<2>(dev, lds);
+    case 3: return decode_grid_of<3>(dev, lds);
+    case 4: return decode_grid_of<4>(dev, lds);
+    default: return 0;
+  }
+}
+
+hipError_t launch_decode_persistent(const DecPhase *phases, int nphases, GridBarrier *bar,
+                                    int grid, size_t lds, int G, hipStream_t s) {
+  const dim3 g((unsigned)grid), b(kWG);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(decode_kernel<1>, g, b, lds, s, phases, nphases, bar); break;
+    case 2: hipLaunchKernelGGL(decode_kernel<2>, g, b, lds, s, phases, nphases, bar); break;
+    case 3: hipLaunchKernelGGL(decode_kernel<3>, g, b, lds, s, phases, nphases, bar); break;
+    case 4: hipLaunchKernelGGL(decode_kernel<4>, g, b, lds, s, phases, nphases, bar); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -111,9 +111,10 @@ static void refusals() {
 
 // Walks every workgroup's tiles of a plan one by one and checks the plan.
 static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int group_size,
-                       bool i8x) {
+                       bool i8x, int grid_cap = 0) {
   q8::StepPlan plan;
-  const int st = q8::plan_step(descs.data(), (int32_t)descs.size(), m, 0, group_size, plan, i8x);
+  const int st = q8::plan_step(descs.data(), (int32_t)descs.size(), m, 0, group_size, plan, i8x,
+                               grid_cap > 0, grid_cap);
   CHECK(st == Q8_OK);
   if (st != Q8_OK) return;
   // descriptors: consecutive tile ranges covering every row
@@ -127,6 +128,7 @@ static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int grou
     ntiles += tiles;
   }
   CHECK(plan.grid >= 1 && plan.grid <= ntiles);
+  if (grid_cap > 0) CHECK(plan.grid <= grid_cap);
   // groups: contiguous ranges that partition [0, ntiles); each workgroup's
   // tiles t0 + slot, + size, ... cover its group's range exactly once
   std::vector<int> owner(ntiles, -1);
@@ -192,6 +194,17 @@ static void planner() {
   check_plan({mv(1024, 2048, false), mv(1024, 1024, false), mv(1024, 1024, false)}, 1,
              q8::kStepGroupSize, false);
   check_plan({mv(256, 1, true)}, 1, q8::kStepGroupSize, false);
+  // the persistent decode step's phases on a grid of 512 (at most one tile
+  // per workgroup where the staged heights allow), and small or odd grids
+  const std::vector<std::vector<q8_matvec_desc>> phases = {
+      {mv(1024, 2048, false), mv(1024, 1024, false), mv(1024, 1024, false)},
+      {mv(2048, 1024, false)},
+      {mv(1024, 3072, false), mv(1024, 3072, false)},
+      {mv(3072, 1024, false)},
+      {mv(1024, 151936, true)}};
+  for (const auto &ph : phases)
+    for (int cap : {512, 513, 7, 1}) check_plan(ph, 1, q8::kStepGroupSize, false, cap);
+  for (int cap : {512, 3}) check_plan(mixed, 1, 8, false, cap);
 }
 
 int main() {

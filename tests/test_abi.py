@@ -228,12 +228,12 @@ def _decode_args(n_layers=1, layer_over=None, buf_over=None, **over):
         layers[i] = q8.DecodeLayer(*[vals[f] for f in q8.LAYER_FIELDS])
     keep.append(layers)
     dims = dict(n_layers=n_layers, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
-                inter=3072, vocab=151936, cache_rows=1024, eps=1e-6, theta=1e6)
+                inter=3072, vocab=151936, cache_rows=1024, eps=1e-6, theta=1e6, form=0)
     dims.update(over)
     model = q8.DecodeModel(dims["n_layers"], dims["hidden"], dims["n_heads"],
                            dims["n_kv_heads"], dims["head_dim"], dims["inter"], dims["vocab"],
                            dims["cache_rows"], dims["eps"], dims["theta"],
-                           ctypes.addressof(layers), 0x7000000, 0x7100000)
+                           ctypes.addressof(layers), 0x7000000, 0x7100000, dims["form"])
     bvals = {f: 0x8000000 + 0x100000 * j for j, f in enumerate(q8.BUFFER_FIELDS)}
     bvals.update(buf_over or {})
     bufs = q8.DecodeBuffers(*[bvals[f] for f in q8.BUFFER_FIELDS])
@@ -268,6 +268,7 @@ def test_decode_graph_refusals(lib):
     assert call(eps=-1.0) == SHAPE
     assert call(eps=float("nan")) == SHAPE
     assert call(theta=0.0) == SHAPE
+    assert call(form=2) == MODE and call(form=-1) == MODE
     assert call(layer_over=dict(wq=0)) == NULL
     assert call(layer_over=dict(k_cache=0)) == NULL
     assert call(layer_over=dict(wo=0x100004)) == ALIGN

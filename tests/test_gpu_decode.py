@@ -52,7 +52,7 @@ def oracle_layer(L):
 class DeviceModel:
     """The model's tensors on the GPU, the step's buffers and its graph."""
 
-    def __init__(self, model, device, logits=True):
+    def __init__(self, model, device, logits=True, form=None):
         import torch
         self.model = model
         self.dims = model["dims"]
@@ -70,10 +70,12 @@ class DeviceModel:
         self.bufs["x_in"].copy_(to_dev(model["x_in"], device))
         self.host = torch.full((1,), -7, dtype=torch.int32).pin_memory()
         self.graph = q8.DecodeGraph(self.dims, self.layers, self.out_norm, self.lm_head,
-                                    self.bufs, host_token=self.host)
+                                    self.bufs, host_token=self.host, form=form)
 
-    def run(self, pos, kernel=False):
+    def run(self, pos, kernel=False, x_in=None):
         import torch
+        if x_in is not None:
+            self.bufs["x_in"].copy_(to_dev(x_in, self.device))
         self.bufs["pos"].fill_(pos)
         self.host.fill_(-7)
         for k in BUF_F32:
@@ -340,3 +342,135 @@ def test_full_step_against_oracle(cuda):
                                      np.abs(res["xf"].astype(np.float64) - ref["xf"]))
     slack = 1e-4 * tol + 1e-6 + dense_abs
     assert oracle.argmax_accepted(res["token"], y_ref, slack), "token"
+
+
+# ---- the persistent form: one launch, a grid-wide barrier between phases ----
+
+PERSIST = [
+    # (label, dims, cache rows, pos): G = 1, 2, 3, 4; the widest shapes the
+    # form takes (hidden and inter 3072); ragged and two-round merges
+    ("p-g1", dict(n_layers=2, hidden=256, n_heads=2, n_kv_heads=2, head_dim=128, inter=512,
+                  vocab=300, eps=1e-6, theta=1e4), 100, 99),
+    ("p-g2-ragged", dict(n_layers=1, hidden=256, n_heads=2, n_kv_heads=1, head_dim=128,
+                         inter=512, vocab=300, eps=1e-5, theta=1e6), 100, 70),
+    ("p-g3", dict(n_layers=3, hidden=768, n_heads=6, n_kv_heads=2, head_dim=128, inter=512,
+                  vocab=1000, eps=1e-6, theta=5e5), 200, 150),
+    ("p-g4-long", dict(n_layers=1, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128,
+                       inter=256, vocab=1000, eps=1e-6, theta=1e6), 2600, 2500),
+    ("p-g2-long", dict(n_layers=1, hidden=256, n_heads=2, n_kv_heads=1, head_dim=128,
+                       inter=256, vocab=300, eps=1e-6, theta=1e6), 5000, 4700),
+    ("p-widest", dict(n_layers=2, hidden=3072, n_heads=8, n_kv_heads=4, head_dim=128,
+                      inter=3072, vocab=5000, eps=1e-6, theta=1e6), 130, 129),
+]
+
+
+def run_both(model, device, pos, logits=True, seq=()):
+    """The node form's and the persistent form's results at one position,
+    then (both forms) at each (position, input) of seq in order: launches
+    that read other values than the launch before (a stale cached copy of
+    the previous launch's activations would show as a difference)."""
+    res = {}
+    for form in (q8.Q8_DECODE_NODES, q8.Q8_DECODE_PERSISTENT):
+        dm = DeviceModel(model, device, logits=logits, form=form)
+        try:
+            res[form] = dm.run(pos)
+            if form == q8.Q8_DECODE_PERSISTENT:  # the same inputs (row pos rewritten alike)
+                res["kernel"] = dm.run(pos, kernel=True)
+                res["again"] = dm.run(pos)
+                res["info"] = dm.graph.info()
+            res[(form, "seq")] = [dm.run(p, x_in=x) for p, x in seq]
+        finally:
+            dm.close()
+    for i, (a, b) in enumerate(zip(res[(q8.Q8_DECODE_NODES, "seq")],
+                                   res[(q8.Q8_DECODE_PERSISTENT, "seq")])):
+        assert_same(a, b, f"node form against persistent form, launch {i + 2}")
+    return res[q8.Q8_DECODE_NODES], res[q8.Q8_DECODE_PERSISTENT], res
+
+
+def assert_same(a, b, label):
+    for k in BUF_F32:
+        if k in a:
+            assert np.array_equal(a[k], b[k], equal_nan=True), f"{label}: {k}"
+    for l in range(len(a["kc"])):
+        assert np.array_equal(a["kc"][l], b["kc"][l]), f"{label}: layer {l} key cache"
+        assert np.array_equal(a["vc"][l], b["vc"][l]), f"{label}: layer {l} value cache"
+    assert a["token"] == b["token"] and a["host_token"] == b["host_token"], label
+
+
+@pytest.mark.parametrize("label,dims,rows,pos", PERSIST, ids=[c[0] for c in PERSIST])
+def test_persistent_shapes(cuda, label, dims, rows, pos):
+    """Each stage against the oracle; the node form's buffers bit for bit
+    (every output row is computed by one workgroup in the same order in both
+    forms, the attention rotation from the same binary32 angle); a kernel
+    launch and a second graph launch the same again; one kernel node."""
+    model = gen.decode_model(dims, cache_rows=rows, seed=17)
+    say(f"persistent {label}: {dims}, cache {rows}, pos {pos}")
+    x2 = np.ascontiguousarray(model["x_in"][::-1] * np.float32(0.5))
+    seq = [(pos - 1, x2), (pos, x2), (pos - 1, model["x_in"])]
+    nodes, pers, extra = run_both(model, cuda, pos, seq=seq)
+    assert pers["token"] >= 0, f"token {pers['token']} (-2: the grid barrier gave up)"
+    check_stages(pers, model, pos, x_in=model["x_in"] if dims["n_layers"] == 1 else None)
+    check_untouched(pers, model, pos)
+    assert_same(nodes, pers, "node form against persistent form")
+    assert_same(pers, extra["kernel"], "kernel launch")
+    assert_same(pers, extra["again"], "second graph launch")
+    assert extra["info"] == (1, 0)
+
+
+@pytest.mark.parametrize("pos", [0, 64, 1023])
+def test_persistent_one_layer(cuda, pos):
+    model = gen.decode_model(QWEN1, cache_rows=1024, seed=pos + 5)
+    say(f"persistent, one Qwen3-shaped layer, pos {pos}")
+    nodes, pers, _ = run_both(model, cuda, pos)
+    check_stages(pers, model, pos, x_in=model["x_in"])
+    check_untouched(pers, model, pos)
+    assert_same(nodes, pers, "node form against persistent form")
+
+
+def test_persistent_bad_position(cuda):
+    """pos outside [0, cache_rows) in the persistent form: as the node form."""
+    dims = dict(n_layers=2, hidden=256, n_heads=2, n_kv_heads=1, head_dim=128, inter=512,
+                vocab=300, eps=1e-6, theta=1e6)
+    model = gen.decode_model(dims, cache_rows=64, seed=9)
+    dm = DeviceModel(model, cuda, form=q8.Q8_DECODE_PERSISTENT)
+    try:
+        for pos in (64, -1):
+            res = dm.run(pos)
+            assert np.isnan(res["attn"]).all()
+            assert res["token"] == -1 and res["host_token"] == -1
+            check_untouched(res, model, -5)
+        res = dm.run(5)
+    finally:
+        dm.close()
+    check_stages(res, model, 5)
+
+
+def test_persistent_full_step(cuda):
+    """The 28-layer Qwen3-shaped step at position 1023 (cache 1024 rows) in
+    both forms: bit-identical buffers, and the last layer's stages against
+    the oracle."""
+    import torch
+    pos = 1023
+    model = gen.decode_model(gen.QWEN3_DIMS, cache_rows=1024, seed=23)
+    say("persistent, full 28-layer step, pos 1023")
+    try:
+        nodes, pers, extra = run_both(model, cuda, pos, logits=False)
+    finally:
+        torch.cuda.empty_cache()
+    assert_same(nodes, pers, "node form against persistent form")
+    assert_same(pers, extra["kernel"], "kernel launch")
+    check_stages(pers, model, pos)
+    check_untouched(pers, model, pos)
+
+
+def test_persistent_refuses_unstaged_shapes(cuda):
+    """Widths the staged tiles do not take (inter 96) or wider than 3072:
+    Q8_ERR_SHAPE for the persistent form; the node form still builds."""
+    for dims in (dict(n_layers=1, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128,
+                      inter=96, vocab=100, eps=1e-6, theta=1e6),
+                 dict(n_layers=1, hidden=4096, n_heads=4, n_kv_heads=2, head_dim=128,
+                      inter=128, vocab=100, eps=1e-6, theta=1e6)):
+        model = gen.decode_model(dims, cache_rows=64, seed=1)
+        with pytest.raises(q8.Q8Error, match="shape"):
+            DeviceModel(model, cuda, form=q8.Q8_DECODE_PERSISTENT)
+        DeviceModel(model, cuda).close()
