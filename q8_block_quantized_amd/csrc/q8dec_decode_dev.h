@@ -28,20 +28,48 @@ __device__ __forceinline__ float ld_dev(const float *p) {
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Cross-lane steps without LDS: DPP permutations within rows of 16 lanes
+// cost a cycle or two, where a __shfl_xor (ds_bpermute) waits for an LDS
+// round trip, and v_readlane moves a lane's value to a scalar register.
+// Every lane of the wave must be active.  A DPP step combines a lane with
+// its partner in the same operand order on both sides (a + b, not b + a),
+// so the lanes of a row end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lanef(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over each row of 16 lanes, in every lane of the row: pairs, quads,
+// half-rows, rows.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);  // row_half_mirror
+  v += dppf<0x140>(v);  // row_mirror
   return v;
+}
+
+// Sum over the wave (the row sums, then rows (0 + 1) + (2 + 3)), the same
+// value in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
 }
 
 __device__ __forceinline__ float wave_maxf(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
 }
 
 // Sum over the 256 threads, the same value returned to every thread, in a
-// fixed order (butterfly in each wave, then the four wave sums pairwise).
+// fixed order (wave_sum in each wave, then the four wave sums pairwise).
 // red: 4 floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
@@ -198,11 +226,6 @@ constexpr int CH = kAttnChunk;
 static_assert(HD == 128 && CH == 64, "the lane mappings below assume these");
 
 // Sum over the 16 lanes of each 16-lane row.
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 16);
-  return v;
-}
 
 __device__ __forceinline__ void load8(const float *p, float (&d)[8]) {
   const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
@@ -303,7 +326,7 @@ struct AttnLds {
   float vn[HD];         // this token's value
   float sc[G][CH];      // scores, then weights
   float ml[G][2];       // chunk maximum and sum
-  float red[4][G][HD];  // per-wave value sums, then the merge's state
+  alignas(16) float red[16][G][HD];  // value sums per 16-lane row, then the merge's state
   uint32_t flag;
 };
 
@@ -364,6 +387,18 @@ __device__ __forceinline__ void attention_block(const AttnArgs &a, int blk, Attn
       load8(a.vc + off, vr[ps]);
     }
   }
+  // the norm weights and the rotation do not depend on the step's values:
+  // read and computed while the barrier completes
+  const float wq0 = a.q_norm[lane], wq1 = a.q_norm[lane + 64];
+  const float wk0 = a.k_norm[lane], wk1 = a.k_norm[lane + 64];
+  float cs, sn;
+  if (COH) {  // the rotation of this position (as the step's first node computes it)
+    const float ang = (float)pos * a.freq[lane];
+    sincosf(ang, &sn, &cs);
+  } else {
+    cs = a.rope[2 * lane];
+    sn = a.rope[2 * lane + 1];
+  }
   wait();  // everything below reads this step's values
   // Vectors: wave w takes vectors w and w + 4 of the G queries, the key (G)
   // and the value (G + 1); lane l holds elements l and l + 64 (RoPE pair l).
@@ -379,16 +414,6 @@ __device__ __forceinline__ void attention_block(const AttnArgs &a, int blk, Attn
       x0[j] = src[lane];
       x1[j] = src[lane + 64];
     }
-  }
-  const float wq0 = a.q_norm[lane], wq1 = a.q_norm[lane + 64];
-  const float wk0 = a.k_norm[lane], wk1 = a.k_norm[lane + 64];
-  float cs, sn;
-  if (COH) {  // the rotation of this position (as the step's first node computes it)
-    const float ang = (float)pos * a.freq[lane];
-    sincosf(ang, &sn, &cs);
-  } else {
-    cs = a.rope[2 * lane];
-    sn = a.rope[2 * lane + 1];
   }
 
   // QK-norm and RoPE of the queries and the key; the value as it is.  The
@@ -477,20 +502,17 @@ __device__ __forceinline__ void attention_block(const AttnArgs &a, int blk, Attn
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[i] += e * vr[ps][i];
     }
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      acc[i] += __shfl_xor(acc[i], 16, 64);
-      acc[i] += __shfl_xor(acc[i], 32, 64);
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) red[wave][h][8 * sub + i] = acc[i];
-    }
+    *(float4 *)&red[slot][h][8 * sub] = float4{acc[0], acc[1], acc[2], acc[3]};
+    *(float4 *)&red[slot][h][8 * sub + 4] = float4{acc[4], acc[5], acc[6], acc[7]};
   }
   __syncthreads();
   for (int t = (int)threadIdx.x; t < G * HD; t += kThreads) {
     const int h = t / HD, d = t % HD;
-    const float s = (red[0][h][d] + red[1][h][d]) + (red[2][h][d] + red[3][h][d]);
+    float q[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+      q[k] = (red[4 * k][h][d] + red[4 * k + 1][h][d]) + (red[4 * k + 2][h][d] + red[4 * k + 3][h][d]);
+    const float s = (q[0] + q[1]) + (q[2] + q[3]);
     float *p = a.part + ((size_t)(g * G + h) * a.chunks + c) * kAttnPart;
     st_dev(p + 4 + d, s);
     if (d == 0) {

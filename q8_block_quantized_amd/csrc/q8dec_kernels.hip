@@ -951,9 +951,12 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
 }
 
 // Registers that carry the next tile's weights (and x, when the next tile
-// belongs to another matvec) while the current tile is computed.
-template <int XC, int CH>
+// belongs to another matvec) while the current tile is computed.  The
+// weights are spread over the first NL threads (load_w, store_w; the other
+// loaders use all kWG).
+template <int XC, int CH, int NL = kWG>
 struct Prefetch {
+  static_assert(NL % 64 == 0 && NL <= kWG, "whole waves load");
   u32x4 w[CH];
   f32x4 x[XC];
 
@@ -961,19 +964,21 @@ struct Prefetch {
   // Every chunk is loaded (offsets past the end repeat the last chunk), so
   // the loads are straight-line code the compiler can count.
   __device__ __forceinline__ void load_w(const uint8_t *base, int32_t bytes) {
+    if (NL < kWG && (int)threadIdx.x >= NL) return;  // wave-uniform
     const __attribute__((address_space(1))) uint8_t *b = gp(base);
 #pragma unroll
     for (int j = 0; j < CH; j++) {
-      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
+      int32_t off = (j * NL + (int32_t)threadIdx.x) * 16;
       off = off < bytes - 16 ? off : bytes - 16;
       w[j] = __builtin_nontemporal_load(
           (const __attribute__((address_space(1))) u32x4 *)(b + off));
     }
   }
   __device__ __forceinline__ void store_w(uint32_t *tl, int32_t bytes) const {
+    if (NL < kWG && (int)threadIdx.x >= NL) return;
 #pragma unroll
     for (int j = 0; j < CH; j++) {
-      int32_t off = (j * kWG + (int32_t)threadIdx.x) * 16;
+      int32_t off = (j * NL + (int32_t)threadIdx.x) * 16;
       off = off < bytes - 16 ? off : bytes - 16;  // repeats write equal data
       *(u32x4 *)((uint8_t *)tl + off) = w[j];
     }
@@ -982,7 +987,7 @@ struct Prefetch {
   // lie `pitch` bytes apart in memory (a column slice of a wider matrix),
   // packed in the registers as load_w packs contiguous rows.
   __device__ __forceinline__ void load_w_strided(const uint8_t *base, int32_t bytes,
-                                                 int32_t rb, int32_t pitch) {
+                                                 int32_t rb, int32_t pitch) {  // NL = kWG only
     const __attribute__((address_space(1))) uint8_t *b = gp(base);
     const int32_t cpr = rb >> 4;  // chunks per row
     // chunk c of row c / cpr: c < 2^12 and c / cpr is at least 1 / (2 cpr)
@@ -1002,7 +1007,7 @@ struct Prefetch {
   // Same, with kMfmaRowPad bytes after every row of `pitch` bytes (a
   // multiple of 16, so no chunk straddles two rows).
   __device__ __forceinline__ void store_w_rows(uint32_t *tl, int32_t bytes,
-                                               int32_t pitch) const {
+                                               int32_t pitch) const {  // NL = kWG only
     const int32_t cpr = pitch >> 4;  // chunks per row
     // chunk c of row c / cpr: c < 2^12 and c / cpr is at least 1 / (2 cpr)
     // from an integer, far above the rounding of the product
@@ -1283,7 +1288,8 @@ template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src,
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr, Wait wait = Wait()) {
-  static_assert(!COH || DEC, "the persistent decode step: the decode variant");
+  static_assert(!COH || (DEC && M1 && !ANY && !I8X && !STRIDED),
+                "the persistent decode step: staged m = 1 tiles of the decode variant");
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
   constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
@@ -1305,7 +1311,13 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     wait();
     return;
   }
-  Prefetch<XC, CH> pf;
+  // The persistent step leaves the last wave's registers free of weight
+  // loads: that wave arrives at and polls the grid barrier, and vector loads
+  // return in issue order, so a poll behind the next phase's tile would
+  // learn of the release only once the tile had arrived.
+  constexpr int NL = COH ? kWG - 64 : kWG;
+  constexpr int CHL = COH ? (kTileMaxBytes + 16 * NL - 1) / (16 * NL) : CH;
+  Prefetch<XC, CHL, NL> pf;
   // The job of tile tn, a later tile than `from`'s: the same matvec, or one
   // found in the table.
   auto job_after = [&](const Job &from, int32_t tn) {
@@ -1817,10 +1829,13 @@ __device__ __forceinline__ void st_dev_u32(uint32_t *p, uint32_t v) {
 // A wait at the grid barrier gives up after this many ticks of the 100 MHz
 // clock (200 ms; a whole decode step takes about 1 ms).
 constexpr uint64_t kBarrierSpinTicks = 20000000ull;
+// The thread that arrives at and polls the barrier: the first of the last
+// wave, which requests no weights (run_tiles with COH).
+constexpr uint32_t kBarrierThread = kWG - 64;
 
 // This workgroup's arrival at the grid barrier that releases generation
 // `target`.  Every wave first waits until its stores are complete (the
-// values it hands on travel with device-scope stores), then thread 0 counts
+// values it hands on travel with device-scope stores), then kBarrierThread counts
 // the workgroup into its team (workgroup b in team b % 32, its counter in
 // its own line); the team's last arrival counts the team in, and the last
 // team's arrival writes `target` into every team's release line.  The
@@ -1831,7 +1846,7 @@ constexpr uint64_t kBarrierSpinTicks = 20000000ull;
 __device__ __forceinline__ void grid_arrive(GridBarrier *b, uint32_t target) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == kBarrierThread) {
     const uint32_t G = gridDim.x, T = kGridTeams, j = blockIdx.x % T;
     const uint32_t size = (G - j + T - 1) / T, nteams = G < T ? G : T;
     const uint32_t prev = __hip_atomic_fetch_add(&b->team[j][0], 1u, __ATOMIC_RELAXED,
@@ -1845,12 +1860,12 @@ __device__ __forceinline__ void grid_arrive(GridBarrier *b, uint32_t target) {
   }
 }
 
-// Waits (thread 0 polls its team's release line) until `target` is
+// Waits (kBarrierThread polls its team's release line) until `target` is
 // released.  False in every thread once the barrier has failed: this wait
 // ran past kBarrierSpinTicks (it then marks the failure and stores -2 as
 // the step's token) or another workgroup's did.  flag: one word of LDS.
 __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint32_t *flag) {
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == kBarrierThread) {
     uint32_t ok = 1u;
     uint32_t *line = &b->gen[blockIdx.x % kGridTeams][0];
     const uint64_t start = __builtin_amdgcn_s_memrealtime();
