@@ -280,6 +280,7 @@ struct SegmentLaunch {
   int kind = kStepNode;
   const q8::Epilogue *epi = nullptr;
   const q8::Prologue *pro = nullptr;
+  const q8::PairOut *pair = nullptr;  // a paired launch's second matrix and outputs
   bool dec = false;  // the decode step's kernel variant
   q8::AttnArgs attn{};
   const float *nx = nullptr, *nw = nullptr;
@@ -304,7 +305,7 @@ hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
     return q8::launch_step_start(L.nx, L.nw, L.nout, L.ncopy, L.ndim, L.neps, L.npos,
                                  L.nfreq, L.rope_out, s);
   return q8::launch_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
-                         L.all_staged, s, i8x, L.epi, L.pro, L.dec);
+                         L.all_staged, s, i8x, L.epi, L.pro, L.dec, L.pair);
 }
 
 struct q8_step_graph {
@@ -373,7 +374,10 @@ namespace q8 {
 // workgroups with contiguous tile ranges of about equal weight bytes, and
 // for every argmax descriptor the arrivals each argmax team waits for.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
-              int group_size, StepPlan &plan, bool i8x, bool dec, int grid_cap) {
+              int group_size, StepPlan &plan, bool i8x, bool dec, int grid_cap,
+              uint32_t paired_mask) {
+  auto paired = [&](int32_t i) { return i < 32 && ((paired_mask >> i) & 1u); };
+  if (paired_mask && (m != 1 || i8x || count > 32)) return Q8_ERR_SHAPE;
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
   plan.i8x = i8x;
@@ -390,6 +394,10 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     t.n = d.n;
     t.p = d.p;
     t.rows_per_tile = step_rows_per_tile(d.n, m, i8x);
+    if (paired(i)) {
+      if (!step_all_staged(1, d.n, false)) return Q8_ERR_SHAPE;
+      t.rows_per_tile = t.rows_per_tile / 2 > 0 ? t.rows_per_tile / 2 : 1;
+    }
     t.tile_begin = (int32_t)tiles;
     tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
     if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
@@ -435,7 +443,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
       tiles = 0;
       for (int32_t i = 0; i < count; i++) {
         StepDesc &t = plan.descs[i];
-        if (t.rows_per_tile > kStepMinRows) {
+        if (t.rows_per_tile > (paired(i) ? kStepMinRows / 2 : kStepMinRows)) {
           t.rows_per_tile >>= 1;
           changed = true;
         }
@@ -460,7 +468,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   std::vector<int64_t> pre((size_t)ntiles + 1, 0);
   for (int32_t i = 0, t = 0; i < count; i++) {
     const StepDesc &d = plan.descs[i];
-    const int64_t pitch = (int64_t)(d.n / 32) * 34;
+    const int64_t pitch = (int64_t)(d.n / 32) * 34 * (paired(i) ? 2 : 1);
     for (int32_t r0 = 0; r0 < d.p; r0 += d.rows_per_tile, t++) {
       const int32_t rows = d.p - r0 < d.rows_per_tile ? d.p - r0 : d.rows_per_tile;
       pre[t + 1] = pre[t] + rows * pitch + 1;  // +1: zero-width tiles still count
@@ -989,6 +997,16 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     d.p = p;
     return d;
   };
+  // The element-wise steps between matvecs run as prologues when every
+  // launch is all staged and the vectors fit the staged x: each workgroup of
+  // the consuming launch computes its x (the residual adds and norms) while
+  // its first tile loads, and the gate/up launch computes the SwiGLU of the
+  // rows it holds (paired tiles: the same rows of both matrices).
+  // Otherwise they run as epilogues, by the last workgroup of the producing
+  // launch, whose outputs then take device-scope stores.
+  const bool pro_path = H <= q8::kProMaxN && I <= q8::kProMaxN &&
+                        q8::step_all_staged(1, H, false) && q8::step_all_staged(1, QW, false) &&
+                        q8::step_all_staged(1, I, false);
   std::vector<std::vector<q8_matvec_desc>> lv;
   for (int32_t l = 0; l < M.n_layers; l++) {
     const q8_decode_layer &L = M.layers[l];
@@ -996,24 +1014,27 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     lv.push_back({mv(L.wq, b.xn, b.q, nullptr, H, QW), mv(L.wk, b.xn, b.k, nullptr, H, KVW),
                   mv(L.wv, b.xn, b.v, nullptr, H, KVW)});
     lv.push_back({mv(L.wo, b.attn, b.attn_out, nullptr, QW, H)});
-    lv.push_back({mv(L.w_gate, b.xn2, b.gate, nullptr, H, I), mv(L.w_up, b.xn2, b.up, nullptr, H, I)});
+    if (pro_path)  // one paired descriptor (w2, y2 and h are filled after planning)
+      lv.push_back({mv(L.w_gate, b.xn2, b.gate, nullptr, H, I)});
+    else
+      lv.push_back({mv(L.w_gate, b.xn2, b.gate, nullptr, H, I), mv(L.w_up, b.xn2, b.up, nullptr, H, I)});
     lv.push_back({mv(L.w_down, b.h, b.ffn_out, nullptr, I, H)});
   }
   lv.push_back({mv(M.lm_head, B.xf, B.logits, B.token, H, M.vocab)});
+  auto paired_level = [&](size_t i) { return pro_path && i + 1 < lv.size() && i % 4 == 2; };
+  // the paired gate/up descriptor of level i (after planning)
+  auto pair_up = [&](size_t i, q8::StepPlan &pl) {
+    if (paired_level(i)) pl.descs[0].flags |= q8::kDescPairedSilu;
+  };
   std::vector<q8::StepPlan> plans(lv.size());
   for (size_t i = 0; i < lv.size(); i++) {
     st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
-                       plans[i], false, true);
+                       plans[i], false, true, 0, paired_level(i) ? 1u : 0u);
     if (st) return st;
+    pair_up(i, plans[i]);
   }
-  // The element-wise steps between matvecs run as prologues when every
-  // launch is all staged and the vectors fit the staged x: each workgroup of
-  // the consuming launch computes its x (the residual adds and norms, the
-  // SwiGLU) while its first tile loads.  Otherwise they run as epilogues, by
-  // the last workgroup of the producing launch, whose outputs then take
-  // device-scope stores.
-  bool pro_path = H <= q8::kProMaxN && I <= q8::kProMaxN;
-  for (const auto &pl : plans) pro_path = pro_path && pl.all_staged;
+  for (const auto &pl : plans)
+    if (pro_path && !pl.all_staged) return Q8_ERR_SHAPE;  // (the shapes above are staged)
   // The persistent form: one launch of as many workgroups as are resident
   // at once with LDS for the widest staged tile and x and for an attention
   // block; every level is planned on that grid, and every output but the
@@ -1028,8 +1049,9 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     if (pgrid < 1) return Q8_ERR_SHAPE;
     for (size_t i = 0; i < lv.size(); i++) {
       st = q8::plan_step(lv[i].data(), (int32_t)lv[i].size(), 1, dev, q8::kStepGroupSize,
-                         plans[i], false, true, pgrid);
+                         plans[i], false, true, pgrid, paired_level(i) ? 1u : 0u);
       if (st) return st;
+      pair_up(i, plans[i]);
       if (i + 1 < lv.size())
         for (auto &d : plans[i].descs) d.flags |= q8::kDescDeviceOut;
     }
@@ -1064,6 +1086,7 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   const size_t o_aarr = take(sizeof(q8::ArgmaxSlot) * (size_t)M.n_kv_heads);
   const size_t o_epi = take(sizeof(q8::Epilogue) * 3 * (size_t)M.n_layers);
   const size_t o_pro = take(sizeof(q8::Prologue) * (3 * (size_t)M.n_layers + 1));
+  const size_t o_pair = take(sizeof(q8::PairOut) * (size_t)M.n_layers);
   const size_t o_freq = take(sizeof(float) * q8::kAttnHeadDim / 2);
   const size_t o_rope = take(sizeof(float) * q8::kAttnHeadDim);
   const size_t o_part = take(sizeof(float) * (size_t)M.n_heads * chunks * q8::kAttnPart);
@@ -1176,6 +1199,20 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
   }
   if (e == hipSuccess)
     e = hipMemcpy(pros, hp.data(), hp.size() * sizeof(q8::Prologue), hipMemcpyHostToDevice);
+  // each layer's paired gate/up launch: the up matrix, and where up and
+  // h = silu(gate) * up go (prologue form)
+  q8::PairOut *pairs = (q8::PairOut *)(ws + o_pair);
+  {
+    std::vector<q8::PairOut> hq(M.n_layers);
+    for (int32_t l = 0; l < M.n_layers; l++) {
+      std::memset(&hq[l], 0, sizeof(q8::PairOut));
+      hq[l].w2 = (const uint8_t *)M.layers[l].w_up;
+      hq[l].y2 = lb[l].up;
+      hq[l].h = lb[l].h;
+    }
+    if (e == hipSuccess)
+      e = hipMemcpy(pairs, hq.data(), hq.size() * sizeof(q8::PairOut), hipMemcpyHostToDevice);
+  }
   for (size_t i = 0; i < plans.size() && e == hipSuccess; i++) {
     e = hipMemcpy(ws + o_tab[i], plans[i].descs.data(),
                   plans[i].descs.size() * sizeof(q8::StepDesc), hipMemcpyHostToDevice);
@@ -1214,8 +1251,9 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     std::vector<q8::AttnArgs> ha(M.n_layers);
     std::vector<q8::DecPhase> ph;
     const q8::AttnArgs *dattn = (const q8::AttnArgs *)(ws + o_attn);
-    auto mphase = [&](size_t i, const q8::Prologue *pro) {
+    auto mphase = [&](size_t i, const q8::Prologue *pro, const q8::PairOut *pair = nullptr) {
       q8::DecPhase d{};
+      d.pair = pair;
       d.kind = q8::kPhaseMatvec;
       d.count = (int32_t)plans[i].descs.size();
       d.group_size = plans[i].group_size;
@@ -1233,8 +1271,8 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
       d.attn = dattn + l;
       ph.push_back(d);
       mphase(4 * (size_t)l + 1, nullptr);
-      mphase(4 * (size_t)l + 2, &pros[3 * (size_t)l]);
-      mphase(4 * (size_t)l + 3, &pros[3 * (size_t)l + 1]);
+      mphase(4 * (size_t)l + 2, &pros[3 * (size_t)l], pairs + l);
+      mphase(4 * (size_t)l + 3, nullptr);  // x = h, from the gate/up phase
     }
     mphase(plans.size() - 1, &pros[3 * (size_t)M.n_layers - 1]);
     e = ph.size() == (size_t)nphases ? hipSuccess : hipErrorInvalidValue;
@@ -1270,12 +1308,14 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
       return run_segment(g->launches[0], 1, false, cs);
     });
   }
-  auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Prologue *pro = nullptr) {
+  auto step_node = [&](size_t i, const q8::Epilogue *epi, const q8::Prologue *pro = nullptr,
+                       const q8::PairOut *pair = nullptr) {
     const q8::StepPlan &pl = plans[i];
     SegmentLaunch L{(const q8::StepDesc *)(ws + o_tab[i]), (const q8::WgGroup *)(ws + o_grp[i]),
                     (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged};
     L.epi = epi;
     L.pro = pro;
+    L.pair = pair;
     L.dec = true;
     g->launches.push_back(L);
   };
@@ -1303,8 +1343,8 @@ int build_decode(const q8_decode_model *md, const q8_decode_buffers *bf, int32_t
     g->launches.push_back(A);
     if (pro_path) {
       step_node(4 * (size_t)l + 1, nullptr);
-      step_node(4 * (size_t)l + 2, nullptr, &pros[3 * (size_t)l]);
-      step_node(4 * (size_t)l + 3, nullptr, &pros[3 * (size_t)l + 1]);
+      step_node(4 * (size_t)l + 2, nullptr, &pros[3 * (size_t)l], pairs + l);
+      step_node(4 * (size_t)l + 3, nullptr);  // x = h, stored by the gate/up node
     } else {
       step_node(4 * (size_t)l + 1, &epis[3 * (size_t)l]);
       step_node(4 * (size_t)l + 2, &epis[3 * (size_t)l + 1]);

@@ -54,12 +54,12 @@ struct StepDesc {
   const uint8_t *w;
   const float *x;
   float *y;
-  int32_t *idx;
-  ArgmaxSlot *slot;
+  int32_t *idx;           // fused argmax: the index output, or NULL
+  ArgmaxSlot *slot;       // fused argmax: its arrival slot
   int32_t n, p;
   int32_t tile_begin;     // first tile of this matvec in the launch
-  int32_t rows_per_tile;
-  int32_t flags;          // kDescDeviceOut: outputs stored at device scope
+  int32_t rows_per_tile;  // (paired: rows of each matrix)
+  int32_t flags;          // kDescDeviceOut, kDescPairedSilu; split-K pitch
   int32_t tile_end;       // one past its last tile: tile_begin + ceil(p / rows_per_tile)
 };
 // y is stored with device-scope stores, so that the launch's epilogue (m = 1)
@@ -73,6 +73,20 @@ __host__ __device__ inline int32_t desc_pitch16(int32_t flags) {
   return (flags >> kDescPitchShift) & 0xFFFF;
 }
 static_assert(sizeof(StepDesc) == 64, "descriptor layout");
+// Paired (the decode step's gate and up projections, prologue form): a tile
+// holds rows r0 .. r0 + rows of w and the same rows of the launch's
+// PairOut::w2, both n wide over the same x; the tile's workgroup stores
+// y[r] = w[r]·x, y2[r] = w2[r]·x and h[r] = silu_hadamard = y[r] / (1 +
+// e^-y[r]) · y2[r].  At most one paired descriptor per launch; no argmax.
+constexpr int32_t kDescPairedSilu = 2;
+constexpr int kPairMaxRows = 32;  // a paired tile's rows of each matrix (plans give <= 32)
+struct PairOut {
+  const uint8_t *w2;  // the second matrix
+  float *y2;          // its outputs
+  float *h;           // silu(y) * y2
+  int64_t pad;
+};
+static_assert(sizeof(PairOut) == 32, "pair layout");
 
 // Workgroups g in [first, first + size) of a persistent step share the
 // contiguous tile range [t0, t1), interleaved: workgroup first + j takes
@@ -139,7 +153,7 @@ hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x = false,
                        const Epilogue *epi = nullptr, const Prologue *pro = nullptr,
-                       bool dec = false);
+                       bool dec = false, const PairOut *pair = nullptr);
 
 // True when a matvec of width n with m rows takes the staged path (the step
 // can then use the kernel variant without the other paths).
@@ -283,8 +297,10 @@ struct DecPhase {
   const WgGroup *groups;
   const Prologue *pro;   // or NULL
   const AttnArgs *attn;  // attention
+  const PairOut *pair;   // matvec: the paired descriptor's, or NULL
+  int64_t pad;
 };
-static_assert(sizeof(DecPhase) == 48, "phase layout");
+static_assert(sizeof(DecPhase) == 64, "phase layout");
 
 // Grid barrier state, zeroed once (the graph's workspace): team j's arrival
 // counter and released generation each in their own 128-byte line.  The
@@ -318,8 +334,11 @@ struct q8_matvec_desc;
 namespace q8 {
 // Plans a persistent step (q8dec_api.hip) with groups of `group_size`.
 // grid_cap > 0: the launch's grid (the persistent decode step's) instead of
-// the step kernel's resident capacity.
+// the step kernel's resident capacity.  paired_mask bit i: descriptor i is
+// paired (kDescPairedSilu, m = 1 staged only): its tiles hold rows of two
+// matrices, so they are half as tall and weigh twice the bytes; the caller
+// fills w2, y2 and h and sets the flag.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
               int group_size, StepPlan &plan, bool i8x = false, bool dec = false,
-              int grid_cap = 0);
+              int grid_cap = 0, uint32_t paired_mask = 0);
 }  // namespace q8

@@ -580,7 +580,8 @@ template <int NBL, bool DEVY>
 __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
                                           int32_t rows, const float *xs,
                                           float *y, int32_t r0, bool keys,
-                                          unsigned long long &best) {
+                                          unsigned long long &best,
+                                          float *stash = nullptr) {
   const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
   const int wave = threadIdx.x >> 6;
   const int32_t pitch = bpr * 34;
@@ -627,6 +628,7 @@ __device__ __forceinline__ void staged_m1(const uint32_t *tl, int32_t bpr,
     acc = half_wave_sum(acc);
     const bool mine = k == 31 && rr < rows;
     if (mine && y) store_y(&y[r0 + rr], acc, DEVY);
+    if (mine && stash) stash[rr] = acc;  // a paired tile's sums (LDS)
     const bool better = mine & ((acc > bv) | ((bv != bv) & (acc == acc)));  // no branches
     bv = better ? acc : bv;
     br = better ? rr : br;
@@ -974,6 +976,21 @@ struct Prefetch {
           (const __attribute__((address_space(1))) u32x4 *)(b + off));
     }
   }
+  // `bytes` bytes at a then `bytes` bytes at b (a paired tile: the same
+  // rows of two matrices), packed as load_w packs 2 * bytes contiguous ones.
+  __device__ __forceinline__ void load_w_pair(const uint8_t *a, const uint8_t *b,
+                                              int32_t bytes) {
+    if (NL < kWG && (int)threadIdx.x >= NL) return;
+    const __attribute__((address_space(1))) uint8_t *pa = gp(a), *pb = gp(b);
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      int32_t off = (j * NL + (int32_t)threadIdx.x) * 16;
+      off = off < 2 * bytes - 16 ? off : 2 * bytes - 16;
+      const __attribute__((address_space(1))) uint8_t *src =
+          off < bytes ? pa + off : pb + (off - bytes);
+      w[j] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)src);
+    }
+  }
   __device__ __forceinline__ void store_w(uint32_t *tl, int32_t bytes) const {
     if (NL < kWG && (int)threadIdx.x >= NL) return;
 #pragma unroll
@@ -1287,7 +1304,8 @@ template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src,
           bool STRIDED = false, bool COH = false, class Wait = NoWait>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
-                          float *lds, const Prologue *pro = nullptr, Wait wait = Wait()) {
+                          float *lds, const Prologue *pro = nullptr, Wait wait = Wait(),
+                          const PairOut *pair = nullptr) {
   static_assert(!COH || (DEC && M1 && !ANY && !I8X && !STRIDED),
                 "the persistent decode step: staged m = 1 tiles of the decode variant");
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
@@ -1330,11 +1348,19 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   bool more = t + stride < end;
   Job nxt = more ? job_after(cur, t + stride) : cur;
   ProRegs prr;
+  // a paired tile's row sums (DEC only): up to kPairMaxRows rows of each matrix
+  float *pair_sums = nullptr;
+  if constexpr (DEC) {
+    __shared__ float pair_lds[2 * kPairMaxRows];
+    pair_sums = pair_lds;
+  }
   // the prologue's descriptor, read before the tiles' loads (and, in the
   // persistent step, before the barrier): its fields address the loads
   Prologue pr{};
+  PairOut po{};  // the launch's paired matrix and outputs (DEC), read before any tile
   if constexpr (DEC) {
     if (pro) pr = *pro;
+    if (pair) po = *pair;
   }
   if constexpr (DEC && !COH) {
     if (pro) pro_load(pr, prr);  // before the tile's loads: see pro_load
@@ -1342,7 +1368,9 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   // a tile's weight bytes: whole rows, or (STRIDED) rows of a column slice
   auto load_tile = [&](const Job &j) {
     const int32_t rb = (j.d.n >> 5) * 34;
-    if (STRIDED)
+    if (DEC && (j.d.flags & kDescPairedSilu))
+      pf.load_w_pair(j.d.w + (uint64_t)j.r0 * rb, po.w2 + (uint64_t)j.r0 * rb, j.rows * rb);
+    else if (STRIDED)
       pf.load_w_strided(j.d.w + (uint64_t)j.r0 * desc_pitch16(j.d.flags) * 16u, j.rows * rb, rb,
                         desc_pitch16(j.d.flags) * 16);
     else
@@ -1379,7 +1407,10 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const bool x_changed = cur.d.x != xptr || cur.d.n != xn;
     const bool new_x = x_in_lds(cur) && x_changed;
     __syncthreads();  // the previous tile's readers of LDS are done
-    if (staged(cur)) pf.store_w(tl, cur.rows * bpr * 34);
+    // a paired tile holds its rows of both matrices, one after the other
+    const bool pair = DEC && (cur.d.flags & kDescPairedSilu);
+    const int32_t trows = pair ? 2 * cur.rows : cur.rows;
+    if (staged(cur)) pf.store_w(tl, trows * bpr * 34);
     else if (mfma(cur)) pf.store_w_rows(tl, cur.rows * bpr * 34, bpr * 34);
     if (new_x) {
       if (I8X) pf.store_xq(xq, xd, m, cur.d.n);
@@ -1418,6 +1449,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const Job nxt2 = more2 ? job_after(nxt, tn2) : nxt;
     const bool keys = cur.d.idx != nullptr;
     const bool devy = DEC && (cur.d.flags & kDescDeviceOut);
+    float *const yout = pair ? nullptr : cur.d.y;
     if (I8X) {
       const int nbl = NBLS ? NBLS : nbl_of(cur.d.n);
       if (M1) {
@@ -1431,14 +1463,28 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       }
     } else if (staged(cur)) {
       const int nbl = NBLS ? NBLS : nbl_of(cur.d.n);
+      float *const stash = pair ? pair_sums : nullptr;
       if (devy) {  // outputs read by the launch's epilogue (decode step levels)
-        if (nbl == 1) staged_m1<1, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else if (nbl == 2) staged_m1<2, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else staged_m1<3, true>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        if (nbl == 1) staged_m1<1, true>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
+        else if (nbl == 2) staged_m1<2, true>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
+        else staged_m1<3, true>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
       } else {
-        if (nbl == 1) staged_m1<1, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else if (nbl == 2) staged_m1<2, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
-        else staged_m1<3, false>(tl, bpr, cur.rows, xs, cur.d.y, cur.r0, keys, best[0]);
+        if (nbl == 1) staged_m1<1, false>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
+        else if (nbl == 2) staged_m1<2, false>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
+        else staged_m1<3, false>(tl, bpr, trows, xs, yout, cur.r0, keys, best[0], stash);
+      }
+      if constexpr (DEC) {
+        if (pair) {  // silu_hadamard of the tile's rows, from both matrices' sums
+          __syncthreads();
+          const int32_t i = (int32_t)threadIdx.x;
+          if (i < cur.rows) {
+            const float gv = pair_sums[i], uv = pair_sums[cur.rows + i];
+            const float hv = gv / (1.0f + expf(-gv)) * uv;
+            store_y(&cur.d.y[cur.r0 + i], gv, devy);
+            store_y(&po.y2[cur.r0 + i], uv, devy);
+            store_y(&po.h[cur.r0 + i], hv, devy);
+          }
+        }
       }
     } else if (mfma(cur)) {
       if (bpr == 32)
@@ -1801,14 +1847,16 @@ template <bool M1, bool ANY, bool I8X, bool DEC>
 __global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
-            const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro) {
+            const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro,
+            const PairOut *__restrict__ pair) {
   static_assert(!DEC || (M1 && !I8X), "the decode variant is m = 1, binary32");
   extern __shared__ __attribute__((aligned(16))) float lds[];
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
   run_tiles<M1, ANY, I8X, !M1 && !I8X, 0, DEC>(src, g.t0 + group_slot(j, g.first, g.size),
-                                               g.t1, g.size, g.d0, m, lds, pro);
+                                               g.t1, g.size, g.d0, m, lds, pro, NoWait(),
+                                               pair);
   if constexpr (DEC) {
     if (epi) {
       __syncthreads();  // every wave is done with the tile buffer
@@ -1952,7 +2000,7 @@ decode_kernel(const DecPhase *__restrict__ phases, int32_t nphases,
         const int32_t j = b - g.first;
         run_tiles<true, false, false, false, 0, true, TableSrc, false, true>(
             src, g.t0 + group_slot(j, g.first, g.size), g.t1, g.size, g.d0, 1, lds, ph.pro,
-            wait);
+            wait, ph.pair);
       } else {
         wait();
       }
@@ -2201,15 +2249,16 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
 hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
                        int group_size, int m, int grid, size_t lds,
                        bool all_staged, hipStream_t s, bool i8x, const Epilogue *epi,
-                       const Prologue *pro, bool dec) {
-  // prologues and epilogues: the decode variant (m = 1, binary32), and a
-  // prologue only where every tile is staged
-  if ((epi || pro) && !dec) return hipErrorInvalidValue;
+                       const Prologue *pro, bool dec, const PairOut *pair) {
+  // prologues, epilogues and paired tiles: the decode variant (m = 1,
+  // binary32), and a prologue or a pair only where every tile is staged
+  if ((epi || pro || pair) && !dec) return hipErrorInvalidValue;
+  if (pair && !all_staged) return hipErrorInvalidValue;
   if (dec && (m != 1 || i8x)) return hipErrorInvalidValue;
   if (pro && !all_staged) return hipErrorInvalidValue;
 #define Q8_STEP(M1, ANY, I8X, DEC)                                                          \
   hipLaunchKernelGGL((step_kernel<M1, ANY, I8X, DEC>), dim3(grid), dim3(kWG), lds, s, descs, \
-                     count, groups, group_size, m, epi, pro)
+                     count, groups, group_size, m, epi, pro, pair)
   if (m > kMaxM) {
     if (i8x) return hipErrorInvalidValue;
     hipLaunchKernelGGL(wide_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,

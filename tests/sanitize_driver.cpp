@@ -111,10 +111,10 @@ static void refusals() {
 
 // Walks every workgroup's tiles of a plan one by one and checks the plan.
 static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int group_size,
-                       bool i8x, int grid_cap = 0) {
+                       bool i8x, int grid_cap = 0, uint32_t paired = 0) {
   q8::StepPlan plan;
   const int st = q8::plan_step(descs.data(), (int32_t)descs.size(), m, 0, group_size, plan, i8x,
-                               grid_cap > 0, grid_cap);
+                               grid_cap > 0 || paired, grid_cap, paired);
   CHECK(st == Q8_OK);
   if (st != Q8_OK) return;
   // descriptors: consecutive tile ranges covering every row
@@ -129,6 +129,13 @@ static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int grou
   }
   CHECK(plan.grid >= 1 && plan.grid <= ntiles);
   if (grid_cap > 0) CHECK(plan.grid <= grid_cap);
+  for (size_t i = 0; i < descs.size() && i < 32; i++)
+    if ((paired >> i) & 1u) {
+      const q8::StepDesc &t = plan.descs[i];
+      CHECK(t.rows_per_tile >= 1 && t.rows_per_tile <= q8::kPairMaxRows);
+      // both matrices' rows of a tile fit the staged tile buffer
+      CHECK(2 * t.rows_per_tile <= q8::step_rows_per_tile(t.n, 1, false));
+    }
   // groups: contiguous ranges that partition [0, ntiles); each workgroup's
   // tiles t0 + slot, + size, ... cover its group's range exactly once
   std::vector<int> owner(ntiles, -1);
@@ -205,6 +212,19 @@ static void planner() {
   for (const auto &ph : phases)
     for (int cap : {512, 513, 7, 1}) check_plan(ph, 1, q8::kStepGroupSize, false, cap);
   for (int cap : {512, 3}) check_plan(mixed, 1, 8, false, cap);
+  // paired gate/up descriptors (the decode step's prologue form): node form
+  // and persistent grids; a paired mask with m > 1 is refused
+  for (int cap : {0, 512, 7})
+    check_plan({mv(1024, 3072, false)}, 1, q8::kStepGroupSize, false, cap, 1u);
+  check_plan({mv(3072, 3072, false)}, 1, q8::kStepGroupSize, false, 512, 1u);
+  check_plan({mv(256, 512, false), mv(1024, 77, false)}, 1, 4, false, 0, 1u);
+  {
+    q8::StepPlan plan;
+    std::vector<q8_matvec_desc> one = {mv(1024, 3072, false)};
+    CHECK(q8::plan_step(one.data(), 1, 8, 0, 1, plan, false, true, 0, 1u) == Q8_ERR_SHAPE);
+    std::vector<q8_matvec_desc> odd = {mv(96, 30, false)};
+    CHECK(q8::plan_step(odd.data(), 1, 1, 0, 1, plan, false, true, 0, 1u) == Q8_ERR_SHAPE);
+  }
 }
 
 int main() {
