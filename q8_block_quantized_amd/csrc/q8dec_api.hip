@@ -232,7 +232,7 @@ int matvec_split(const void *w, const float *x, float *y, int32_t *idx, int32_t 
   q8::ArgmaxSlot *slot = nullptr;
   if ((st = stream_slot(dev, stream, &slot))) return st;
   float *part = nullptr;
-  if ((st = stream_part(dev, stream, (size_t)q8::split_slices(n, nullptr) * (size_t)p, &part)))
+  if ((st = stream_part(dev, stream, (size_t)q8::split_plan(1, n, p, nullptr) * (size_t)p, &part)))
     return st;
   hipError_t e = q8::launch_matvec_split((const uint8_t *)w, x, y, n, p, part,
                                          idx ? slot : nullptr, idx, stream);
@@ -563,7 +563,7 @@ int q8_matvec(const void *w, const float *x, float *y, int32_t n, int32_t p,
               void *stream) {
   int st = check_matvec(w, x, y, nullptr, 1, n, p, true);
   if (st) return st;
-  if (p > 0 && q8::split_shape_ok(1, n))
+  if (q8::split_plan(1, n, p, nullptr) > 1)
     return matvec_split(w, x, y, nullptr, n, p, (hipStream_t)stream);
   if ((st = ensure_device(nullptr))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, 1, n, p, nullptr,
@@ -575,7 +575,7 @@ int q8_matvec_batched(const void *w, const float *x, float *y, int32_t m,
                       int32_t n, int32_t p, void *stream) {
   int st = check_matvec(w, x, y, nullptr, m, n, p, true);
   if (st) return st;
-  if (p > 0 && q8::split_shape_ok(m, n))
+  if (q8::split_plan(m, n, p, nullptr) > 1)
     return matvec_split(w, x, y, nullptr, n, p, (hipStream_t)stream);
   if ((st = ensure_device(nullptr))) return st;
   hipError_t e = q8::launch_matvec((const uint8_t *)w, x, y, m, n, p, nullptr,
@@ -603,7 +603,7 @@ int q8_matvec_argmax(const void *w, const float *x, float *y_or_null,
   if (!idx) return Q8_ERR_NULL;
   int st = check_matvec(w, x, y_or_null, idx, m, n, p, false);
   if (st) return st;
-  if (q8::split_shape_ok(m, n))
+  if (q8::split_plan(m, n, p, nullptr) > 1)
     return matvec_split(w, x, y_or_null, idx, n, p, (hipStream_t)stream);
   int dev = 0;
   if ((st = ensure_device(&dev))) return st;

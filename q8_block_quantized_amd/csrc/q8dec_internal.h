@@ -128,6 +128,13 @@ bool i8x_shape_ok(int n);
 // the argmax taken over the sums.  Two launches on s.
 bool split_shape_ok(int m, int n);
 int split_slices(int n, int32_t *sb);
+// split_plan(m, n, p, &sb): the slice count of a split launch (>= 2, with
+// sb), or 0 for an unsplit one.  Only wide matrices split: a staged width
+// with few output rows (the rvllm page's K-split of a 960 x 320 matrix, "The
+// matmul pain story") was cut into slices too and measured 1.8-2.2x slower
+// on MI355X, since its unsplit launch is bound by one tile's latency, not by
+// idle compute units, and the split adds the summing launch.
+int split_plan(int m, int n, int p, int32_t *sb);
 hipError_t launch_matvec_split(const uint8_t *w, const float *x, float *y, int n, int p,
                                float *part, ArgmaxSlot *slot, int32_t *idx, hipStream_t s);
 

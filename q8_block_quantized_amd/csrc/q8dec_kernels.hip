@@ -2303,6 +2303,11 @@ int split_slices(int n, int32_t *sb) {
   return s;
 }
 
+int split_plan(int m, int n, int p, int32_t *sb) {
+  if (p < 1 || !split_shape_ok(m, n)) return 0;
+  return split_slices(n, sb);
+}
+
 namespace {
 template <int NBLS>
 int split_grid_cap(int dev) {
@@ -2317,9 +2322,9 @@ int split_grid_cap(int dev) {
 
 hipError_t launch_matvec_split(const uint8_t *w, const float *x, float *y, int n, int p,
                                float *part, ArgmaxSlot *slot, int32_t *idx, hipStream_t s) {
-  if (p <= 0 || !split_shape_ok(1, n)) return hipErrorInvalidValue;
   int32_t sb = 0;
-  const int32_t slices = split_slices(n, &sb);
+  const int32_t slices = split_plan(1, n, p, &sb);
+  if (slices < 2) return hipErrorInvalidValue;
   SliceSrc src{};
   src.base.w = w;
   src.base.x = x;
