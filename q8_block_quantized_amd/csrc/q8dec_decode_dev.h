@@ -71,6 +71,30 @@ __device__ __forceinline__ float wave_maxf(float v) {
 // Sum over the 256 threads, the same value returned to every thread, in a
 // fixed order (wave_sum in each wave, then the four wave sums pairwise).
 // red: 4 floats of LDS.
+// A workgroup barrier that orders LDS accesses only: every LDS write before
+// it is complete (lgkmcnt) before any wave passes it, and the compiler moves
+// no memory access across it.  __syncthreads() also waits for the wave's
+// vector memory requests (its fence counts them, as they may be LDS writes),
+// and with them for weight loads in flight that the code after the barrier
+// does not yet need.
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), as the builtin's operand
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// block_sum with LDS-only barriers: for callers whose values before and
+// after the sum are registers and LDS only.
+__device__ __forceinline__ float block_sum_lds(float v, float *red) {
+  v = wave_sum(v);
+  lds_barrier();  // earlier readers of red are done
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  lds_barrier();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   __syncthreads();  // earlier readers of red are done

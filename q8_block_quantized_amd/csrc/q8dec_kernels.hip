@@ -1219,7 +1219,7 @@ __device__ __forceinline__ void pro_finish(const Prologue &p, ProRegs &r, float 
 #pragma unroll
       for (int e = 0; e < 4; e++) ss += r.a[k][e] * r.a[k][e];
     }
-    ss = dec::block_sum(ss, red);
+    ss = dec::block_sum_lds(ss, red);  // (the tile's loads in flight are not waited for)
     inv = 1.0f / sqrtf(ss / (float)p.n + p.eps);
   }
 #pragma unroll
@@ -1945,9 +1945,12 @@ __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint3
     }
     *flag = ok;
   }
-  __syncthreads();
+  // LDS-only barriers: the weight loads the other waves issued before the
+  // wait are not waited for here (the code after the wait issues its own
+  // loads first)
+  dec::lds_barrier();
   const bool ok = *flag != 0u;
-  __syncthreads();  // the flag is rewritten by the next wait
+  dec::lds_barrier();  // the flag is rewritten by the next wait
   return ok;
 }
 
