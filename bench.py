@@ -291,6 +291,29 @@ def matvec_chain(torch, q8, dev, sets, copies: int = 240, reps: int = 10) -> dic
                     "launched back to back, HIP events"}
 
 
+def lm_head_chain(torch, q8, lm_w, lm_x, nodes: int = 40, reps: int = 10) -> dict:
+    """The fused lm_head as graph nodes: a chain graph of `nodes` lm_head
+    matvecs with their argmax, rotating the weight copies, launched back to
+    back; the time per node is the kernel's cost without host dispatch."""
+    dev = lm_x.device
+    idx = torch.full((nodes,), -1, dtype=torch.int32, device=dev)
+    descs = [dict(w=lm_w[c % len(lm_w)], x=lm_x, y=None, idx=idx[c:c + 1], n=1024, p=151936)
+             for c in range(nodes)]
+    g = q8.StepGraph(descs, 1, mode=q8.Q8_GRAPH_CHAIN)
+    assert g.info() == (nodes, 0)
+    t = event_time(torch, lambda k: g.launch(), reps, warmup=2)
+    got = idx.cpu().tolist()
+    g.close()
+    k = len(lm_w)
+    assert all(got[c] == got[c % k] >= 0 for c in range(nodes)), "lm_head chain tokens differ"
+    lb = alg_bytes(1024, 151936, 1, False, True)
+    per = t / nodes
+    return {"timing": f"HIP events around back-to-back launches of a chain graph of {nodes} "
+                      f"fused lm_head nodes ({k} weight copies rotated)",
+            "per_node_us": round(per * 1e6, 2), "GBps": round(lb / per / 1e9, 1),
+            "pct_of_peak": round(100 * lb / per / 1e9 / HBM_PEAK_GBS, 2), "alg_bytes": lb}
+
+
 def weight_bytes_of(n: int, p: int) -> int:
     return p * (n // 32) * 34
 
@@ -538,6 +561,7 @@ def only_workload(args, torch, q8, dev) -> int:
         t = event_time(torch, lambda k: calls[k % 4](), args.steps, args.warmup)
         b = alg_bytes(1024, 151936, 1, False, True)
         out.update(avg_us=round(t * 1e6, 2), GBps=round(b / t / 1e9, 1), alg_bytes=b)
+        out["graph"] = lm_head_chain(torch, q8, ws, x)
     elif args.only == "wide":
         m = 32
         sets32 = [StepSet(torch, dev, 0, 7000 + 1000 * j, m, False) for j in range(2)]
@@ -790,6 +814,7 @@ def main() -> int:
             "pct_of_peak": round(100 * lb / lt / 1e9 / HBM_PEAK_GBS, 2),
             "alg_bytes": lb,
         }
+        extra["lm_head_fused_graph"] = lm_head_chain(torch, q8, lm_w, lm_x)
         lm_y = torch.empty(151936, dtype=torch.float32, device=dev)
         plain = [c_call(q8, "q8_matvec", w.data_ptr(), lm_x.data_ptr(), lm_y.data_ptr(),
                         1024, 151936) for w in lm_w]
