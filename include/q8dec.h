@@ -208,7 +208,13 @@ typedef struct q8_step_graph q8_step_graph;
  *    buffer).
  *  Q8_GRAPH_PERSISTENT: one kernel node that walks a device-side table of
  *    all descriptors with no ordering between them (valid when no
- *    descriptor reads another's output).
+ *    descriptor reads another's output).  For 1 < m <= 8 with every width
+ *    1024, 2048 or 3072 and no argmax on a matvec wider than 1024, the
+ *    wider matvecs run as column slices of 1024 whose partial outputs (in
+ *    a buffer the graph owns) a second kernel node adds in slice order:
+ *    two kernel nodes, and the wider matvecs' outputs round as that sum
+ *    does (not bit-identical to q8_matvec_batched; within the same
+ *    bound of the exact result).
  *  Q8_GRAPH_PERSISTENT_I8X: as Q8_GRAPH_PERSISTENT, every matvec computed
  *    as q8_matvec_i8x (every width must be one it takes, else
  *    Q8_ERR_SHAPE). */
@@ -252,8 +258,8 @@ int q8_step_graph_build_levels(const q8_matvec_desc *descs, const int32_t *level
 /* Enqueues the whole step with one hipGraphLaunch on `stream`. */
 int q8_step_graph_launch(q8_step_graph *g, void *stream);
 
-/* All but Q8_GRAPH_CHAIN: enqueues the same recorded step (its kernel, or
- * its kernels in level or node order, with the arguments fixed at build
+/* All but Q8_GRAPH_CHAIN: enqueues the same recorded step (its kernel or
+ * kernels, in level or node order, with the arguments fixed at build
  * time; for Q8_GRAPH_DECODE the 5 * n_layers + 2 kernels of the decode step)
  * with kernel launches instead of hipGraphLaunch: the same work, results and
  * host_idx writes.  Runs on the graph's device whatever device is current; `stream`

@@ -271,6 +271,8 @@ constexpr uint32_t kGraphMagic = 0x51384447u;  // "Q8DG"
 // Decode graphs add attention and norm nodes (kind), or hold the one
 // launch of the persistent decode step (kDecodeNode).
 constexpr int kStepNode = 0, kAttnNode = 1, kNormNode = 2, kDecodeNode = 3;
+// the batched step in column slices (sliced_step_kernel), then its sums
+constexpr int kSlicedNode = 4, kSliceSumNode = 5;
 struct SegmentLaunch {
   const q8::StepDesc *table;
   const q8::WgGroup *groups;
@@ -294,10 +296,16 @@ struct SegmentLaunch {
   int32_t nphases = 0;                   // the barrier and the query heads
   q8::GridBarrier *bar = nullptr;        // per key/value head
   int32_t heads_per_kv = 0;
+  const q8::SliceSum *sums = nullptr;    // kSliceSumNode: the sliced matvecs,
+  int32_t nsums = 0, sum_len = 0;        // their count and largest m * p
 };
 
 hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
   if (L.kind == kAttnNode) return q8::launch_attention(L.attn, s);
+  if (L.kind == kSlicedNode)
+    return q8::launch_sliced_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
+                                  s);
+  if (L.kind == kSliceSumNode) return q8::launch_slice_sum(L.sums, L.nsums, L.sum_len, s);
   if (L.kind == kDecodeNode)
     return q8::launch_decode_persistent(L.phases, L.nphases, L.bar, L.grid, L.lds,
                                         L.heads_per_kv, s);
@@ -375,9 +383,11 @@ namespace q8 {
 // for every argmax descriptor the arrivals each argmax team waits for.
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
               int group_size, StepPlan &plan, bool i8x, bool dec, int grid_cap,
-              uint32_t paired_mask) {
+              uint32_t paired_mask, bool sliced) {
   auto paired = [&](int32_t i) { return i < 32 && ((paired_mask >> i) & 1u); };
   if (paired_mask && (m != 1 || i8x || count > 32)) return Q8_ERR_SHAPE;
+  if (sliced && (m < 2 || m > Q8_MAX_M_NARROW || i8x || dec || paired_mask))
+    return Q8_ERR_SHAPE;
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
   plan.i8x = i8x;
@@ -393,7 +403,8 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     t.idx = d.idx;
     t.n = d.n;
     t.p = d.p;
-    t.rows_per_tile = step_rows_per_tile(d.n, m, i8x);
+    if (sliced && d.n != kSliceWidth) return Q8_ERR_SHAPE;
+    t.rows_per_tile = sliced ? sliced_rows_per_tile() : step_rows_per_tile(d.n, m, i8x);
     if (paired(i)) {
       if (!step_all_staged(1, d.n, false)) return Q8_ERR_SHAPE;
       t.rows_per_tile = t.rows_per_tile / 2 > 0 ? t.rows_per_tile / 2 : 1;
@@ -402,9 +413,9 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
     if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
     t.tile_end = (int32_t)tiles;
-    const size_t l = step_lds_bytes(m, d.n, i8x);
+    const size_t l = sliced ? sliced_lds_bytes() : step_lds_bytes(m, d.n, i8x);
     if (l > widest) widest = l;
-    plan.all_staged = plan.all_staged && step_all_staged(m, d.n, i8x);
+    plan.all_staged = plan.all_staged && (sliced || step_all_staged(m, d.n, i8x));
   }
   if (tiles < 1) return Q8_ERR_SHAPE;  // nothing to run
   if (grid_cap > 0 && m == 1 && !i8x && plan.all_staged) {
@@ -457,7 +468,9 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   const int32_t ntiles = (int32_t)tiles;
   plan.lds = widest;
   if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;
-  int grid = grid_cap > 0 ? grid_cap : step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
+  int grid = grid_cap > 0 ? grid_cap
+             : sliced   ? sliced_step_grid(dev)
+                        : step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
   if (group_size < 1) group_size = 1;
@@ -709,6 +722,19 @@ int capture_graph(q8_step_graph *g, q8_step_graph **out, F record) {
 }
 }  // extern "C++"
 
+// Device memory freed on scope exit unless released.
+struct DevBuf {
+  void *p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+  void *release() {
+    void *r = p;
+    p = nullptr;
+    return r;
+  }
+};
+
 // Builds every form of step graph.  levels (Q8_GRAPH_LEVELS only) gives each
 // descriptor's dependency level; each run of equal levels becomes one
 // persistent kernel node, the nodes in level order.
@@ -749,13 +775,76 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
     if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
   }
 
+  // The batched persistent step in column slices (q8::SliceSum): every width
+  // 1024, 2048 or 3072, no argmax on a wider matvec.  `ex` then holds the
+  // launch's descriptors (a wider matvec's slices in its place, their y
+  // partial outputs in `part`), and `sums` the second launch's table.
+  bool sliced = mode == Q8_GRAPH_PERSISTENT && !i8x && m >= 2 && m <= Q8_MAX_M_NARROW;
+  for (int32_t i = 0; i < count && sliced; i++) {
+    const q8_matvec_desc &d = descs[i];
+    if (d.n != 1024 && d.n != 2048 && d.n != 3072) sliced = false;
+    else if (d.n > 1024 && (d.idx || (int64_t)m * d.p > 0x7FFFFFFF)) sliced = false;
+  }
+  std::vector<q8_matvec_desc> ex;
+  std::vector<int32_t> ex_pitch16;
+  std::vector<q8::SliceSum> sums;
+  int32_t sum_len = 0;
+  DevBuf part;
+  if (sliced) {
+    size_t part_floats = 0;
+    for (int32_t i = 0; i < count; i++)
+      if (descs[i].n > q8::kSliceWidth)
+        part_floats += (size_t)(descs[i].n / q8::kSliceWidth) * (size_t)m * (size_t)descs[i].p;
+    if (part_floats) {
+      hipError_t pe = hipMalloc(&part.p, part_floats * sizeof(float));
+      if (pe != hipSuccess) return hip_fail(pe);
+    }
+    float *pb = (float *)part.p;
+    size_t off = 0;
+    for (int32_t i = 0; i < count; i++) {
+      const q8_matvec_desc &d = descs[i];
+      const int32_t pitch16 = d.n / 32 * 34 / 16;
+      if (d.n == q8::kSliceWidth) {
+        ex.push_back(d);
+        ex_pitch16.push_back(pitch16);
+        continue;
+      }
+      const int32_t k = d.n / q8::kSliceWidth;
+      const size_t len = (size_t)m * (size_t)d.p;
+      for (int32_t sl = 0; sl < k; sl++) {
+        q8_matvec_desc sd = d;
+        sd.w = (const uint8_t *)d.w + (size_t)sl * (q8::kSliceWidth / 32) * 34;
+        sd.x = d.x + (size_t)sl * q8::kSliceWidth;
+        sd.y = len ? pb + off + (size_t)sl * len : nullptr;
+        sd.n = q8::kSliceWidth;
+        ex.push_back(sd);
+        ex_pitch16.push_back(pitch16);
+      }
+      if (len) {
+        sums.push_back(q8::SliceSum{d.y, pb + off, k, (int32_t)len});
+        off += (size_t)k * len;
+        sum_len = (int32_t)len > sum_len ? (int32_t)len : sum_len;
+      }
+    }
+    if ((int64_t)ex.size() > Q8_MAX_DESCS) sliced = false;  // (the unsliced plan then)
+  }
+  const q8_matvec_desc *pdescs = sliced ? ex.data() : descs;
+  const int32_t pcount = sliced ? (int32_t)ex.size() : count;
+
   // persistent segments: all descriptors, or each run of one level
   struct Segment {
     int32_t begin, end;
     q8::StepPlan plan;
   };
   std::vector<Segment> segs;
-  if (persistent) {
+  if (persistent && sliced) {
+    segs.push_back(Segment{0, pcount, q8::StepPlan()});
+    st = q8::plan_step(pdescs, pcount, m, dev, q8::kStepGroupSizeBatched, segs[0].plan, false,
+                       false, 0, 0u, true);
+    if (st) return st;
+    for (int32_t i = 0; i < pcount; i++)
+      segs[0].plan.descs[i].flags |= ex_pitch16[i] << q8::kDescPitchShift;
+  } else if (persistent) {
     for (int32_t i = 0; i < count;) {
       int32_t j = i + 1;
       if (mode == Q8_GRAPH_LEVELS) {
@@ -793,6 +882,9 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
     group_off.push_back(total);
     total += (sg.plan.groups.size() * sizeof(q8::WgGroup) + 15) & ~(size_t)15;
   }
+  const size_t sums_off = total;  // the sliced step's sums table
+  total += (sums.size() * sizeof(q8::SliceSum) + 15) & ~(size_t)15;
+  g->act = part.release();  // (freed with the graph)
   hipError_t e = hipMalloc(&g->workspace, total);
   if (e == hipSuccess) e = hipMemset(g->workspace, 0, total);
   if (e != hipSuccess) {
@@ -835,6 +927,17 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
       g->launches.push_back(SegmentLaunch{
           (const q8::StepDesc *)(ws + table_off[i]), (const q8::WgGroup *)(ws + group_off[i]),
           segs[i].end - segs[i].begin, pl.group_size, pl.grid, pl.lds, pl.all_staged});
+      if (sliced) g->launches.back().kind = kSlicedNode;
+    }
+    if (sliced && !sums.empty() && e == hipSuccess) {
+      e = hipMemcpy(ws + sums_off, sums.data(), sums.size() * sizeof(q8::SliceSum),
+                    hipMemcpyHostToDevice);
+      SegmentLaunch L{nullptr, nullptr, 0, 0, 0, 0, true};
+      L.kind = kSliceSumNode;
+      L.sums = (const q8::SliceSum *)(ws + sums_off);
+      L.nsums = (int32_t)sums.size();
+      L.sum_len = sum_len;
+      g->launches.push_back(L);
     }
     if (e != hipSuccess) {
       release_graph(g);
@@ -864,19 +967,6 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
 }
 
 bool ok16(const void *p) { return p && aligned(p, 16); }
-
-// Device memory freed on scope exit unless released.
-struct DevBuf {
-  void *p = nullptr;
-  ~DevBuf() {
-    if (p) (void)hipFree(p);
-  }
-  void *release() {
-    void *r = p;
-    p = nullptr;
-    return r;
-  }
-};
 
 // The whole decode step: argument checks, then the plans, the workspace and
 // the node list (norm; per layer q/k/v, attention, o + add + norm, gate/up +

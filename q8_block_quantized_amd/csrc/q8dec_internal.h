@@ -176,6 +176,26 @@ size_t step_lds_bytes(int m, int n, bool i8x = false);
 int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x = false,
               bool dec = false);
 
+// The batched persistent step in column slices (1 < m <= 8, every width
+// 1024, 2048 or 3072): a matvec wider than 1024 runs as n / 1024 column
+// slices of 1024, each a descriptor of its own (flags: the matrix's pitch;
+// its x rows the matrix's width apart) whose y is a partial output, and a
+// second launch adds the slices' partials in slice order.  Every slice is
+// then as narrow as the 1024-wide matvecs, whose tiles need a third of the
+// x registers and LDS, so three workgroups fit a CU instead of two.
+struct SliceSum {
+  float *y;           // m * p outputs
+  const float *part;  // k partial outputs of m * p floats, slice after slice
+  int32_t k, len;     // slices, m * p
+};
+constexpr int kSliceWidth = 1024;
+int sliced_rows_per_tile();
+size_t sliced_lds_bytes();
+int sliced_step_grid(int device);
+hipError_t launch_sliced_step(const StepDesc *descs, int count, const WgGroup *groups,
+                              int group_size, int m, int grid, size_t lds, hipStream_t s);
+hipError_t launch_slice_sum(const SliceSum *sums, int count, int max_len, hipStream_t s);
+
 // Everything a persistent step launch needs, worked out on the host.
 struct StepPlan {
   std::vector<StepDesc> descs;  // slot pointers filled in by the caller
@@ -345,7 +365,9 @@ namespace q8 {
 // paired (kDescPairedSilu, m = 1 staged only): its tiles hold rows of two
 // matrices, so they are half as tall and weigh twice the bytes; the caller
 // fills w2, y2 and h and sets the flag.
+// sliced: a launch of sliced_step_kernel (every descriptor 1024 wide, 1 < m
+// <= 8; the caller sets each descriptor's pitch flags).
 int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
               int group_size, StepPlan &plan, bool i8x = false, bool dec = false,
-              int grid_cap = 0, uint32_t paired_mask = 0);
+              int grid_cap = 0, uint32_t paired_mask = 0, bool sliced = false);
 }  // namespace q8

@@ -840,16 +840,18 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 // x row (lane % 16) & 7, hi or lo part, elements 8 (lane / 16) .. + 7 of each
 // block; NBW = n / 128 blocks per wave.  Lanes i and i + 8 of a 16-lane row
 // need the same eight floats: each loads four and a DPP rotation by 8 within
-// the row swaps the halves.
-template <int NBW>
-__device__ __forceinline__ void load_xa(u32x4 (&xa)[kMfmaMaxBlocks],
-                                        const float *x, int32_t m, int32_t n) {
+// the row swaps the halves.  xstride: floats from one x row to the next (n,
+// or the whole matrix's width for a column slice).
+template <int NBW, int MB>
+__device__ __forceinline__ void load_xa(u32x4 (&xa)[MB],
+                                        const float *x, int32_t m, int32_t xstride) {
+  static_assert(NBW <= MB, "the slice fits the registers");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, xr = i & 7, g = lane >> 4;
   const bool lo = i >= 8, live = xr < m;
   const __attribute__((address_space(1))) f32x4 *src =
       (const __attribute__((address_space(1))) f32x4 *)gp(
-          x + (int64_t)(live ? xr : 0) * n + 32 * wave * NBW + 8 * g + 4 * lo);
+          x + (int64_t)(live ? xr : 0) * xstride + 32 * wave * NBW + 8 * g + 4 * lo);
   f32x4 v[NBW];
 #pragma unroll
   for (int t = 0; t < NBW; t++) v[t] = src[8 * t];
@@ -882,10 +884,10 @@ __device__ __forceinline__ void load_xa(u32x4 (&xa)[kMfmaMaxBlocks],
 // Rows [0, rows) of a batched tile in LDS (row pitch 34 * bpr + kMfmaRowPad
 // bytes, bpr = 4 * NBW): y[i][r0 + row] for i < m.  `red` is kRedFloats of LDS.  Keys of
 // x row threadIdx.x / 16 (threads below 128) go to `kb`.
-template <int NBW>
+template <int NBW, int MB>
 __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
                                           int32_t rows, int32_t m, int32_t p,
-                                          const u32x4 (&xa)[kMfmaMaxBlocks],
+                                          const u32x4 (&xa)[MB],
                                           float *red, float *y, int32_t r0,
                                           bool keys, unsigned long long &kb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1301,7 +1303,8 @@ struct NoWait {
   __device__ bool operator()() const { return true; }
 };
 template <bool M1, bool ANY, bool I8X, bool PRIO, int NBLS, bool DEC, class Src,
-          bool STRIDED = false, bool COH = false, class Wait = NoWait>
+          bool STRIDED = false, bool COH = false, class Wait = NoWait,
+          int MTB = kMfmaTileBytes, int MMB = kMfmaMaxBlocks>
 __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                           int32_t stride, int32_t d_hint, int32_t m,
                           float *lds, const Prologue *pro = nullptr, Wait wait = Wait(),
@@ -1310,9 +1313,10 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
                 "the persistent decode step: staged m = 1 tiles of the decode variant");
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
-  constexpr int CH = (M1 || I8X) ? kStageChunks : kMfmaChunks;
+  // MTB, MMB: the batched tile's LDS bytes and each wave's x blocks
+  constexpr int CH = (M1 || I8X) ? kStageChunks : (MTB + 16 * kWG - 1) / (16 * kWG);
   uint32_t *tl = (uint32_t *)lds;
-  float *red = lds + ((M1 || I8X) ? kTileMaxBytes : kMfmaTileBytes) / 4;
+  float *red = lds + ((M1 || I8X) ? kTileMaxBytes : MTB) / 4;
   float *xs = M1 ? red : red + kRedFloats;
   // int8 activations: the steps, then the packed codes, after the tile
   float *xd = red;
@@ -1396,7 +1400,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     pf.load_x(cur.d.x, m * cur.d.n);
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
-  u32x4 xa[kMfmaMaxBlocks];      // batched path: this lane's operand A
+  u32x4 xa[MMB];                 // batched path: this lane's operand A
   const int32_t total = (end - 1 - first) / stride + 1;  // this workgroup's tiles
   (void)total;
   for (;;) {
@@ -1426,9 +1430,16 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     // a new matvec's operand A is loaded before the next tile's bytes are
     // requested, so waiting for it does not wait for them
     if (mfma(cur) && (cur.d.x != xaptr || cur.d.n != xan)) {
-      if (bpr == 32) load_xa<8>(xa, cur.d.x, m, cur.d.n);
-      else if (bpr == 64) load_xa<16>(xa, cur.d.x, m, cur.d.n);
-      else load_xa<24>(xa, cur.d.x, m, cur.d.n);
+      // a column slice's x rows lie the whole matrix's width apart
+      const int32_t xstride =
+          STRIDED ? desc_pitch16(cur.d.flags) * 16 / 34 * 32 : cur.d.n;
+      if constexpr (MMB >= 24) {
+        if (bpr == 32) load_xa<8>(xa, cur.d.x, m, xstride);
+        else if (bpr == 64) load_xa<16>(xa, cur.d.x, m, xstride);
+        else load_xa<24>(xa, cur.d.x, m, xstride);
+      } else {  // (every batched matvec of the launch 1024 wide)
+        load_xa<8>(xa, cur.d.x, m, xstride);
+      }
       xaptr = cur.d.x;
       xan = cur.d.n;
     }
@@ -1487,12 +1498,16 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         }
       }
     } else if (mfma(cur)) {
-      if (bpr == 32)
+      if constexpr (MMB >= 24) {
+        if (bpr == 32)
+          mfma_tile<8>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+        else if (bpr == 64)
+          mfma_tile<16>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+        else
+          mfma_tile<24>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+      } else {
         mfma_tile<8>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
-      else if (bpr == 64)
-        mfma_tile<16>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
-      else
-        mfma_tile<24>(tl, bpr, cur.rows, m, cur.d.p, xa, red, cur.d.y, cur.r0, keys, kb);
+      }
     } else if (ANY) {
       Tile c;
       c.w = cur.d.w;
@@ -1954,6 +1969,59 @@ __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint3
   return ok;
 }
 
+// The batched step in column slices: every descriptor 1024 wide with its
+// matrix's row pitch (a column slice, or a 1024-wide matrix whole), so each
+// wave keeps 8 blocks of x (a third of the registers of 3072-wide rows) and
+// a tile is two 16-row groups (35 KB of LDS): three workgroups a CU.
+constexpr int kSliceRows = 32;
+constexpr int kMaxSlices = 3;  // 3072 / kSliceWidth
+constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRowPad);
+__global__ void __launch_bounds__(kWG, 3)
+sliced_step_kernel(const StepDesc *__restrict__ table, int32_t count,
+                   const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  TableSrc src{table, count};
+  const WgGroup g = groups[blockIdx.x / group_size];
+  const int32_t j = (int32_t)blockIdx.x - g.first;
+  run_tiles<false, false, false, true, 0, false, TableSrc, true, false, NoWait, kSliceTileBytes,
+            (kSliceWidth >> 5) / kWaves>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
+                                         g.size, g.d0, m, lds);
+}
+
+// y = the sum of a sliced matvec's partial outputs, in slice order
+// (blockIdx.y: the matvec).
+// Four outputs a thread where the lengths and addresses allow it, with every
+// slice's load in flight at once.
+__global__ void __launch_bounds__(kWG)
+slice_sum_kernel(const SliceSum *__restrict__ sums, int32_t count) {
+  const SliceSum s = sums[blockIdx.y];
+  const bool vec = (s.len & 3) == 0 && ((uintptr_t)s.y & 15) == 0 && ((uintptr_t)s.part & 15) == 0;
+  if (vec) {  // (uniform)
+    const f32x4 *pv = (const f32x4 *)s.part;
+    f32x4 *yv = (f32x4 *)s.y;
+    const int32_t n4 = s.len >> 2;
+    for (int32_t e = (int32_t)(blockIdx.x * kWG + threadIdx.x); e < n4;
+         e += (int32_t)(gridDim.x * kWG)) {
+      f32x4 t[kMaxSlices];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; q++)
+        if (q < s.k) t[q] = pv[(int64_t)q * n4 + e];
+      f32x4 v = t[0];
+#pragma unroll
+      for (int q = 1; q < kMaxSlices; q++)
+        if (q < s.k) v = v + t[q];
+      yv[e] = v;
+    }
+    return;
+  }
+  for (int32_t e = (int32_t)(blockIdx.x * kWG + threadIdx.x); e < s.len;
+       e += (int32_t)(gridDim.x * kWG)) {
+    float v = s.part[e];
+    for (int32_t q = 1; q < s.k; q++) v += s.part[(int64_t)q * s.len + e];
+    s.y[e] = v;
+  }
+}
+
 // The whole decode step in one launch (G query heads per key/value head):
 // the phases of a device-side table in order, every workgroup meeting the
 // others at the grid barrier between two phases.  A matvec phase runs the
@@ -2280,6 +2348,33 @@ hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
     else Q8_STEP(false, true, false, false);
   }
 #undef Q8_STEP
+  return hipGetLastError();
+}
+
+int sliced_rows_per_tile() { return kSliceRows; }
+
+size_t sliced_lds_bytes() { return kSliceTileBytes + (size_t)kRedFloats * sizeof(float); }
+
+int sliced_step_grid(int dev) {
+  static int cache[64] = {0};
+  int &c = cache[dev & 63];
+  if (!c) c = resident_wgs(sliced_step_kernel, sliced_lds_bytes(), dev);
+  return c;
+}
+
+hipError_t launch_sliced_step(const StepDesc *descs, int count, const WgGroup *groups,
+                              int group_size, int m, int grid, size_t lds, hipStream_t s) {
+  if (m < 2 || m > kMaxM) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sliced_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,
+                     group_size, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_slice_sum(const SliceSum *sums, int count, int max_len, hipStream_t s) {
+  if (count < 1 || max_len < 1) return hipErrorInvalidValue;
+  int gx = (max_len + kWG * 4 - 1) / (kWG * 4);  // 4 outputs a thread
+  gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(gx, count), dim3(kWG), 0, s, sums, count);
   return hipGetLastError();
 }
 

@@ -141,7 +141,9 @@ def test_full_batched_step_every_output(cuda):
     shapes, ws, xs = step_inputs(28, 151936, m, seed=2)
     descs = device_step(shapes, ws, xs, m, cuda)
     g, host = run_graph(descs, m, 1, cuda)
-    assert g.info() == (1, 0)
+    # the step kernel over column slices of 1024, then the slices' sums (o
+    # and down are 2048 and 3072 wide)
+    assert g.info() == (2, 0)
     g.launch()
     torch.cuda.synchronize()
     say("full m=8 step: checking every output against the oracle")
@@ -153,6 +155,68 @@ def test_full_batched_step_every_output(cuda):
             for r in range(m):
                 assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
                 assert int(host[r]) == oracle.argmax_f32(y[r])
+    g.close()
+
+
+@pytest.mark.parametrize("m", [2, 3, 5, 7])
+def test_sliced_batched_step(cuda, m):
+    """The batched persistent step in column slices (every width 1024, 2048
+    or 3072): wide matvecs with ragged row counts (not a multiple of the
+    32-row tile), an odd m (m * p not a multiple of four: the sums' scalar
+    path), one empty matvec and an argmax on a 1024-wide one; every output
+    against the oracle, over three launches with the outputs poisoned in
+    between, and the kernel launch equal to the graph launch."""
+    import torch
+    shapes = [("a", 2048, 77), ("b", 1024, 100), ("c", 3072, 33), ("empty", 3072, 0),
+              ("d", 2048, 1), ("e", 3072, 200), ("lm", 1024, 5000)]
+    ws = [gen.weights(p, n, seed=11, index=i) for i, (_, n, p) in enumerate(shapes)]
+    xs = [gen.activations(m, n, seed=11, index=i) for i, (_, n, p) in enumerate(shapes)]
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, 1, cuda)
+    assert g.info() == (2, 0)  # the sliced step, then the slices' sums
+    refs = [oracle_rows(ws[i], xs[i]) if p else None for i, (_, n, p) in enumerate(shapes)]
+    first = None
+    for rep in range(3):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        host[:] = -9
+        (g.launch if rep != 2 else g.launch_kernel)()
+        torch.cuda.synchronize()
+        for i, (name, n, p) in enumerate(shapes):
+            if not p:
+                continue
+            y = descs[i]["y"].cpu().numpy()
+            assert_parity(y, refs[i][0], refs[i][1], f"m={m} {name} rep {rep}")
+        ref, tol = refs[-1]
+        for r in range(m):
+            assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+        outs = [d["y"].clone() for d in descs]
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a, b)
+    g.close()
+
+
+def test_wide_argmax_keeps_the_unsliced_step(cuda):
+    """An argmax on a matvec wider than 1024 keeps the whole-row step (one
+    node): its outputs and token against the oracle."""
+    import torch
+    m = 4
+    shapes = [("a", 1024, 64), ("lm", 2048, 3000)]
+    ws = [gen.weights(p, n, seed=12, index=i) for i, (_, n, p) in enumerate(shapes)]
+    xs = [gen.activations(m, n, seed=12, index=i) for i, (_, n, p) in enumerate(shapes)]
+    descs = device_step(shapes, ws, xs, m, cuda)
+    g, host = run_graph(descs, m, 1, cuda)
+    assert g.info() == (1, 0)
+    g.launch()
+    torch.cuda.synchronize()
+    for i, (name, n, p) in enumerate(shapes):
+        ref, tol = oracle_rows(ws[i], xs[i])
+        assert_parity(descs[i]["y"].cpu().numpy(), ref, tol, name)
+    for r in range(m):
+        assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
     g.close()
 
 
