@@ -906,7 +906,18 @@ def main() -> int:
         }
         for g in p8:
             g.close()
-        del sets8, p8
+        log("batched m=8 int8-activation step (persistent graph)")
+        p8i = [q8.StepGraph(s.descs, 8, host_idx=host8, mode=q8.Q8_GRAPH_PERSISTENT_I8X)
+               for s in sets8]
+        s8i, _ = time_graph_steps(torch, p8i, host8, steps2, 3, poll=True)
+        extra["i8x_batched_m8_step"] = {
+            "step_latency_us": round(s8i * 1e6, 2),
+            "GBps": round(b8 / s8i / 1e9, 1),
+            "note": "int8 activations, 8 rows: the matrix-core int8 tile",
+        }
+        for g in p8i:
+            g.close()
+        del sets8, p8, p8i
 
         log("batched m=32 step (wide batch, persistent graph)")
         sets32 = [StepSet(torch, dev, 0, 7000 + 1000 * j, 32, False, weights=s.w)

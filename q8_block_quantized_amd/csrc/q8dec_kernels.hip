@@ -42,6 +42,7 @@ namespace q8 {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
 typedef uint32_t u32_a4 __attribute__((aligned(4)));
@@ -677,11 +678,13 @@ __device__ __forceinline__ float q8x_chunk(const f32x4 v, uint32_t &codes) {
 
 // m rows of x ([m][n] f32 in global memory) quantised into LDS: xq (packed
 // codes, row i block b at dword 8 (i * n/32 + b)) and xd (the steps, block
-// i * n/32 + b).  Loaded directly (the batched form, once per matvec).
-template <int NT>
+// i * n/32 + b, or with BM block-major: b * kMaxM + i).  Loaded directly
+// (the batched form, once per matvec).
+template <int NT, bool BM = false>
 __device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
                                uint32_t *xq, float *xd) {
   const int32_t chunks = (m * n) >> 2;  // a multiple of 8: no block is split
+  const int32_t bpr = n >> 5;
   for (int32_t c0 = 0; c0 < chunks; c0 += NT) {
     const int32_t c = c0 + (int32_t)threadIdx.x;
     const f32x4 v = gp((const f32x4 *)x)[c < chunks ? c : chunks - 1];
@@ -689,7 +692,10 @@ __device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
     const float d = q8x_chunk(v, codes);
     if (c < chunks) {
       xq[c] = codes;
-      if ((c & 7) == 0) xd[c >> 3] = d;
+      if ((c & 7) == 0) {
+        const int32_t k = c >> 3, i = BM ? k / bpr : 0;
+        xd[BM ? (k - i * bpr) * kMaxM + i : k] = d;
+      }
     }
   }
 }
@@ -813,6 +819,33 @@ __device__ __forceinline__ void staged_mb_i8(const uint32_t *tl, int32_t bpr,
 // in LDS, where y[i][row] = sum over waves of column i plus column i + 8.
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-row group's outputs of the int8 matrix-core tile from the four waves'
+// partials acc, through LDS as mfma_tile's (there y[xr][row] also adds the
+// column xr + 8 of x's low parts, which the int8 form does not have).
+__device__ __forceinline__ void mfma_group_out(const f32x4 &acc, float *red, int buf,
+                                               int32_t rg, int32_t rows, int32_t m,
+                                               int32_t p, float *y, int32_t r0, bool keys,
+                                               unsigned long long &kb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float *rb = red + buf * (kWaves * 4 * kRedStride);
+#pragma unroll
+  for (int r = 0; r < 4; r++) rb[(wave * 4 + r) * kRedStride + lane] = acc[r];
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int xr = threadIdx.x >> 4, jj = threadIdx.x & 15;
+    const int hi = (xr & 3) * kRedStride + 16 * (xr >> 2) + jj;  // column xr
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) v += rb[w * 4 * kRedStride + hi];
+    const int32_t rr = rg + jj;
+    if (xr < m && rr < rows) {
+      if (y) store_y(&y[(int64_t)xr * p + r0 + rr], v);
+      if (keys) kb = umax64(kb, argmax_key(v, (uint32_t)(r0 + rr)));
+    }
+  }
+}
 
 // Two int8 quants (bytes lo, lo + 1 of q) as a pair of bf16 (exact): the f32
 // of a small integer has zero low halves, so the high halves are the bf16.
@@ -952,6 +985,81 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
     // orders this group's reads before the one after reuses this buffer
     buf ^= 1;
   }
+}
+
+// Rows [0, rows) of a batched tile against int8 activations (1 < m <= 8,
+// n = 32 NBW * kWaves): a 16-row group against one block is one
+// v_mfma_i32_16x16x32_i8, operand A the x rows' codes (rows >= m zero),
+// operand B the 16 weight rows' quants as they are stored (no conversion),
+// D[i][j] the exact integer block sum of x row i and weight row j.  Each
+// block's sum is then scaled as the VALU form scales it, by the weight
+// row's scale times x row i's step (xd, block-major: xd[b * kMaxM + i]),
+// and added to the f32 accumulator of its x row; the waves' partials meet
+// in LDS as mfma_tile's do.  The lane layout is mfma_tile's (operands of
+// 8 bytes instead of 8 bf16).
+template <int NBW, int MB>
+__device__ __forceinline__ void mfma_tile_i8(const uint32_t *tl, int32_t bpr,
+                                             int32_t rows, int32_t m, int32_t p,
+                                             const u32x2 (&xi)[MB], const float *xd,
+                                             float *red, float *y, int32_t r0,
+                                             bool keys, unsigned long long &kb) {
+  static_assert(NBW <= MB && NBW % 2 == 0, "a wave's blocks: pairs within its registers");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int32_t lpd = (bpr * 34 + kMfmaRowPad) >> 2;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const i32x4 izero = {0, 0, 0, 0};
+  // steps of x rows 4 g .. 4 g + 3 (rows 8 .. 15, which A holds as zeros,
+  // read rows 0 .. 7's: their sums are 0 and never leave the tile)
+  const float *xdw = xd + (wave * NBW) * kMaxM + 4 * (g & 1);
+  int buf = 0;
+  for (int32_t rg = 0; rg < rows; rg += 16) {
+    const int32_t row = min(rg + j, rows - 1);
+    const uint32_t *rp = tl + row * lpd + ((34 * wave * NBW) >> 2);
+    f32x4 acc = zero;
+#pragma unroll
+    for (int t = 0; t < NBW; t += 2) {
+      // blocks t (quants from byte 2 of wp) and t + 1 (from byte 36)
+      const uint32_t *wp = rp + 17 * (t >> 1);
+      const uint32_t *wq = wp + 2 * g;
+      const uint32_t e0 = wq[0], e1 = wq[1], e2 = wq[2];
+      const uint32_t o0 = wq[9], o1 = wq[10];
+      const uint32_t s01 = wp[0], s23 = wp[8];
+      const int64_t qe = (int64_t)(((uint64_t)__builtin_amdgcn_perm(e2, e1, 0x05040302u) << 32) |
+                                   __builtin_amdgcn_perm(e1, e0, 0x05040302u));
+      const int64_t qo = (int64_t)(((uint64_t)o1 << 32) | o0);
+      const i32x4 de = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          (int64_t)__builtin_bit_cast(uint64_t, xi[t]), qe, izero, 0, 0, 0);
+      const i32x4 dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          (int64_t)__builtin_bit_cast(uint64_t, xi[t + 1]), qo, izero, 0, 0, 0);
+      const float se = (float)__builtin_bit_cast(_Float16, (uint16_t)(s01 & 0xFFFFu));
+      const float so = (float)__builtin_bit_cast(_Float16, (uint16_t)(s23 >> 16));
+      const f32x4 xe = *(const f32x4 *)(xdw + t * kMaxM);
+      const f32x4 xo = *(const f32x4 *)(xdw + (t + 1) * kMaxM);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        acc[r] = fmaf((float)de[r], se * xe[r], acc[r]);
+        acc[r] = fmaf((float)dd[r], so * xo[r], acc[r]);
+      }
+    }
+    mfma_group_out(acc, red, buf, rg, rows, m, p, y, r0, keys, kb);
+    buf ^= 1;
+  }
+}
+
+// Each wave's operand A of the int8 tile: lane l takes x row l % 16 (zero
+// from row m on), block wave * NBW + t, codes 8 (l / 16) .. + 7, from the
+// codes quantize_x_lds left in LDS (row i block b at dword 8 (i bpr + b)).
+template <int NBW, int MB>
+__device__ __forceinline__ void load_xi(u32x2 (&xi)[MB], const uint32_t *xq, int32_t m,
+                                        int32_t bpr) {
+  static_assert(NBW <= MB, "a wave's blocks fit its registers");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const u32x2 z = {0u, 0u};
+#pragma unroll
+  for (int t = 0; t < NBW; t++)
+    xi[t] = i < m ? *(const u32x2 *)(xq + 8 * (i * bpr + wave * NBW + t) + 2 * g) : z;
 }
 
 // Registers that carry the next tile's weights (and x, when the next tile
@@ -1314,16 +1422,23 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   static_assert(!(I8X && ANY), "int8 activations: staged shapes only");
   constexpr int XC = M1 ? 3 : (ANY ? 8 : 1);  // float4 chunks of x per thread
   // MTB, MMB: the batched tile's LDS bytes and each wave's x blocks
-  constexpr int CH = (M1 || I8X) ? kStageChunks : (MTB + 16 * kWG - 1) / (16 * kWG);
+  constexpr int CH = M1 ? kStageChunks : (MTB + 16 * kWG - 1) / (16 * kWG);
   uint32_t *tl = (uint32_t *)lds;
-  float *red = lds + ((M1 || I8X) ? kTileMaxBytes : MTB) / 4;
+  float *red = lds + (M1 ? kTileMaxBytes : MTB) / 4;
   float *xs = M1 ? red : red + kRedFloats;
-  // int8 activations: the steps, then the packed codes, after the tile
-  float *xd = red;
-  uint32_t *xq = (uint32_t *)(red + kI8xMaxBlocks);
-  // which path a tile takes; without ANY every tile takes the staged one
-  auto staged = [&](const Job &j) { return I8X || (M1 && (!ANY || j.path == kStaged)); };
-  auto mfma = [&](const Job &j) { return !I8X && !M1 && (!ANY || j.path == kMfma); };
+  // int8 activations: the steps, then the packed codes (m = 1: after the
+  // tile; batched: after the partial sums; the matrix-core tiles hold their
+  // codes in registers and need no packed region)
+  float *xd = M1 ? red : red + kRedFloats;
+  uint32_t *xq = (uint32_t *)(xd + kI8xMaxBlocks);
+  // which path a tile takes; without ANY every m = 1 tile takes the staged
+  // one; batched int8 tiles of the matrix-core widths take the matrix cores
+  auto staged = [&](const Job &j) {
+    return (I8X && (M1 || j.path != kMfma)) || (M1 && (!ANY || j.path == kStaged));
+  };
+  auto mfma = [&](const Job &j) {
+    return !M1 && (I8X ? j.path == kMfma : (!ANY || j.path == kMfma));
+  };
   // x prefetched into registers and staged in LDS with the tile
   auto x_in_lds = [&](const Job &j) {
     return M1 ? (!ANY || j.path != kGeneric) : (ANY && j.path == kDirect);
@@ -1401,6 +1516,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   unsigned long long best[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
   unsigned long long kb = 0ull;  // batched path: key of x row threadIdx.x / 16
   u32x4 xa[MMB];                 // batched path: this lane's operand A
+  u32x2 xi[MMB];                 // batched int8 path: the same, x's codes
   const int32_t total = (end - 1 - first) / stride + 1;  // this workgroup's tiles
   (void)total;
   for (;;) {
@@ -1411,6 +1527,20 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const bool x_changed = cur.d.x != xptr || cur.d.n != xn;
     const bool new_x = x_in_lds(cur) && x_changed;
     __syncthreads();  // the previous tile's readers of LDS are done
+    // batched int8 on the matrix cores: a new x's codes go through the tile
+    // buffer (before this tile is staged there) into each wave's operand A;
+    // its steps stay in LDS, block-major
+    const bool quant_xi = I8X && !M1 && mfma(cur) && x_changed;
+    if constexpr (I8X && !M1) {
+      if (quant_xi) {
+        quantize_x_lds<kWG, true>(cur.d.x, m, cur.d.n, tl, xd);
+        __syncthreads();
+        if (bpr == 32) load_xi<8>(xi, tl, m, bpr);
+        else if (bpr == 64) load_xi<16>(xi, tl, m, bpr);
+        else load_xi<24>(xi, tl, m, bpr);
+        __syncthreads();  // every wave holds its codes: the tile may overwrite them
+      }
+    }
     // a paired tile holds its rows of both matrices, one after the other
     const bool pair = DEC && (cur.d.flags & kDescPairedSilu);
     const int32_t trows = pair ? 2 * cur.rows : cur.rows;
@@ -1420,16 +1550,17 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       if (I8X) pf.store_xq(xq, xd, m, cur.d.n);
       else pf.store_x(xs, m, cur.d.n);
     }
-    const bool quant_x = I8X && !M1 && x_changed;  // batched: straight from memory
+    // batched (VALU tiles): straight from memory
+    const bool quant_x = I8X && !M1 && !mfma(cur) && x_changed;
     if (quant_x) quantize_x_lds<kWG>(cur.d.x, m, cur.d.n, xq, xd);
     __syncthreads();
-    if (new_x || quant_x) {
+    if (new_x || quant_x || quant_xi) {
       xptr = cur.d.x;
       xn = cur.d.n;
     }
     // a new matvec's operand A is loaded before the next tile's bytes are
     // requested, so waiting for it does not wait for them
-    if (mfma(cur) && (cur.d.x != xaptr || cur.d.n != xan)) {
+    if (!I8X && mfma(cur) && (cur.d.x != xaptr || cur.d.n != xan)) {
       // a column slice's x rows lie the whole matrix's width apart
       const int32_t xstride =
           STRIDED ? desc_pitch16(cur.d.flags) * 16 / 34 * 32 : cur.d.n;
@@ -1467,6 +1598,15 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         if (nbl == 1) staged_m1_i8<1>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
         else if (nbl == 2) staged_m1_i8<2>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
         else staged_m1_i8<3>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
+      } else if (mfma(cur)) {
+        if constexpr (I8X && !M1) {
+          if (bpr == 32)
+            mfma_tile_i8<8>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
+          else if (bpr == 64)
+            mfma_tile_i8<16>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
+          else
+            mfma_tile_i8<24>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
+        }
       } else {
         if (nbl == 1) staged_mb_i8<1>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
         else if (nbl == 2) staged_mb_i8<2>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
@@ -1808,7 +1948,7 @@ __device__ void wide_tiles(const Src &src, int32_t first, int32_t end, int32_t s
 // grid (gridDim.x <= tiles, so every workgroup arrives at the argmax): at
 // any moment the grid streams one contiguous window of the weights.
 template <bool M1, bool ANY, bool I8X, int NBLS>
-__global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
+__global__ void __launch_bounds__(kWG, M1 ? 1 : 2)
 mv_kernel(StepDesc d, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   OneSrc src{d};
@@ -1859,7 +1999,7 @@ reduce_slices(const float *__restrict__ part, int32_t slices, int32_t p, float *
 // NULL: element-wise work that the last workgroup to finish runs once every
 // tile is written); the other launches do not carry that code.
 template <bool M1, bool ANY, bool I8X, bool DEC>
-__global__ void __launch_bounds__(kWG, (M1 || I8X) ? 1 : 2)
+__global__ void __launch_bounds__(kWG, M1 ? 1 : 2)
 step_kernel(const StepDesc *__restrict__ table, int32_t count,
             const WgGroup *__restrict__ groups, int32_t group_size, int32_t m,
             const Epilogue *__restrict__ epi, const Prologue *__restrict__ pro,
@@ -2136,8 +2276,19 @@ argmax_rows(const float *__restrict__ logits, int32_t m, int32_t p,
 
 // Dynamic LDS of a launch whose matvecs have widths up to n_max.
 // int8 activations: tile, steps, packed codes (m * n bytes).
+// Batched (m > 1): the batched tile and its partial sums, the steps, and
+// the packed codes for widths off the matrix cores (whose tiles keep x's
+// codes in registers).
 size_t lds_bytes_i8x(int m, int n) {
-  return kTileMaxBytes + (size_t)kI8xMaxBlocks * 4 + (size_t)m * n;
+  if (m == 1) return kTileMaxBytes + (size_t)kI8xMaxBlocks * 4 + (size_t)n;
+  return kMfmaTileBytes + (size_t)(kRedFloats + kI8xMaxBlocks) * 4 +
+         (path_of(m, n) == kMfma ? 0 : (size_t)m * n);
+}
+
+// Rows per tile of the int8-activation variant: staged tiles, except the
+// batched matrix-core widths (whole 16-row groups, as the f32 batched path).
+int i8x_tile_rows(int m, int n) {
+  return m > 1 && path_of(m, n) == kMfma ? tile_rows_of(m, n) : tile_rows_of(1, n);
 }
 
 size_t lds_bytes_for(int m, int n) {
@@ -2210,7 +2361,7 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
   // two tile heights, 21 and 22 rows for the lm_head, measured 1.5 us
   // slower: more tiles, and a part-empty last round also frees bandwidth
   // for the workgroups still running.)
-  if ((I8X || path_of(m, d.n) != kMfma) && tiles_of(d) > cap) {
+  if (path_of(m, d.n) != kMfma && tiles_of(d) > cap) {
     int32_t best_rows = d.rows_per_tile;
     int64_t best_cost = INT64_MAX;
     for (int32_t r = d.rows_per_tile; r >= (3 * d.rows_per_tile + 3) / 4; r--) {
@@ -2231,7 +2382,7 @@ hipError_t launch_mv(StepDesc d, int m, hipStream_t s) {
 }  // namespace
 
 int step_rows_per_tile(int n, int m, bool i8x) {
-  return tile_rows_of(i8x ? 1 : m, n);  // int8 activations: staged tiles for any m
+  return i8x ? i8x_tile_rows(m, n) : tile_rows_of(m, n);
 }
 
 size_t step_lds_bytes(int m, int n, bool i8x) {
@@ -2276,7 +2427,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
   d.n = n;
   d.p = p;
   d.tile_begin = 0;
-  d.rows_per_tile = tile_rows_of(i8x ? 1 : m, n);
+  d.rows_per_tile = i8x ? i8x_tile_rows(m, n) : tile_rows_of(m, n);
   d.tile_end = tiles_of(d);
   if (m > kMaxM) {  // wide batch: 128-row tiles round-robin over the grid
     const int32_t ntiles = tiles_of(d);
@@ -2287,7 +2438,7 @@ hipError_t launch_matvec(const uint8_t *w, const float *x, float *y, int m,
     hipLaunchKernelGGL(wide_mv_kernel, dim3(grid), dim3(kWG), kWideLds, s, d, m);
     return hipGetLastError();
   }
-  const int path = i8x ? (int)kStaged : path_of(m, n);
+  const int path = i8x && (m == 1 || path_of(m, n) != kMfma) ? (int)kStaged : path_of(m, n);
   // small matvecs: shorter tiles spread them over more workgroups (batched
   // tiles stay whole 16-row groups)
   if (path == kMfma) {
