@@ -217,7 +217,9 @@ typedef struct q8_step_graph q8_step_graph;
  *    bound of the exact result).
  *  Q8_GRAPH_PERSISTENT_I8X: as Q8_GRAPH_PERSISTENT, every matvec computed
  *    as q8_matvec_i8x (every width must be one it takes, else
- *    Q8_ERR_SHAPE). */
+ *    Q8_ERR_SHAPE), column slices included (the wider matvecs' outputs
+ *    then round as the slices' sum does, not bit-identical to
+ *    q8_matvec_i8x; within its bound). */
 #define Q8_GRAPH_CHAIN 0
 #define Q8_GRAPH_PERSISTENT 1
 #define Q8_GRAPH_PERSISTENT_I8X 2

@@ -304,7 +304,7 @@ hipError_t run_segment(const SegmentLaunch &L, int m, bool i8x, hipStream_t s) {
   if (L.kind == kAttnNode) return q8::launch_attention(L.attn, s);
   if (L.kind == kSlicedNode)
     return q8::launch_sliced_step(L.table, L.count, L.groups, L.group_size, m, L.grid, L.lds,
-                                  s);
+                                  i8x, s);
   if (L.kind == kSliceSumNode) return q8::launch_slice_sum(L.sums, L.nsums, L.sum_len, s);
   if (L.kind == kDecodeNode)
     return q8::launch_decode_persistent(L.phases, L.nphases, L.bar, L.grid, L.lds,
@@ -386,7 +386,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
               uint32_t paired_mask, bool sliced) {
   auto paired = [&](int32_t i) { return i < 32 && ((paired_mask >> i) & 1u); };
   if (paired_mask && (m != 1 || i8x || count > 32)) return Q8_ERR_SHAPE;
-  if (sliced && (m < 2 || m > Q8_MAX_M_NARROW || i8x || dec || paired_mask))
+  if (sliced && (m < 2 || m > Q8_MAX_M_NARROW || dec || paired_mask))
     return Q8_ERR_SHAPE;
   plan.descs.assign(count, StepDesc());
   plan.all_staged = true;
@@ -413,7 +413,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
     tiles += (d.p + t.rows_per_tile - 1) / t.rows_per_tile;
     if (tiles > 0x7FFFFFFF) return Q8_ERR_SHAPE;
     t.tile_end = (int32_t)tiles;
-    const size_t l = sliced ? sliced_lds_bytes() : step_lds_bytes(m, d.n, i8x);
+    const size_t l = sliced ? sliced_lds_bytes(i8x) : step_lds_bytes(m, d.n, i8x);
     if (l > widest) widest = l;
     plan.all_staged = plan.all_staged && (sliced || step_all_staged(m, d.n, i8x));
   }
@@ -469,7 +469,7 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   plan.lds = widest;
   if (i8x && !plan.all_staged) return Q8_ERR_SHAPE;
   int grid = grid_cap > 0 ? grid_cap
-             : sliced   ? sliced_step_grid(dev)
+             : sliced   ? sliced_step_grid(dev, i8x)
                         : step_grid(dev, m, plan.lds, plan.all_staged, i8x, dec);
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
@@ -775,11 +775,12 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
     if (he != hipSuccess || !host_dev) return hip_fail(he != hipSuccess ? he : hipErrorInvalidValue);
   }
 
-  // The batched persistent step in column slices (q8::SliceSum): every width
-  // 1024, 2048 or 3072, no argmax on a wider matvec.  `ex` then holds the
+  // The batched persistent step in column slices (q8::SliceSum), binary32 or
+  // int8 activations: every width 1024, 2048 or 3072, no argmax on a wider
+  // matvec.  `ex` then holds the
   // launch's descriptors (a wider matvec's slices in its place, their y
   // partial outputs in `part`), and `sums` the second launch's table.
-  bool sliced = mode == Q8_GRAPH_PERSISTENT && !i8x && m >= 2 && m <= Q8_MAX_M_NARROW;
+  bool sliced = (mode == Q8_GRAPH_PERSISTENT || i8x) && m >= 2 && m <= Q8_MAX_M_NARROW;
   for (int32_t i = 0; i < count && sliced; i++) {
     const q8_matvec_desc &d = descs[i];
     if (d.n != 1024 && d.n != 2048 && d.n != 3072) sliced = false;
@@ -839,7 +840,7 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
   std::vector<Segment> segs;
   if (persistent && sliced) {
     segs.push_back(Segment{0, pcount, q8::StepPlan()});
-    st = q8::plan_step(pdescs, pcount, m, dev, q8::kStepGroupSizeBatched, segs[0].plan, false,
+    st = q8::plan_step(pdescs, pcount, m, dev, q8::kStepGroupSizeBatched, segs[0].plan, i8x,
                        false, 0, 0u, true);
     if (st) return st;
     for (int32_t i = 0; i < pcount; i++)

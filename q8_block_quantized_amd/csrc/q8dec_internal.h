@@ -182,7 +182,8 @@ int step_grid(int device, int m, size_t lds, bool all_staged, bool i8x = false,
 // its x rows the matrix's width apart) whose y is a partial output, and a
 // second launch adds the slices' partials in slice order.  Every slice is
 // then as narrow as the 1024-wide matvecs, whose tiles need a third of the
-// x registers and LDS, so three workgroups fit a CU instead of two.
+// x registers and LDS, so three workgroups fit a CU instead of two.  The
+// int8-activation step (i8x) is sliced the same way.
 struct SliceSum {
   float *y;           // m * p outputs
   const float *part;  // k partial outputs of m * p floats, slice after slice
@@ -190,10 +191,11 @@ struct SliceSum {
 };
 constexpr int kSliceWidth = 1024;
 int sliced_rows_per_tile();
-size_t sliced_lds_bytes();
-int sliced_step_grid(int device);
+size_t sliced_lds_bytes(bool i8x = false);
+int sliced_step_grid(int device, bool i8x = false);
 hipError_t launch_sliced_step(const StepDesc *descs, int count, const WgGroup *groups,
-                              int group_size, int m, int grid, size_t lds, hipStream_t s);
+                              int group_size, int m, int grid, size_t lds, bool i8x,
+                              hipStream_t s);
 hipError_t launch_slice_sum(const SliceSum *sums, int count, int max_len, hipStream_t s);
 
 // Everything a persistent step launch needs, worked out on the host.

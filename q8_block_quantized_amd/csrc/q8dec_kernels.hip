@@ -680,14 +680,22 @@ __device__ __forceinline__ float q8x_chunk(const f32x4 v, uint32_t &codes) {
 // codes, row i block b at dword 8 (i * n/32 + b)) and xd (the steps, block
 // i * n/32 + b, or with BM block-major: b * kMaxM + i).  Loaded directly
 // (the batched form, once per matvec).
+// With BM, x's rows may lie xstride floats apart (a column slice of a wider
+// x, whose blocks quantise as they do in the whole row).
 template <int NT, bool BM = false>
 __device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
-                               uint32_t *xq, float *xd) {
+                               uint32_t *xq, float *xd, int32_t xstride = 0) {
   const int32_t chunks = (m * n) >> 2;  // a multiple of 8: no block is split
   const int32_t bpr = n >> 5;
   for (int32_t c0 = 0; c0 < chunks; c0 += NT) {
     const int32_t c = c0 + (int32_t)threadIdx.x;
-    const f32x4 v = gp((const f32x4 *)x)[c < chunks ? c : chunks - 1];
+    const int32_t cc = c < chunks ? c : chunks - 1;
+    int32_t at = cc;  // the chunk's f32x4 index in x
+    if (BM) {
+      const int32_t r = cc / (n >> 2);
+      at = (r * xstride >> 2) + (cc - r * (n >> 2));
+    }
+    const f32x4 v = gp((const f32x4 *)x)[at];
     uint32_t codes;
     const float d = q8x_chunk(v, codes);
     if (c < chunks) {
@@ -1533,11 +1541,18 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
     const bool quant_xi = I8X && !M1 && mfma(cur) && x_changed;
     if constexpr (I8X && !M1) {
       if (quant_xi) {
-        quantize_x_lds<kWG, true>(cur.d.x, m, cur.d.n, tl, xd);
+        // a column slice's x rows lie the whole matrix's width apart
+        const int32_t xstride =
+            STRIDED ? desc_pitch16(cur.d.flags) * 16 / 34 * 32 : cur.d.n;
+        quantize_x_lds<kWG, true>(cur.d.x, m, cur.d.n, tl, xd, xstride);
         __syncthreads();
-        if (bpr == 32) load_xi<8>(xi, tl, m, bpr);
-        else if (bpr == 64) load_xi<16>(xi, tl, m, bpr);
-        else load_xi<24>(xi, tl, m, bpr);
+        if constexpr (MMB >= 24) {
+          if (bpr == 32) load_xi<8>(xi, tl, m, bpr);
+          else if (bpr == 64) load_xi<16>(xi, tl, m, bpr);
+          else load_xi<24>(xi, tl, m, bpr);
+        } else {  // (every batched matvec of the launch 1024 wide)
+          load_xi<8>(xi, tl, m, bpr);
+        }
         __syncthreads();  // every wave holds its codes: the tile may overwrite them
       }
     }
@@ -1599,15 +1614,17 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         else if (nbl == 2) staged_m1_i8<2>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
         else staged_m1_i8<3>(tl, bpr, cur.rows, xq, xd, cur.d.y, cur.r0, keys, best[0]);
       } else if (mfma(cur)) {
-        if constexpr (I8X && !M1) {
+        if constexpr (I8X && !M1 && MMB >= 24) {
           if (bpr == 32)
             mfma_tile_i8<8>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
           else if (bpr == 64)
             mfma_tile_i8<16>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
           else
             mfma_tile_i8<24>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
+        } else if constexpr (I8X && !M1) {
+          mfma_tile_i8<8>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
         }
-      } else {
+      } else if constexpr (!STRIDED) {  // (the sliced step's tiles all take the matrix cores)
         if (nbl == 1) staged_mb_i8<1>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
         else if (nbl == 2) staged_mb_i8<2>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
         else staged_mb_i8<3>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
@@ -2116,6 +2133,10 @@ __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint3
 constexpr int kSliceRows = 32;
 constexpr int kMaxSlices = 3;  // 3072 / kSliceWidth
 constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRowPad);
+// I8X: int8 activations (the matrix-core int8 tile, x quantised per slice:
+// a slice starts at a block boundary, so its blocks' codes and steps are
+// those of the whole row).
+template <bool I8X>
 __global__ void __launch_bounds__(kWG, 3)
 sliced_step_kernel(const StepDesc *__restrict__ table, int32_t count,
                    const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
@@ -2123,7 +2144,7 @@ sliced_step_kernel(const StepDesc *__restrict__ table, int32_t count,
   TableSrc src{table, count};
   const WgGroup g = groups[blockIdx.x / group_size];
   const int32_t j = (int32_t)blockIdx.x - g.first;
-  run_tiles<false, false, false, true, 0, false, TableSrc, true, false, NoWait, kSliceTileBytes,
+  run_tiles<false, false, I8X, true, 0, false, TableSrc, true, false, NoWait, kSliceTileBytes,
             (kSliceWidth >> 5) / kWaves>(src, g.t0 + group_slot(j, g.first, g.size), g.t1,
                                          g.size, g.d0, m, lds);
 }
@@ -2504,20 +2525,30 @@ hipError_t launch_step(const StepDesc *descs, int count, const WgGroup *groups,
 
 int sliced_rows_per_tile() { return kSliceRows; }
 
-size_t sliced_lds_bytes() { return kSliceTileBytes + (size_t)kRedFloats * sizeof(float); }
+// The tile and its partial sums (int8 activations: and x's steps, block-major).
+size_t sliced_lds_bytes(bool i8x) {
+  return kSliceTileBytes + (size_t)(kRedFloats + (i8x ? kI8xMaxBlocks : 0)) * sizeof(float);
+}
 
-int sliced_step_grid(int dev) {
-  static int cache[64] = {0};
-  int &c = cache[dev & 63];
-  if (!c) c = resident_wgs(sliced_step_kernel, sliced_lds_bytes(), dev);
+int sliced_step_grid(int dev, bool i8x) {
+  static int cache[2][64] = {{0}};
+  int &c = cache[i8x ? 1 : 0][dev & 63];
+  if (!c)
+    c = i8x ? resident_wgs(sliced_step_kernel<true>, sliced_lds_bytes(true), dev)
+            : resident_wgs(sliced_step_kernel<false>, sliced_lds_bytes(false), dev);
   return c;
 }
 
 hipError_t launch_sliced_step(const StepDesc *descs, int count, const WgGroup *groups,
-                              int group_size, int m, int grid, size_t lds, hipStream_t s) {
+                              int group_size, int m, int grid, size_t lds, bool i8x,
+                              hipStream_t s) {
   if (m < 2 || m > kMaxM) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sliced_step_kernel, dim3(grid), dim3(kWG), lds, s, descs, count, groups,
-                     group_size, m);
+  if (i8x)
+    hipLaunchKernelGGL(sliced_step_kernel<true>, dim3(grid), dim3(kWG), lds, s, descs, count,
+                       groups, group_size, m);
+  else
+    hipLaunchKernelGGL(sliced_step_kernel<false>, dim3(grid), dim3(kWG), lds, s, descs, count,
+                       groups, group_size, m);
   return hipGetLastError();
 }
 

@@ -118,7 +118,7 @@ static void check_plan(const std::vector<q8_matvec_desc> &descs, int m, int grou
   CHECK(st == Q8_OK);
   if (st != Q8_OK) return;
   if (sliced) {  // 32-row tiles of 1024-wide descriptors, the sliced kernel's LDS
-    CHECK(plan.lds == q8::sliced_lds_bytes() && plan.all_staged);
+    CHECK(plan.lds == q8::sliced_lds_bytes(i8x) && plan.all_staged);
     for (const q8::StepDesc &t : plan.descs)
       CHECK(t.rows_per_tile == q8::sliced_rows_per_tile() && t.n == q8::kSliceWidth);
   }
@@ -224,9 +224,9 @@ static void planner() {
   check_plan({mv(3072, 3072, false)}, 1, q8::kStepGroupSize, false, 512, 1u);
   check_plan({mv(256, 512, false), mv(1024, 77, false)}, 1, 4, false, 0, 1u);
   // the batched step in column slices: what the graph builder hands the
-  // planner for the decode step at m = 8 (o and down as 2 and 3 slices), a
-  // ragged set with empty slices, and the refusals (m = 1, i8x, a slice
-  // wider than 1024)
+  // planner for the decode step at m = 8 (o and down as 2 and 3 slices;
+  // binary32 and int8 activations), a ragged set with empty slices, and the
+  // refusals (m = 1 either way, a slice wider than 1024)
   {
     std::vector<q8_matvec_desc> sl;
     const int slices[7][2] = {{1024, 2048}, {1024, 1024}, {1024, 1024}, {1024, 1024},
@@ -236,13 +236,16 @@ static void planner() {
       for (int k = 0; k < 7; k++)
         for (int r = 0; r < reps[k]; r++) sl.push_back(mv(slices[k][0], slices[k][1], false));
     sl.push_back(mv(1024, 151936, true));
-    for (int m : {2, 8}) check_plan(sl, m, 1, false, 0, 0u, true);
-    check_plan({mv(1024, 77, false), mv(1024, 0, false), mv(1024, 33, false), mv(1024, 1, true)},
-               3, 1, false, 0, 0u, true);
+    for (int m : {2, 8})
+      for (bool i8x : {false, true}) check_plan(sl, m, 1, i8x, 0, 0u, true);
+    for (bool i8x : {false, true})
+      check_plan({mv(1024, 77, false), mv(1024, 0, false), mv(1024, 33, false),
+                  mv(1024, 1, true)},
+                 3, 1, i8x, 0, 0u, true);
     q8::StepPlan plan;
     std::vector<q8_matvec_desc> one = {mv(1024, 64, false)};
     CHECK(q8::plan_step(one.data(), 1, 1, 0, 1, plan, false, false, 0, 0u, true) == Q8_ERR_SHAPE);
-    CHECK(q8::plan_step(one.data(), 1, 8, 0, 1, plan, true, false, 0, 0u, true) == Q8_ERR_SHAPE);
+    CHECK(q8::plan_step(one.data(), 1, 1, 0, 1, plan, true, false, 0, 0u, true) == Q8_ERR_SHAPE);
     std::vector<q8_matvec_desc> wide = {mv(2048, 64, false)};
     CHECK(q8::plan_step(wide.data(), 1, 8, 0, 1, plan, false, false, 0, 0u, true) == Q8_ERR_SHAPE);
   }
