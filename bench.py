@@ -608,11 +608,11 @@ def only_workload(args, torch, q8, dev) -> int:
                    alg_bytes=b)
         for g in gs:
             g.close()
-    else:
+    else:  # batched, i8x_batched: the m = 8 step, binary32 or int8 activations
+        mode = q8.Q8_GRAPH_PERSISTENT_I8X if args.only == "i8x_batched" else q8.Q8_GRAPH_PERSISTENT
         sets8 = [StepSet(torch, dev, 0, 5000 + 1000 * j, 8, False) for j in range(2)]
         host8 = torch.zeros(8, dtype=torch.int32).pin_memory()
-        p8 = [q8.StepGraph(s.descs, 8, host_idx=host8, mode=q8.Q8_GRAPH_PERSISTENT)
-              for s in sets8]
+        p8 = [q8.StepGraph(s.descs, 8, host_idx=host8, mode=mode) for s in sets8]
         s8, _ = time_graph_steps(torch, p8, host8, args.steps, args.warmup, poll=True)
         b8 = sets8[0].bytes
         out.update(step_latency_us=round(s8 * 1e6, 2), GBps=round(b8 / s8 / 1e9, 1),
@@ -631,8 +631,9 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline step (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "decode", "wide",
-                                       "stream", "matvec_graph", "layer_graphs", "chain"],
+    ap.add_argument("--only", choices=["lm_head", "batched", "i8x_step", "i8x_batched", "decode",
+                                       "wide", "stream", "matvec_graph", "layer_graphs",
+                                       "chain"],
                     default=None,
                     help="only time one other configuration (for profiling runs): "
                          "the fused lm_head (1024 -> 151,936 + argmax, m = 1), "
