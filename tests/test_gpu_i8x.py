@@ -81,6 +81,25 @@ def test_i8x_special_blocks(cuda):
     assert np.all(np.isnan(y)) and np.all(np.isnan(ref))
 
 
+@pytest.mark.parametrize("m,n", [(3, 1024), (5, 3072), (8, 2048)])
+def test_i8x_bad_block_stays_in_its_row(cuda, m, n):
+    """A NaN (or infinity) block in one x row makes that row's outputs NaN
+    and leaves every other row at the oracle's bar (each x row keeps its own
+    steps and sums, also on the matrix-core tile); a zero block in another
+    row adds nothing."""
+    p = 70
+    w, _ = rich_case(p, n, seed=n + m)
+    x = gen.activations(m, n, seed=m, index=n + 1)
+    bad = m // 2
+    x[bad, 37] = np.nan if m % 2 else np.inf
+    x[0, 0:32] = 0.0
+    y = gpu_i8x(w, x, cuda)
+    ref, tol = oracle.matvec_i8x(w, x)
+    assert np.all(np.isnan(y[bad])) and np.all(np.isnan(ref[bad]))
+    keep = [r for r in range(m) if r != bad]
+    assert_parity(y[keep], ref[keep], tol[keep], f"rows beside the bad one, m={m} n={n}")
+
+
 def test_i8x_exact_on_grid(cuda):
     """x already on its grid (power-of-two steps, one code 127 per block):
     quantising changes nothing and the result meets the f32 oracle's bar."""
