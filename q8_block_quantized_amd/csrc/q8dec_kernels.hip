@@ -258,7 +258,7 @@ __device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
 // counts come from the groups' `expected`
 // fields, or, when those are 0, from "every workgroup arrives once".
 // Atomics are relaxed: each counter increment is issued only after the
-// updates before it have returned (performed at the memory side), which
+// updates before it have completed (performed at the memory side), which
 // orders them without L2 write-back or invalidation.  Four dependent round
 // trips separate the last arrival from the result.
 template <int MR>
@@ -281,19 +281,26 @@ __device__ void argmax_arrive(const unsigned long long (*lk)[MR], int m,
       size = (nwg - j + T - 1) / T;
       nteams = nwg < T ? nwg : T;
     }
-    unsigned long long dep = 0ull;
-    for (int r = 0; r < m; r++) {
-      unsigned long long v = lk[0][r];
-      for (int w = 1; w < kWaves; w++) v = umax64(v, lk[w][r]);
-      dep |= __hip_atomic_fetch_max(&g->keys[r], v, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    // The m maxima go out together as global atomics that return nothing,
+    // and one wait for all of them (vmcnt covers stores and atomics: they
+    // are then performed at the memory side) orders them before the counter.
+    // (Atomics that return the old value were turned by the compiler into
+    // one read of each result right after its atomic: m round trips.)
+#pragma unroll
+    for (int r = 0; r < MR; r++) {
+      if (r < m) {
+        unsigned long long v = lk[0][r];
+        for (int w = 1; w < kWaves; w++) v = umax64(v, lk[w][r]);
+        __hip_atomic_fetch_max(gpw(&g->keys[r]), v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    asm volatile("" ::"v"(dep));  // the maxima have returned
-    const uint32_t prev = __hip_atomic_fetch_add(&g->counter, 1u, __ATOMIC_RELAXED,
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the maxima are performed
+    const uint32_t prev = __hip_atomic_fetch_add(gpw(&g->counter), 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev == size - 1u) {
-      __hip_atomic_store(&g->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t p2 = __hip_atomic_fetch_add(&slot->top.counter, 1u,
+      __hip_atomic_store(gpw(&g->counter), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t p2 = __hip_atomic_fetch_add(gpw(&slot->top.counter), 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = p2 == nteams - 1u;
     }
@@ -305,23 +312,34 @@ __device__ void argmax_arrive(const unsigned long long (*lk)[MR], int m,
   for (int r = 0; r < MR; r++) {
     v[r] = 0ull;
     if (r < m && lane < (int)T)
-      v[r] = __hip_atomic_exchange(&slot->team[lane].keys[r], 0ull, __ATOMIC_RELAXED,
+      v[r] = __hip_atomic_exchange(gpw(&slot->team[lane].keys[r]), 0ull, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
   }
+  // One wait for every exchange, every row's index, then all the stores
+  // together, as global stores: a wait between them would also wait for the
+  // stores before it, the host copy's round trip included.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int32_t res[MR];
 #pragma unroll
   for (int r = 0; r < MR; r++) {
-    if (r < m) {
-      const unsigned long long k = wave_max64(v[r]);
-      if (lane == 0) {
-        idx[r] = key_index(k);
+    res[r] = 0;
+    if (r < m) res[r] = key_index(wave_max64(v[r]));
+  }
+#pragma unroll
+  for (int r = 0; r < MR; r++) asm volatile("" ::"v"(res[r]));
+  asm volatile("" ::: "memory");
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < MR; r++) {
+      if (r < m) {
+        gpw(idx)[r] = res[r];
         if (host)
-          __hip_atomic_store(&host[r], key_index(k), __ATOMIC_RELAXED,
+          __hip_atomic_store(gpw(&host[r]), res[r], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
+    __hip_atomic_store(gpw(&slot->top.counter), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (lane == 0)
-    __hip_atomic_store(&slot->top.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- matvec geometry ---------------------------------------------------------
