@@ -477,14 +477,20 @@ int plan_step(const q8_matvec_desc *descs, int32_t count, int32_t m, int dev,
   if (group_size > grid) group_size = grid;
   plan.grid = grid;
   plan.group_size = group_size;
-  // prefix sums of tile weight bytes
+  // prefix sums of tile weight bytes.  An argmax matvec's tiles count
+  // kArgmaxWeightPct % more (kArgmaxWeightPctBatched for m > 1): the
+  // workgroups holding them end with the arrival chain after their last
+  // tile, so they get that much less to stream and the chain overlaps the
+  // others' last tiles.
   std::vector<int64_t> pre((size_t)ntiles + 1, 0);
+  const int64_t argmax_pct = 100 + (m > 1 ? kArgmaxWeightPctBatched : kArgmaxWeightPct);
   for (int32_t i = 0, t = 0; i < count; i++) {
     const StepDesc &d = plan.descs[i];
     const int64_t pitch = (int64_t)(d.n / 32) * 34 * (paired(i) ? 2 : 1);
+    const int64_t pct = d.idx ? argmax_pct : 100;
     for (int32_t r0 = 0; r0 < d.p; r0 += d.rows_per_tile, t++) {
       const int32_t rows = d.p - r0 < d.rows_per_tile ? d.p - r0 : d.rows_per_tile;
-      pre[t + 1] = pre[t] + rows * pitch + 1;  // +1: zero-width tiles still count
+      pre[t + 1] = pre[t] + rows * pitch * pct / 100 + 1;  // +1: zero-width tiles still count
     }
   }
   const int ngroups = (grid + group_size - 1) / group_size;

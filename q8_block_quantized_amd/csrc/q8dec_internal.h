@@ -223,6 +223,11 @@ constexpr int kStepMinRows = 8;                   // only heights above one pass
 // the wave priority by progress, 1 measured fastest of 1–512 for m = 4, 8,
 // 16, 32 and int8 activations: m = 8 148 µs against 153 µs at 2)
 constexpr int kStepGroupSizeBatched = 1;
+// Extra weight of an argmax matvec's tiles in the step's byte balancing
+// (percent): the arrival chain after the last tile (about 3 us at m = 1,
+// 6 us at m = 8) measured best hidden at 3 % and 6 % (of 0, 3, 6, 10).
+constexpr int kArgmaxWeightPct = 3;
+constexpr int kArgmaxWeightPctBatched = 6;
 
 // Host stub of one kernel, used to check that the code object loads.
 const void *probe_kernel();
