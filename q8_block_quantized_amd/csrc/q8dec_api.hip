@@ -931,9 +931,11 @@ int build_graph(const q8_matvec_desc *descs, const int32_t *levels, int32_t coun
       if (e == hipSuccess)
         e = hipMemcpy(ws + group_off[i], pl.groups.data(),
                       pl.groups.size() * sizeof(q8::WgGroup), hipMemcpyHostToDevice);
+      // the table's own length (the planner may hand back a table of another
+      // length than the segment's matvecs)
       g->launches.push_back(SegmentLaunch{
           (const q8::StepDesc *)(ws + table_off[i]), (const q8::WgGroup *)(ws + group_off[i]),
-          segs[i].end - segs[i].begin, pl.group_size, pl.grid, pl.lds, pl.all_staged});
+          (int32_t)pl.descs.size(), pl.group_size, pl.grid, pl.lds, pl.all_staged});
       if (sliced) g->launches.back().kind = kSlicedNode;
     }
     if (sliced && !sums.empty() && e == hipSuccess) {
