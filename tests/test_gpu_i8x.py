@@ -275,6 +275,32 @@ def test_i8x_full_step_against_oracle(cuda):
     g.close()
 
 
+def test_i8x_full_batched_step_every_output(cuda):
+    """m = 8 through all 197 matvecs of a step with int8 activations, in the
+    persistent launch the benchmark times (column slices and their sums):
+    every output of every matvec for all 8 x rows against the oracle's
+    quantised product, and the lm_head's 8 tokens."""
+    import torch
+    m = 8
+    say("full int8 m=8 step: generating 197 matvecs")
+    shapes, ws, xs, descs = _step(28, 151936, m, 2, cuda)
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X, device=cuda)
+    assert g.info() == (2, 0)
+    g.launch()
+    torch.cuda.synchronize()
+    say("full int8 m=8 step: checking every output against the oracle")
+    for i, (name, n, p) in enumerate(shapes):
+        y = descs[i]["y"].cpu().numpy()
+        ref, tol = oracle.matvec_i8x(ws[i], xs[i])
+        assert_parity(y, ref, tol, f"i8x m=8 {name}")
+        if i == len(shapes) - 1:
+            for r in range(m):
+                assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+                assert int(host[r]) == oracle.argmax_f32(y[r])
+    g.close()
+
+
 def test_i8x_step_refuses_other_widths(cuda):
     import torch
     shapes, ws, xs, descs = _step(0, 64, 1, 5, cuda)
