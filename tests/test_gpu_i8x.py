@@ -275,6 +275,41 @@ def test_i8x_full_step_against_oracle(cuda):
     g.close()
 
 
+@pytest.mark.parametrize("m", [2, 4])
+def test_i8x_mixed_width_batched_step(cuda, m):
+    """A batched int8 step whose widths mix the matrix-core ones with others
+    (256, 512: the VALU tile, with x's packed codes in LDS after the steps),
+    one launch (not sliced), an argmax on a 1024-wide matvec: every output
+    against the oracle, over two launches."""
+    import torch
+    shapes = [("a", 512, 100), ("b", 1024, 77), ("c", 2048, 40), ("d", 256, 33),
+              ("e", 3072, 50), ("lm", 1024, 3000)]
+    ws = [rich_case(p, n, seed=20 + i)[0] for i, (_, n, p) in enumerate(shapes)]
+    xs = [gen.activations(m, n, seed=20, index=i) for i, (_, n, p) in enumerate(shapes)]
+    descs = []
+    for i, (name, n, p) in enumerate(shapes):
+        descs.append(dict(n=n, p=p, w=to_dev(ws[i].reshape(-1), cuda), x=to_dev(xs[i], cuda),
+                          y=torch.full((m, p), float("nan"), dtype=torch.float32, device=cuda),
+                          idx=torch.full((m,), -7, dtype=torch.int32, device=cuda)
+                          if name == "lm" else None))
+    host = torch.full((m,), -5, dtype=torch.int32).pin_memory()
+    g = q8.StepGraph(descs, m, host_idx=host, mode=q8.Q8_GRAPH_PERSISTENT_I8X, device=cuda)
+    assert g.info() == (1, 0)
+    refs = [oracle.matvec_i8x(ws[i], xs[i]) for i in range(len(shapes))]
+    for rep in range(2):
+        for d in descs:
+            d["y"].fill_(float("nan"))
+        g.launch()
+        torch.cuda.synchronize()
+        for i, (name, n, p) in enumerate(shapes):
+            assert_parity(descs[i]["y"].cpu().numpy(), refs[i][0], refs[i][1],
+                          f"m={m} {name} rep {rep}")
+        ref, tol = refs[-1]
+        for r in range(m):
+            assert oracle.argmax_accepted(int(host[r]), ref[r], tol[r])
+    g.close()
+
+
 def test_i8x_full_batched_step_every_output(cuda):
     """m = 8 through all 197 matvecs of a step with int8 activations, in the
     persistent launch the benchmark times (column slices and their sums):
