@@ -373,7 +373,13 @@ constexpr int kMfmaMaxBlocks = kMaxLdsBlocks / kWaves;  // x blocks per wave
 constexpr int kMaxM = 8;  // activation rows of the m <= 8 paths (wider: kWide)
 constexpr int kI8xMaxBlocks = kMaxM * kMaxLdsBlocks;  // int8-activation steps
 constexpr int kRedStride = 80;  // floats between a wave's partial-sum entries
-constexpr int kRedFloats = 2 * kWaves * 4 * kRedStride;  // two sets per wave
+// One set of the waves' partial sums of a 16-row group.  An odd group puts
+// its set into the tile rows of the group before it instead (every wave has
+// read them before that group's barrier), so consecutive groups still write
+// different LDS and need no barrier between one's reads and the next's
+// writes, and the tile's own barrier orders the last group's reads before
+// the next tile is stored.
+constexpr int kRedFloats = kWaves * 4 * kRedStride;
 
 __host__ __device__ inline int path_of(int m, int n) {
   const int bpr = n >> 5;
@@ -385,6 +391,8 @@ __host__ __device__ inline int path_of(int m, int n) {
 }
 
 __host__ __device__ inline int nbl_of(int n) { return ((n >> 5) + 31) >> 5; }
+// matrix-core tiles are at least 32 blocks wide: 16 rows hold a set of partials
+static_assert(16 * ((32 * 34 + kMfmaRowPad) / 4) >= kRedFloats, "partials fit a row group");
 
 // Rows per tile: staged tiles fill up to kTileMaxBytes (at least one pass of
 // 8 rows), batched tiles up to kMfmaTileBytes in 16-row groups; direct and
@@ -850,12 +858,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 // A 16-row group's outputs of the int8 matrix-core tile from the four waves'
 // partials acc, through LDS as mfma_tile's (there y[xr][row] also adds the
 // column xr + 8 of x's low parts, which the int8 form does not have).
-__device__ __forceinline__ void mfma_group_out(const f32x4 &acc, float *red, int buf,
+__device__ __forceinline__ void mfma_group_out(const f32x4 &acc, float *rb,
                                                int32_t rg, int32_t rows, int32_t m,
                                                int32_t p, float *y, int32_t r0, bool keys,
                                                unsigned long long &kb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float *rb = red + buf * (kWaves * 4 * kRedStride);
 #pragma unroll
   for (int r = 0; r < 4; r++) rb[(wave * 4 + r) * kRedStride + lane] = acc[r];
   __syncthreads();
@@ -989,7 +996,7 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
     // writes (fixed r) and its reads below (four r, sixteen lanes each)
     // both fall in 64 different banks; column i of row jj is entry i % 4
     // of lane 16 (i / 4) + jj
-    float *rb = red + buf * (kWaves * 4 * kRedStride);
+    float *rb = buf ? (float *)(tl + (rg - 16) * lpd) : red;
 #pragma unroll
     for (int r = 0; r < 4; r++) rb[(wave * 4 + r) * kRedStride + lane] = acc[r];
     __syncthreads();
@@ -1007,8 +1014,8 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
         if (keys) kb = umax64(kb, argmax_key(v, (uint32_t)(r0 + rr)));
       }
     }
-    // the other buffer serves the next group; the barrier after its writes
-    // orders this group's reads before the one after reuses this buffer
+    // the next group's set is elsewhere (kRedFloats); the barrier after its
+    // writes orders this group's reads before the one after reuses this set
     buf ^= 1;
   }
 }
@@ -1068,7 +1075,8 @@ __device__ __forceinline__ void mfma_tile_i8(const uint32_t *tl, int32_t bpr,
         acc[r] = fmaf((float)dd[r], so * xo[r], acc[r]);
       }
     }
-    mfma_group_out(acc, red, buf, rg, rows, m, p, y, r0, keys, kb);
+    mfma_group_out(acc, buf ? (float *)(tl + (rg - 16) * lpd) : red, rg, rows, m, p, y, r0,
+                   keys, kb);
     buf ^= 1;
   }
 }
@@ -2147,7 +2155,8 @@ __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint3
 // The batched step in column slices: every descriptor 1024 wide with its
 // matrix's row pitch (a column slice, or a 1024-wide matrix whole), so each
 // wave keeps 8 blocks of x (a third of the registers of 3072-wide rows) and
-// a tile is two 16-row groups (35 KB of LDS): three workgroups a CU.
+// a tile is two 16-row groups (35 KB of LDS, 40 KB with the partial sums):
+// four workgroups a CU (three with the int8 form's x steps).
 constexpr int kSliceRows = 32;
 constexpr int kMaxSlices = 3;  // 3072 / kSliceWidth
 constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRowPad);
@@ -2155,7 +2164,7 @@ constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRow
 // a slice starts at a block boundary, so its blocks' codes and steps are
 // those of the whole row).
 template <bool I8X>
-__global__ void __launch_bounds__(kWG, 3)
+__global__ void __launch_bounds__(kWG, I8X ? 3 : 4)
 sliced_step_kernel(const StepDesc *__restrict__ table, int32_t count,
                    const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
