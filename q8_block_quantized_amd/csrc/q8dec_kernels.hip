@@ -708,7 +708,10 @@ __device__ __forceinline__ float q8x_chunk(const f32x4 v, uint32_t &codes) {
 // (the batched form, once per matvec).
 // With BM, x's rows may lie xstride floats apart (a column slice of a wider
 // x, whose blocks quantise as they do in the whole row).
-template <int NT, bool BM = false>
+// PADS (BM only): block b's steps at (b / 2) * kRedStride + 8 (b % 2) + i,
+// the unused tail of a set of partial sums' entries (16 blocks of steps
+// where a set has 16 entries, offset by 64 floats).
+template <int NT, bool BM = false, bool PADS = false>
 __device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
                                uint32_t *xq, float *xd, int32_t xstride = 0) {
   const int32_t chunks = (m * n) >> 2;  // a multiple of 8: no block is split
@@ -728,7 +731,8 @@ __device__ void quantize_x_lds(const float *x, int32_t m, int32_t n,
       xq[c] = codes;
       if ((c & 7) == 0) {
         const int32_t k = c >> 3, i = BM ? k / bpr : 0;
-        xd[BM ? (k - i * bpr) * kMaxM + i : k] = d;
+        const int32_t b = k - i * bpr;
+        xd[!BM ? k : (PADS ? (b >> 1) * kRedStride + 8 * (b & 1) + i : b * kMaxM + i)] = d;
       }
     }
   }
@@ -1030,7 +1034,7 @@ __device__ __forceinline__ void mfma_tile(const uint32_t *tl, int32_t bpr,
 // and added to the f32 accumulator of its x row; the waves' partials meet
 // in LDS as mfma_tile's do.  The lane layout is mfma_tile's (operands of
 // 8 bytes instead of 8 bf16).
-template <int NBW, int MB>
+template <int NBW, int MB, bool PADS = false>
 __device__ __forceinline__ void mfma_tile_i8(const uint32_t *tl, int32_t bpr,
                                              int32_t rows, int32_t m, int32_t p,
                                              const u32x2 (&xi)[MB], const float *xd,
@@ -1044,7 +1048,9 @@ __device__ __forceinline__ void mfma_tile_i8(const uint32_t *tl, int32_t bpr,
   const i32x4 izero = {0, 0, 0, 0};
   // steps of x rows 4 g .. 4 g + 3 (rows 8 .. 15, which A holds as zeros,
   // read rows 0 .. 7's: their sums are 0 and never leave the tile)
-  const float *xdw = xd + (wave * NBW) * kMaxM + 4 * (g & 1);
+  // (PADS: the steps as quantize_x_lds places them in the partials' padding)
+  const float *xdw =
+      xd + (PADS ? ((wave * NBW) >> 1) * kRedStride : (wave * NBW) * kMaxM) + 4 * (g & 1);
   int buf = 0;
   for (int32_t rg = 0; rg < rows; rg += 16) {
     const int32_t row = min(rg + j, rows - 1);
@@ -1067,8 +1073,9 @@ __device__ __forceinline__ void mfma_tile_i8(const uint32_t *tl, int32_t bpr,
           (int64_t)__builtin_bit_cast(uint64_t, xi[t + 1]), qo, izero, 0, 0, 0);
       const float se = (float)__builtin_bit_cast(_Float16, (uint16_t)(s01 & 0xFFFFu));
       const float so = (float)__builtin_bit_cast(_Float16, (uint16_t)(s23 >> 16));
-      const f32x4 xe = *(const f32x4 *)(xdw + t * kMaxM);
-      const f32x4 xo = *(const f32x4 *)(xdw + (t + 1) * kMaxM);
+      const float *xdt = xdw + (PADS ? (t >> 1) * kRedStride : t * kMaxM);
+      const f32x4 xe = *(const f32x4 *)xdt;
+      const f32x4 xo = *(const f32x4 *)(xdt + (PADS ? 8 : kMaxM));
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         acc[r] = fmaf((float)de[r], se * xe[r], acc[r]);
@@ -1463,7 +1470,12 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
   // int8 activations: the steps, then the packed codes (m = 1: after the
   // tile; batched: after the partial sums; the matrix-core tiles hold their
   // codes in registers and need no packed region)
-  float *xd = M1 ? red : red + kRedFloats;
+  // (column slices: the steps of a slice's 32 blocks fit the last 16 floats
+  // of the 16 entries of the partial sums, which no reduction touches)
+  constexpr bool XPAD = I8X && STRIDED && !M1;
+  static_assert(!XPAD || MMB * kWaves <= 2 * kWaves * 4, "a slice's steps fit the padding");
+  static_assert(kRedStride - 64 >= 16, "two blocks of steps an entry");
+  float *xd = M1 ? red : (XPAD ? red + 64 : red + kRedFloats);
   uint32_t *xq = (uint32_t *)(xd + kI8xMaxBlocks);
   // which path a tile takes; without ANY every m = 1 tile takes the staged
   // one; batched int8 tiles of the matrix-core widths take the matrix cores
@@ -1570,7 +1582,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
         // a column slice's x rows lie the whole matrix's width apart
         const int32_t xstride =
             STRIDED ? desc_pitch16(cur.d.flags) * 16 / 34 * 32 : cur.d.n;
-        quantize_x_lds<kWG, true>(cur.d.x, m, cur.d.n, tl, xd, xstride);
+        quantize_x_lds<kWG, true, XPAD>(cur.d.x, m, cur.d.n, tl, xd, xstride);
         __syncthreads();
         if constexpr (MMB >= 24) {
           if (bpr == 32) load_xi<8>(xi, tl, m, bpr);
@@ -1592,7 +1604,7 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
       else pf.store_x(xs, m, cur.d.n);
     }
     // batched (VALU tiles): straight from memory
-    const bool quant_x = I8X && !M1 && !mfma(cur) && x_changed;
+    const bool quant_x = I8X && !M1 && !XPAD && !mfma(cur) && x_changed;
     if (quant_x) quantize_x_lds<kWG>(cur.d.x, m, cur.d.n, xq, xd);
     __syncthreads();
     if (new_x || quant_x || quant_xi) {
@@ -1648,7 +1660,8 @@ __device__ void run_tiles(const Src &src, int32_t first, int32_t end,
           else
             mfma_tile_i8<24>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
         } else if constexpr (I8X && !M1) {
-          mfma_tile_i8<8>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0, keys, kb);
+          mfma_tile_i8<8, MMB, XPAD>(tl, bpr, cur.rows, m, cur.d.p, xi, xd, red, cur.d.y, cur.r0,
+                                     keys, kb);
         }
       } else if constexpr (!STRIDED) {  // (the sliced step's tiles all take the matrix cores)
         if (nbl == 1) staged_mb_i8<1>(tl, bpr, cur.rows, m, cur.d.p, xq, xd, cur.d.y, cur.r0, keys, best);
@@ -2155,8 +2168,8 @@ __device__ __forceinline__ bool grid_wait(GridBarrier *b, uint32_t target, uint3
 // The batched step in column slices: every descriptor 1024 wide with its
 // matrix's row pitch (a column slice, or a 1024-wide matrix whole), so each
 // wave keeps 8 blocks of x (a third of the registers of 3072-wide rows) and
-// a tile is two 16-row groups (35 KB of LDS, 40 KB with the partial sums):
-// four workgroups a CU (three with the int8 form's x steps).
+// a tile is two 16-row groups (35 KB of LDS, 40 KB with the partial sums,
+// in whose padding the int8 form keeps x's steps): four workgroups a CU.
 constexpr int kSliceRows = 32;
 constexpr int kMaxSlices = 3;  // 3072 / kSliceWidth
 constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRowPad);
@@ -2164,7 +2177,7 @@ constexpr int kSliceTileBytes = kSliceRows * ((kSliceWidth >> 5) * 34 + kMfmaRow
 // a slice starts at a block boundary, so its blocks' codes and steps are
 // those of the whole row).
 template <bool I8X>
-__global__ void __launch_bounds__(kWG, I8X ? 3 : 4)
+__global__ void __launch_bounds__(kWG, 4)
 sliced_step_kernel(const StepDesc *__restrict__ table, int32_t count,
                    const WgGroup *__restrict__ groups, int32_t group_size, int32_t m) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -2554,7 +2567,8 @@ int sliced_rows_per_tile() { return kSliceRows; }
 
 // The tile and its partial sums (int8 activations: and x's steps, block-major).
 size_t sliced_lds_bytes(bool i8x) {
-  return kSliceTileBytes + (size_t)(kRedFloats + (i8x ? kI8xMaxBlocks : 0)) * sizeof(float);
+  (void)i8x;  // the int8 form's steps live in the partial sums' padding
+  return kSliceTileBytes + (size_t)kRedFloats * sizeof(float);
 }
 
 int sliced_step_grid(int dev, bool i8x) {
